@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+One step = one selective_scan_fwd over the Mamba-2.8B-shaped layer
+(batch 4, L 8192, d_inner 5120, d_state 16, bfloat16 activations, float32
+state and arithmetic) followed by one selective_state_update over the decode
+workload (256 sequences x 5120 channels x 16 states).  Inputs are seeded
+synthetic data (synth.make) already resident in HBM; decode states rotate
+over three buffers so the 256 MB Infinity Cache cannot hold them between
+steps.
+
+Prints one JSON line.  `value` is tokens*channels processed per second over
+the whole step (forward B*L*D plus decode B*D).  `roofline` describes the
+forward kernel (the dominant one); `cpu_baseline` times the float64 oracle on
+a bounded sample of the same workload on the host.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+# MI355X public figures: 256 CUs x 4 SIMD16 units at 2.4 GHz -> 39.3 T fp32
+# vector lane-operations per second without packed math (the published
+# 157.3 TFLOP/s counts an FMA as 2 flops and packed pairs as 2 lanes).
+HBM_PEAK_GBS = 8000.0
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+METRIC = "selective-scan fwd tokens·channels/s and achieved HBM GB/s (% of peak), 1 GPU"
+
+
+def valu_slots_per_token_channel(n):
+    """Algorithmic fp32 VALU issue slots per token*channel of the forward:
+    per state mul(Delta*A), exp, mul(Delta*u*B), fma(h), fma(y) = 6 slots with
+    the transcendental at half rate (2 slots); per channel step softplus
+    (exp, log, rcp + 5 ops = 11), gate (exp, rcp + 3 ops = 7), Delta*u and
+    D*u (2): 20 slots."""
+    return 6 * n + 20
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="mamba2p8b",
+                   choices=["mamba130m", "mamba2p8b", "seq1m"],
+                   help="forward workload of the step (default: the 2.8B-shaped layer)")
+    p.add_argument("--no-decode", action="store_true", help="time the forward alone")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate host time budget of the oracle baseline")
+    return p.parse_args()
+
+
+def cpu_baseline(x, w, dec, budget_s):
+    """Times the oracle (as it stands) on a bounded prefix of the workload:
+    batch row 0, all channels, the first L' steps, sized to ~budget_s; plus
+    one decode step on a 32-sequence slice of the decode workload."""
+    import oracle
+
+    def sample(L):
+        sl = slice(0, L)
+        return (x["u"][:1, sl], x["delta"][:1, sl], x["A"], x["B"][:1, sl], x["C"][:1, sl],
+                x["D"], x["z"][:1, sl], x["dt_bias"])
+
+    t0 = time.perf_counter()
+    oracle.scan_fwd(*sample(8))
+    per_step = (time.perf_counter() - t0) / 8
+    L = int(max(8, min(w.seqlen, budget_s / max(per_step, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.scan_fwd(*sample(L))
+    t_fwd = time.perf_counter() - t0
+    nb = 32
+    t0 = time.perf_counter()
+    oracle.state_update(dec["state"][:nb], dec["u"][:nb], dec["delta"][:nb], dec["A"],
+                        dec["B"][:nb], dec["C"][:nb], dec["D"], dec["z"][:nb],
+                        dec["dt_bias"])
+    t_dec = time.perf_counter() - t0
+    tokch = L * w.dim + nb * dec_dim(dec)
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas_threads = None
+    return {
+        "value": tokch / (t_fwd + t_dec),
+        "unit": "tokens·channels/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle, single-threaded ufuncs: forward on batch row 0, "
+                   f"{L} of {w.seqlen} steps, all {w.dim} channels ({t_fwd:.1f} s) + one "
+                   f"decode step on {nb} sequences ({t_dec:.2f} s)"),
+        "host_cpus_available": len(os.sched_getaffinity(0)),
+        "blas_threads_idle": blas_threads,
+    }
+
+
+def dec_dim(dec):
+    return dec["u"].shape[1]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this path runs on one GPU "
+              "(no collectives, no sharding); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_38_amd import (check_device_errors, fwd_plan,
+                                              selective_scan_fwd, selective_state_update)
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    dw = synth.WORKLOADS["decode"]
+    act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dact = torch.bfloat16 if dw.dtype == "bf16" else torch.float32
+    print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = synth.make(w)
+    dec = synth.make(dw)
+
+    def up(a, dtype=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dtype)
+
+    u, dt, z = up(x["u"], act), up(x["delta"], act), up(x["z"], act)
+    Bm, Cm = up(x["B"], act), up(x["C"], act)
+    A, Dv, bias = up(x["A"]), up(x["D"]), up(x["dt_bias"])
+    out = torch.empty_like(u)
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+    n_rot = 3
+    states = [up(dec["state"]) for _ in range(n_rot)]
+    dx, ddt, dz = up(dec["u"], dact), up(dec["delta"], dact), up(dec["z"], dact)
+    dB, dC = up(dec["B"], dact), up(dec["C"], dact)
+    dA, dD, dbias = up(dec["A"]), up(dec["D"]), up(dec["dt_bias"])
+    dout = torch.empty_like(dx)
+    torch.cuda.synchronize()
+
+    def fwd():
+        selective_scan_fwd(u, dt, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, delta_softplus=True,
+                           return_last_state=True, out=out, last_state=last)
+
+    def decode(i):
+        selective_state_update(states[i % n_rot], dx, ddt, dA, dB, dC, D=dD, z=dz,
+                               dt_bias=dbias, dt_softplus=True, out=dout)
+
+    for i in range(args.warmup):
+        fwd()
+        if not args.no_decode:
+            decode(i)
+    torch.cuda.synchronize()
+    check_device_errors(dev)
+    print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        fwd()
+        ev[i][1].record()
+        if not args.no_decode:
+            decode(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    check_device_errors(dev)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    fwd_avg = float(np.mean(fwd_ms))
+    dec_avg = float(np.mean(dec_ms))
+
+    tokch_fwd = w.batch * w.seqlen * w.dim
+    tokch_dec = 0 if args.no_decode else dw.batch * dw.dim
+    value = (tokch_fwd + tokch_dec) / (ms_per_step / 1e3)
+    fwd_bytes = synth.algorithmic_bytes(w)
+    dec_bytes = synth.algorithmic_bytes(dw)
+    slots = valu_slots_per_token_channel(w.dstate) * tokch_fwd
+    achieved_t = slots / (fwd_avg / 1e3) / 1e12
+    plan = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate, act)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens·channels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) activations, S4D-real A, log-uniform dt bias)",
+        "config": {
+            "workload": (f"{w.name} forward (B={w.batch}, L={w.seqlen}, D={w.dim}, N={w.dstate}, "
+                         f"{w.dtype} activations)"
+                         + ("" if args.no_decode else
+                            f" + decode update (B={dw.batch}, D={dw.dim}, N={dw.dstate}, "
+                            f"{dw.dtype})")),
+            "io_dtype": w.dtype,
+            "forward_plan": plan,
+        },
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved_t,
+            "peak": VALU_PEAK_TOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved_t / VALU_PEAK_TOPS,
+            "traffic": None,
+            "kernel": "scan_fwd_kernel",
+            "ops_per_unit": f"{valu_slots_per_token_channel(w.dstate)} fp32 VALU issue slots "
+                            "per token*channel",
+            "units_per_launch": tokch_fwd,
+            "avg_launch_ms": fwd_avg,
+        },
+        "hbm": {
+            "forward_GBps": fwd_bytes / (fwd_avg / 1e3) / 1e9,
+            "forward_frac_of_8TBps": fwd_bytes / (fwd_avg / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "forward_algorithmic_bytes": fwd_bytes,
+            "decode_GBps": (None if args.no_decode else
+                            dec_bytes / (dec_avg / 1e3) / 1e9),
+            "decode_frac_of_8TBps": (None if args.no_decode else
+                                     dec_bytes / (dec_avg / 1e3) / 1e9 / HBM_PEAK_GBS),
+            "decode_algorithmic_bytes": dec_bytes,
+            "decode_avg_launch_ms": None if args.no_decode else dec_avg,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(x, w, dec, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * Operations (pages cited by title and section):
+ *   selective_scan_fwd     Selective state-space (S6) forward over a sequence:
+ *                          Delta = softplus(dt + dt_bias), Abar = exp(Delta*A),
+ *                          Bbar*x = Delta*B*x, h_t = Abar_t*h_{t-1} + Bbar_t*x_t,
+ *                          y_t = C_t . h_t + D*x_t, out = y * SiLU(z).
+ *                          "Mamba: Linear-Time Sequence Modeling with Selective
+ *                          State Spaces" (reading guide), sections Method and
+ *                          Selection mechanism (S6); "Mamba / MambaMini" Steps 1-4
+ *                          (pair operator, prefix scan, h_{-1} = 0) and Q&A
+ *                          (Delta*B, SiLU gate); CSDN "Mamba" section 3(1) (D).
+ *   selective_scan_fwd_h0  The same with a caller-given initial state h_{-1}
+ *                          ("Mamba / MambaMini" Step 4: h_t = A_cum_t*h_{-1} +
+ *                          B_cum_t), so a sequence can be processed in pieces.
+ *   selective_state_update One decode step of the same recurrence on a stored
+ *                          state (reading guide FAQ: fixed D x N state per
+ *                          layer, constant time per token, no KV cache).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     keeps none of them after returning.  Calls are asynchronous on `stream`
+ *     (a hipStream_t; NULL means the null stream): buffers must stay valid
+ *     until the stream's work has finished.
+ *   - Layouts are contiguous row-major in the index order written in the
+ *     comments; there is no stride support.
+ *   - dtype (dims->dtype) is the storage type of the activations u/x, delta/dt,
+ *     z, B, C and out: SSM_F32 or SSM_BF16.  A, D, dt_bias, h0, state and
+ *     last_state are always float32.  Arithmetic and accumulation are float32;
+ *     bfloat16 outputs are rounded to nearest even.
+ *   - Nullable arguments: D (treated as 0), z (no gate), dt_bias (0),
+ *     h0 (zeros), last_state (not written).
+ *   - Errors are reported only through the return value (an ssm_status);
+ *     nothing is printed and nothing is thrown.  Argument validation happens
+ *     on the host before any HIP call: dims must be > 0, dstate must be one of
+ *     1, 2, 4, 8, 16, 32, 64, required pointers non-null, pointers 4-byte
+ *     aligned, `out` must not alias an input.  A failed launch returns
+ *     SSM_ELAUNCH; faults inside a kernel surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - The forward allocates stream-ordered scratch (hipMallocAsync) for the
+ *     carries between sequence segments and frees it on the same stream;
+ *     failure returns SSM_ENOMEM.  There is no other global state except a
+ *     per-device error counter read by ssm_check_device_errors, so calls on
+ *     different streams or host threads may run concurrently.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_EINVAL = -1,   /* bad dimension, null required pointer, aliasing */
+  SSM_EDTYPE = -2,   /* dims->dtype is not an ssm_dtype */
+  SSM_EALIGN = -3,   /* a pointer is not 4-byte aligned */
+  SSM_ENOMEM = -4,   /* scratch allocation failed */
+  SSM_ELAUNCH = -5,  /* the HIP runtime rejected a launch */
+  SSM_ETIMEOUT = -6  /* a carry wait exceeded its bound (see ssm_check_device_errors) */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+typedef struct {
+  int64_t batch;   /* B */
+  int64_t seqlen;  /* L (must be 1 for selective_state_update) */
+  int64_t dim;     /* D, the number of channels (d_inner) */
+  int64_t dstate;  /* N, the state size per channel (d_state) */
+  int32_t dtype;   /* ssm_dtype of the activations */
+} ssm_dims;
+
+/*
+ * Forward selective scan.
+ *   u, delta, z : [B][L][D] of dtype      (delta holds the raw dt)
+ *   A           : [D][N] float32
+ *   B, C        : [B][L][N] of dtype
+ *   D, dt_bias  : [D] float32 (nullable)
+ *   softplus    : nonzero -> Delta = softplus(delta + dt_bias),
+ *                 zero    -> Delta = delta + dt_bias
+ *   out         : [B][L][D] of dtype, written
+ *   last_state  : [B][D][N] float32 (nullable), the state after step L-1
+ * Returns an ssm_status.
+ */
+int selective_scan_fwd(const void* u, const void* delta, const float* A,
+                       const void* B, const void* C, const float* D,
+                       const void* z, const float* dt_bias, int softplus,
+                       void* out, float* last_state, const ssm_dims* dims,
+                       void* stream);
+
+/*
+ * As selective_scan_fwd, starting from h0 : [B][D][N] float32 (nullable =
+ * zeros).  selective_scan_fwd(...) == selective_scan_fwd_h0(..., NULL, ...).
+ */
+int selective_scan_fwd_h0(const void* u, const void* delta, const float* A,
+                          const void* B, const void* C, const float* D,
+                          const void* z, const float* dt_bias, int softplus,
+                          const float* h0, void* out, float* last_state,
+                          const ssm_dims* dims, void* stream);
+
+/*
+ * One decode step, in place on `state`.
+ *   state       : [B][D][N] float32, read and overwritten with the new state
+ *   x, dt, z    : [B][D] of dtype (z nullable)
+ *   A           : [D][N] float32;  D, dt_bias : [D] float32 (nullable)
+ *   B, C        : [B][N] of dtype
+ *   out         : [B][D] of dtype, written
+ *   dims->seqlen must be 1.  `out` must not alias an input or `state`.
+ */
+int selective_state_update(float* state, const void* x, const void* dt,
+                           const float* A, const void* B, const void* C,
+                           const float* D, const void* z,
+                           const float* dt_bias, int softplus, void* out,
+                           const ssm_dims* dims, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* ssm_status_string(int status);
+
+/*
+ * Synchronises `stream`, then reports and clears the current device's count of
+ * carry waits that hit their bound (a bounded spin in the forward kernel's
+ * segment hand-off; a non-zero count means some outputs are invalid).
+ * Returns SSM_OK, SSM_ETIMEOUT, or SSM_ELAUNCH if the runtime call failed.
+ */
+int ssm_check_device_errors(void* stream);
+
+/*
+ * Launch plan the forward would use for `dims` (host only, no GPU call):
+ * lanes_per_channel = waves sharing one channel block (state groups),
+ * segments = sequence segments, lookback = 1 if segments exchange partial
+ * aggregates (decoupled look-back), 0 if each waits for its predecessor's
+ * final state.  Returns SSM_OK or a validation error.
+ */
+typedef struct {
+  int32_t state_groups;
+  int32_t states_per_group;
+  int32_t segments;
+  int32_t segment_len;
+  int32_t lookback;
+  int32_t chunk;
+  int64_t workgroups;
+} ssm_fwd_plan;
+
+int ssm_fwd_plan_for(const ssm_dims* dims, ssm_fwd_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

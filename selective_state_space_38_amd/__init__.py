@@ -1,0 +1,9 @@
+"""MI355X (gfx950) selective-scan (Mamba S6) library: a C-ABI shared library
+with hand-written HIP kernels, and a thin PyTorch binding."""
+
+from .api import (  # noqa: F401
+    selective_scan_fwd,
+    selective_state_update,
+    check_device_errors,
+    fwd_plan,
+)

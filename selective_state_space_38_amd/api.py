@@ -1,0 +1,138 @@
+"""PyTorch-facing binding of the selective-scan C ABI.
+
+Argument marshalling only: every tensor must already be a contiguous tensor on
+the current HIP device with the documented dtype; the functions pass raw
+device pointers and the current stream to the library and raise
+RuntimeError with the library's status text on failure.  No arithmetic of the
+method happens here.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.SSM_F32, torch.bfloat16: _lib.SSM_BF16}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _raise(rc):
+    if rc != 0:
+        raise RuntimeError(_lib.status_string(rc))
+
+
+def fwd_plan(batch, seqlen, dim, dstate, dtype=torch.float32):
+    """Launch plan the forward uses for these sizes (host-only query)."""
+    lib = _lib.load()
+    dims = _lib.SsmDims(batch, seqlen, dim, dstate, _DTYPES[dtype])
+    plan = _lib.SsmFwdPlan()
+    _raise(lib.ssm_fwd_plan_for(ctypes.byref(dims), ctypes.byref(plan)))
+    return {f: getattr(plan, f) for f, _ in plan._fields_}
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, return_last_state=False, h0=None,
+                       out=None, last_state=None):
+    """Selective-scan forward on the GPU.
+
+    u, delta, z: [batch, L, dim]; B, C: [batch, L, dstate] (float32 or
+    bfloat16, all the same); A: [dim, dstate], D, delta_bias: [dim] and
+    h0: [batch, dim, dstate] float32.  Returns out (same dtype as u) and, with
+    return_last_state, the float32 final state [batch, dim, dstate].
+    """
+    if u.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {u.dtype}")
+    bsz, L, dim = u.shape
+    dstate = A.shape[1]
+    dev = u.device
+    act = u.dtype
+    _check(u, "u", act, (bsz, L, dim), dev)
+    _check(delta, "delta", act, (bsz, L, dim), dev)
+    _check(z, "z", act, (bsz, L, dim), dev)
+    _check(B, "B", act, (bsz, L, dstate), dev)
+    _check(C, "C", act, (bsz, L, dstate), dev)
+    _check(A, "A", torch.float32, (dim, dstate), dev)
+    _check(D, "D", torch.float32, (dim,), dev)
+    _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _check(h0, "h0", torch.float32, (bsz, dim, dstate), dev)
+    if out is None:
+        out = torch.empty_like(u)
+    _check(out, "out", act, (bsz, L, dim), dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((bsz, dim, dstate), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", torch.float32, (bsz, dim, dstate), dev)
+    dims = _lib.SsmDims(bsz, L, dim, dstate, _DTYPES[act])
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.selective_scan_fwd_h0(
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(out),
+            _ptr(last_state), ctypes.byref(dims), _stream(dev))
+    _raise(rc)
+    return (out, last_state) if return_last_state else out
+
+
+def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                           dt_softplus=True, out=None):
+    """One decode step on the GPU, updating ``state`` in place.
+
+    state: [batch, dim, dstate] float32; x, dt, z: [batch, dim] and
+    B, C: [batch, dstate] (float32 or bfloat16, all the same); A, D, dt_bias
+    as in the forward.  Returns out [batch, dim] in the activation dtype.
+    """
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    bsz, dim = x.shape
+    dstate = A.shape[1]
+    dev = x.device
+    act = x.dtype
+    _check(state, "state", torch.float32, (bsz, dim, dstate), dev)
+    _check(x, "x", act, (bsz, dim), dev)
+    _check(dt, "dt", act, (bsz, dim), dev)
+    _check(z, "z", act, (bsz, dim), dev)
+    _check(B, "B", act, (bsz, dstate), dev)
+    _check(C, "C", act, (bsz, dstate), dev)
+    _check(A, "A", torch.float32, (dim, dstate), dev)
+    _check(D, "D", torch.float32, (dim,), dev)
+    _check(dt_bias, "dt_bias", torch.float32, (dim,), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", act, (bsz, dim), dev)
+    dims = _lib.SsmDims(bsz, 1, dim, dstate, _DTYPES[act])
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.selective_state_update(
+            _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(dt_bias), 1 if dt_softplus else 0, _ptr(out), ctypes.byref(dims),
+            _stream(dev))
+    _raise(rc)
+    return out
+
+
+def check_device_errors(device=None):
+    """Synchronises the current stream and raises if a carry wait timed out."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    _raise(_lib.load().ssm_check_device_errors(_stream(dev)))

@@ -1,0 +1,245 @@
+// C ABI of the selective-scan library: validation, launch planning, scratch,
+// dispatch.  The operations and conventions are documented in ssm_scan.h.
+
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/ssm_scan.h"
+#include "ssm_internal.h"
+
+namespace {
+
+constexpr int kDefaultSpinLimit = 1 << 24;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_dstate(int64_t n) {
+  return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64;
+}
+
+int env_int(const char* name, int fallback) {
+  const char* v = getenv(name);
+  if (!v || !*v) return fallback;
+  char* end = nullptr;
+  const long x = strtol(v, &end, 10);
+  return (end && *end == '\0') ? static_cast<int>(x) : fallback;
+}
+
+int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of states each wave keeps per channel.
+int states_per_group(int64_t n) {
+  int g = env_int("SSM_FORCE_STATES_PER_GROUP", 0);
+  if (g > 0 && g <= 16 && n % g == 0) {
+    const int64_t groups = n / g;
+    // instantiated (groups, per-group) pairs
+    if ((n <= 2 && groups == 1) || (n == 4 && groups == 1) || (n == 8 && (groups <= 2)) ||
+        (n == 16 && (groups == 1 || groups == 2 || groups == 4 || groups == 8)) ||
+        (n == 32 && groups == 8) || (n == 64 && groups == 16))
+      return g;
+  }
+  return n < 4 ? static_cast<int>(n) : 4;
+}
+
+// Chooses state groups, segments and the carry mode for a forward call.
+// Chained segments cost no extra arithmetic but only one segment per channel
+// block runs at a time; look-back segments all run at once but each (except
+// the first) scans its inputs twice.  Chained mode is used when the channel
+// blocks alone give at least half the chip's SIMDs a wave.
+void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
+  const int g = states_per_group(d.dstate);
+  const int groups = static_cast<int>(d.dstate / g);
+  const int64_t cblk = div_up(d.dim, 64);
+  const int64_t chains = d.batch * cblk;
+  const int64_t waves_per_slice = chains * groups;
+  int lookback = waves_per_slice >= 512 ? 0 : 1;
+  const int force_mode = env_int("SSM_FORCE_LOOKBACK", -1);
+  if (force_mode == 0 || force_mode == 1) lookback = force_mode;
+
+  int64_t seg_len;
+  if (!lookback) {
+    seg_len = 1024;  // hand-off granularity that lets idle CUs pick up work
+  } else {
+    // enough segments for ~4096 waves, each at least 256 steps
+    const int64_t want = div_up(4096, waves_per_slice);
+    seg_len = div_up(d.seqlen, want);
+    if (seg_len < 256) seg_len = 256;
+  }
+  const int force_seg = env_int("SSM_FORCE_SEGMENT", 0);
+  if (force_seg > 0) seg_len = force_seg;
+  seg_len = div_up(seg_len, ssm::kChunk) * ssm::kChunk;
+  if (seg_len > d.seqlen) seg_len = div_up(d.seqlen, ssm::kChunk) * ssm::kChunk;
+  const int64_t n_seg = div_up(d.seqlen, seg_len);
+  if (n_seg == 1) lookback = 0;
+
+  p->state_groups = groups;
+  p->states_per_group = g;
+  p->segments = static_cast<int32_t>(n_seg);
+  p->segment_len = static_cast<int32_t>(seg_len);
+  p->lookback = lookback;
+  p->chunk = ssm::kChunk;
+  p->workgroups = chains * n_seg;
+}
+
+int check_dims(const ssm_dims* dims) {
+  if (!dims) return SSM_EINVAL;
+  if (dims->dtype != SSM_F32 && dims->dtype != SSM_BF16) return SSM_EDTYPE;
+  if (dims->batch <= 0 || dims->seqlen <= 0 || dims->dim <= 0 || dims->dstate <= 0)
+    return SSM_EINVAL;
+  if (!valid_dstate(dims->dstate)) return SSM_EINVAL;
+  // 32-bit limits of the launch arithmetic
+  const int64_t cblk = div_up(dims->dim, 64);
+  if (dims->batch * cblk > (1LL << 30)) return SSM_EINVAL;
+  return SSM_OK;
+}
+
+int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+             const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
+             void* out, float* last_state, const ssm_dims* dims, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != SSM_OK) return rc;
+  if (!u || !delta || !A || !B || !C || !out) return SSM_EINVAL;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return SSM_EALIGN;
+  const void* inputs[] = {u, delta, A, B, C, D, z, dt_bias, h0};
+  for (const void* p : inputs)
+    if (p && (p == out || p == last_state)) return SSM_EINVAL;
+  if (last_state && last_state == out) return SSM_EINVAL;
+
+  ssm_fwd_plan plan;
+  plan_forward(*dims, &plan);
+  const int64_t cblk = div_up(dims->dim, 64);
+  const int64_t chains = dims->batch * cblk;
+  const int64_t recs = chains * plan.segments;
+  if (recs * plan.state_groups > (1LL << 30) || plan.workgroups > (1LL << 31) - 1)
+    return SSM_EINVAL;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t N = dims->dstate;
+  // scratch: ticket + status (ints), then records (floats), 256-byte aligned pieces
+  auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
+  const bool need_carry = plan.segments > 1;
+  const int64_t n_int = 1 + (need_carry ? recs * plan.state_groups : 0);
+  const int64_t off_inc = up256(n_int * 4);
+  const int64_t inc_bytes = need_carry ? up256(recs * N * 64 * 4) : 0;
+  const int64_t aggb_bytes = plan.lookback ? up256(recs * N * 64 * 4) : 0;
+  const int64_t aggs_bytes = plan.lookback ? up256(recs * plan.state_groups * 64 * 4) : 0;
+  const int64_t total = off_inc + inc_bytes + aggb_bytes + aggs_bytes;
+
+  if (env_int("SSM_TEST_FAIL_ALLOC", 0) == 1) return SSM_ENOMEM;
+  char* scratch = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&scratch), static_cast<size_t>(total), st) !=
+          hipSuccess ||
+      !scratch)
+    return SSM_ENOMEM;
+
+  ssm::FwdScratch sc;
+  sc.ticket = reinterpret_cast<int*>(scratch);
+  sc.status = sc.ticket + 1;
+  sc.inc = reinterpret_cast<float*>(scratch + off_inc);
+  sc.agg_b = reinterpret_cast<float*>(scratch + off_inc + inc_bytes);
+  sc.agg_s = reinterpret_cast<float*>(scratch + off_inc + inc_bytes + aggb_bytes);
+  sc.spin_limit = env_int("SSM_TEST_SPIN_LIMIT", kDefaultSpinLimit);
+
+  ssm::FwdShape sh;
+  sh.seqlen = dims->seqlen;
+  sh.dim = dims->dim;
+  sh.chains = static_cast<int32_t>(chains);
+  sh.n_cblk = static_cast<int32_t>(cblk);
+  sh.n_seg = plan.segments;
+  sh.seg_len = plan.segment_len;
+  sh.softplus = softplus ? 1 : 0;
+  sh.lookback = plan.lookback;
+  sh.has_bias = dt_bias != nullptr;
+  sh.has_D = D != nullptr;
+  sh.has_z = z != nullptr;
+  sh.has_h0 = h0 != nullptr;
+  sh.has_last = last_state != nullptr;
+
+  ssm::FwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
+
+  rc = SSM_OK;
+  if (ssm::launch_fill_zero(sc.ticket, n_int, st) != hipSuccess) rc = SSM_ELAUNCH;
+  if (rc == SSM_OK &&
+      ssm::launch_scan_fwd(dims->dtype, plan.state_groups, plan.states_per_group, p, sc, sh,
+                           plan.workgroups, st) != hipSuccess)
+    rc = SSM_ELAUNCH;
+  if (hipFreeAsync(scratch, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                       const void* C, const float* D, const void* z, const float* dt_bias,
+                       int softplus, void* out, float* last_state, const ssm_dims* dims,
+                       void* stream) {
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, nullptr, out, last_state, dims,
+                  stream);
+}
+
+int selective_scan_fwd_h0(const void* u, const void* delta, const float* A, const void* B,
+                          const void* C, const float* D, const void* z, const float* dt_bias,
+                          int softplus, const float* h0, void* out, float* last_state,
+                          const ssm_dims* dims, void* stream) {
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, out, last_state, dims,
+                  stream);
+}
+
+int selective_state_update(float* state, const void* x, const void* dt, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* dt_bias, int softplus, void* out, const ssm_dims* dims,
+                           void* stream) {
+  int rc = check_dims(dims);
+  if (rc != SSM_OK) return rc;
+  if (dims->seqlen != 1) return SSM_EINVAL;
+  if (!state || !x || !dt || !A || !B || !C || !out) return SSM_EINVAL;
+  const void* ptrs[] = {state, x, dt, A, B, C, D, z, dt_bias, out};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return SSM_EALIGN;
+  if (dims->dstate >= 4 && (!aligned(state, 16) || !aligned(A, 16))) return SSM_EALIGN;
+  const void* inputs[] = {state, x, dt, A, B, C, D, z, dt_bias};
+  for (const void* p : inputs)
+    if (p == out) return SSM_EINVAL;
+  if (dims->batch * dims->dim * dims->dstate > (1LL << 40)) return SSM_EINVAL;
+  if (ssm::launch_state_update(dims->dtype, static_cast<int>(dims->dstate), state, x, dt, A, B,
+                               C, D, z, dt_bias, softplus ? 1 : 0, out, dims->batch, dims->dim,
+                               static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSM_ELAUNCH;
+  return SSM_OK;
+}
+
+const char* ssm_status_string(int status) {
+  switch (status) {
+    case SSM_OK: return "SSM_OK: success";
+    case SSM_EINVAL: return "SSM_EINVAL: invalid argument (dimension, null pointer or aliasing)";
+    case SSM_EDTYPE: return "SSM_EDTYPE: unsupported dtype";
+    case SSM_EALIGN: return "SSM_EALIGN: misaligned pointer";
+    case SSM_ENOMEM: return "SSM_ENOMEM: scratch allocation failed";
+    case SSM_ELAUNCH: return "SSM_ELAUNCH: kernel launch failed";
+    case SSM_ETIMEOUT: return "SSM_ETIMEOUT: a segment carry wait hit its bound";
+    default: return "SSM_UNKNOWN: unknown status code";
+  }
+}
+
+int ssm_check_device_errors(void* stream) {
+  unsigned count = 0;
+  if (ssm::read_and_clear_errors(static_cast<hipStream_t>(stream), &count) != hipSuccess)
+    return SSM_ELAUNCH;
+  return count ? SSM_ETIMEOUT : SSM_OK;
+}
+
+int ssm_fwd_plan_for(const ssm_dims* dims, ssm_fwd_plan* plan) {
+  const int rc = check_dims(dims);
+  if (rc != SSM_OK) return rc;
+  if (!plan) return SSM_EINVAL;
+  plan_forward(*dims, plan);
+  return SSM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Device helpers shared by the gfx950 selective-scan kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Activation storage: float, or bfloat16 held as its 16 raw bits.
+using bf16_t = uint16_t;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+__device__ __forceinline__ void store_act(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_act(bf16_t* p, int64_t i, float v) {
+  // gfx950 converts with round-to-nearest-even in one instruction.
+  const __bf16 r = static_cast<__bf16>(v);
+  p[i] = __builtin_bit_cast(bf16_t, r);
+}
+
+// Loads G consecutive activations of a wave-uniform row slice (B_t or C_t)
+// as float.  The address is uniform, so these become scalar loads; bfloat16
+// pairs are fetched as dwords and split with scalar shifts, which keeps the
+// unpacking off the vector ALU.  Callers guarantee 4-byte alignment of the
+// slice for G >= 2 (even offsets into a 4-byte aligned array).
+template <int G>
+__device__ __forceinline__ void load_slice(const float* p, float (&v)[G]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = p[g];
+}
+template <int G>
+__device__ __forceinline__ void load_slice(const bf16_t* p, float (&v)[G]) {
+  if constexpr (G == 1) {
+    v[0] = to_f32(p[0]);  // a lone 16-bit value: no dword to share
+  } else {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+    for (int k = 0; k < G / 2; ++k) {
+      const uint32_t word = q[k];
+      v[2 * k] = __uint_as_float(word << 16);
+      v[2 * k + 1] = __uint_as_float(word & 0xffff0000u);
+    }
+  }
+}
+
+// Hardware transcendentals (v_exp_f32 / v_log_f32 / v_rcp_f32, base 2).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(s) = max(s, 0) + log1p(e^-|s|).  log1p(e) is evaluated as
+// ln(w) * e / (w - 1) with w = 1 + e: w - 1 is exact, so the factor
+// e / (w - 1) undoes the rounding of 1 + e and keeps full relative accuracy
+// for tiny e (and gives e itself when w rounds to 1).
+__device__ __forceinline__ float softplus_f32(float s) {
+  const float e = exp2_hw(-fabsf(s) * kLog2e);
+  const float w = 1.0f + e;
+  const float wm1 = w - 1.0f;
+  const float lw = log2_hw(w) * kLn2;
+  const float lp = (wm1 == 0.0f) ? e : lw * (e * rcp_hw(wm1));
+  return fmaxf(s, 0.0f) + lp;
+}
+
+// y * SiLU(z) = y * z / (1 + e^-z)
+__device__ __forceinline__ float silu_gate(float y, float z) {
+  return y * (z * rcp_hw(1.0f + exp2_hw(-z * kLog2e)));
+}
+
+__device__ __forceinline__ int load_acquire(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_release(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace ssm

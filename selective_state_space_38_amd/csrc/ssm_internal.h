@@ -1,0 +1,70 @@
+// Internal launch interfaces between the C ABI layer (api.hip) and the
+// kernel translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Carry records exchanged between sequence segments of one channel block.
+// A record is indexed by rec = chain * n_seg + seg, and split per state group
+// (one wave per group), so every wave publishes and consumes its own part.
+struct FwdScratch {
+  int* ticket;       // [1] work-order counter (zeroed before launch)
+  int* status;       // [recs][groups] 0 empty, 1 aggregate, 2 inclusive
+  float* inc;        // [recs][N][64] state at the end of the segment
+  float* agg_b;      // [recs][N][64] segment's own final state from zero (look-back only)
+  float* agg_s;      // [recs][groups][64] segment's sum of Delta (look-back only)
+  int spin_limit;    // bound on each carry wait (iterations of s_sleep)
+};
+
+struct FwdShape {
+  int64_t seqlen;
+  int64_t dim;
+  int32_t chains;    // batch * channel blocks
+  int32_t n_cblk;    // channel blocks of 64
+  int32_t n_seg;     // sequence segments per chain
+  int32_t seg_len;   // timesteps per segment (multiple of the chunk)
+  int32_t softplus;
+  int32_t lookback;  // 1: decoupled look-back over aggregates, 0: chained
+  int32_t has_bias, has_D, has_z, has_h0, has_last;
+};
+
+struct FwdPtrs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  const float* h0;
+  void* out;
+  float* last_state;
+};
+
+// Chunk length (timesteps staged through LDS per step of the segment loop).
+constexpr int kChunk = 16;
+
+// Launches the forward kernel instance for (dtype, groups, states/group).
+// Returns hipErrorInvalidValue for an unsupported combination.
+hipError_t launch_scan_fwd(int dtype, int groups, int per_group,
+                           const FwdPtrs& p, const FwdScratch& s,
+                           const FwdShape& sh, int64_t workgroups,
+                           hipStream_t stream);
+
+hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t stream);
+
+hipError_t launch_state_update(int dtype, int dstate, float* state,
+                               const void* x, const void* dt, const float* A,
+                               const void* B, const void* C, const float* D,
+                               const void* z, const float* dt_bias,
+                               int softplus, void* out, int64_t batch,
+                               int64_t dim, hipStream_t stream);
+
+// Reads and clears this device's count of carry waits that timed out.
+hipError_t read_and_clear_errors(hipStream_t stream, unsigned* count);
+
+}  // namespace ssm

@@ -1,0 +1,135 @@
+"""Shared helpers of the GPU parity tests: seeded inputs from ``synth``, the
+GPU path through the C ABI, the oracle (full or on sampled columns) and the
+tolerance check.
+
+Tolerance (max-abs error over the compared outputs, scaled by the oracle's
+max |y| over the same outputs): 1e-4 for float32 activations, 2e-2 for
+bfloat16 activations.  The final state is held to the same bound, on the
+same max |y| scale.
+"""
+
+import contextlib
+import os
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def gpu_available():
+    return torch.cuda.is_available()
+
+
+@contextlib.contextmanager
+def env(**kv):
+    old = {k: os.environ.get(k) for k in kv}
+    try:
+        for k, v in kv.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = str(v)
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def to_dev(x, dtype):
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device="cuda", dtype=dtype)
+
+
+def act_dtype(tag):
+    return torch.bfloat16 if tag == "bf16" else torch.float32
+
+
+def gpu_forward(x, tag, *, D=True, z=True, bias=True, softplus=True, h0=None,
+                last=True):
+    from selective_state_space_38_amd import selective_scan_fwd
+    dt = act_dtype(tag)
+    res = selective_scan_fwd(
+        to_dev(x["u"], dt), to_dev(x["delta"], dt), to_dev(x["A"], torch.float32),
+        to_dev(x["B"], dt), to_dev(x["C"], dt),
+        D=to_dev(x["D"], torch.float32) if D else None,
+        z=to_dev(x["z"], dt) if z else None,
+        delta_bias=to_dev(x["dt_bias"], torch.float32) if bias else None,
+        delta_softplus=softplus, return_last_state=last,
+        h0=to_dev(h0, torch.float32) if h0 is not None else None)
+    torch.cuda.synchronize()
+    if last:
+        out, st = res
+        return out.float().cpu().numpy(), st.cpu().numpy()
+    return res.float().cpu().numpy(), None
+
+
+def oracle_forward(x, *, D=True, z=True, bias=True, softplus=True, h0=None,
+                   cols=None):
+    """Oracle outputs; with ``cols`` (list of (b, d)) only those columns:
+    returns arrays [len(cols), L] and [len(cols), N]."""
+    if cols is None:
+        return oracle.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                               x["D"] if D else None, x["z"] if z else None,
+                               x["dt_bias"] if bias else None,
+                               delta_softplus=softplus, h0=h0)
+    outs, states = [], []
+    by_b = {}
+    for i, (b, d) in enumerate(cols):
+        by_b.setdefault(b, []).append((i, d))
+    res_o = [None] * len(cols)
+    res_s = [None] * len(cols)
+    for b, items in by_b.items():
+        ds = [d for _, d in items]
+        o, s = oracle.scan_fwd(
+            x["u"][b:b + 1][:, :, ds], x["delta"][b:b + 1][:, :, ds], x["A"][ds],
+            x["B"][b:b + 1], x["C"][b:b + 1], x["D"][ds] if D else None,
+            x["z"][b:b + 1][:, :, ds] if z else None,
+            x["dt_bias"][ds] if bias else None, delta_softplus=softplus,
+            h0=None if h0 is None else h0[b:b + 1][:, ds])
+        for k, (i, _) in enumerate(items):
+            res_o[i] = o[0, :, k]
+            res_s[i] = s[0, k]
+    outs = np.stack(res_o)
+    states = np.stack(res_s)
+    return outs, states
+
+
+def check(name, got, ref, scale, tol):
+    err = float(np.max(np.abs(got.astype(np.float64) - ref))) if got.size else 0.0
+    bound = tol * scale
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert err <= bound, f"{name}: max-abs error {err:.3e} > {bound:.3e} (scale {scale:.3e})"
+    return err
+
+
+def check_forward(x, tag, got_out, got_state, ref_out, ref_state):
+    scale = float(np.max(np.abs(ref_out)))
+    tol = TOL[tag]
+    e1 = check("out", got_out, ref_out, scale, tol)
+    e2 = None
+    if got_state is not None:
+        e2 = check("last_state", got_state, ref_state, scale, tol)
+    return e1, e2, scale
+
+
+def sample_columns(bsz, dim, count, seed):
+    """Deterministic (b, d) columns including the first and last channel of
+    every batch row and the last (possibly partial) block of 64 channels."""
+    r = np.random.default_rng(seed)
+    cols = set()
+    for b in range(bsz):
+        cols.add((b, 0))
+        cols.add((b, dim - 1))
+        cols.add((b, (dim - 1) // 64 * 64))
+    while len(cols) < count:
+        cols.add((int(r.integers(bsz)), int(r.integers(dim))))
+    return sorted(cols)
