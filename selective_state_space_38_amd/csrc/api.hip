@@ -158,6 +158,17 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.has_z = z != nullptr;
   sh.has_h0 = h0 != nullptr;
   sh.has_last = last_state != nullptr;
+  {
+    // per-thread runs of the chunk tile: kChunk / groups consecutive channels
+    const int64_t ept = ssm::kChunk / plan.state_groups;
+    const int64_t esz = dims->dtype == SSM_BF16 ? 2 : 4;
+    const uintptr_t need = static_cast<uintptr_t>(ept * esz >= 16 ? 16 : ept * esz);
+    bool ok = ept * esz >= 4 && dims->dim % ept == 0;
+    const void* acts[] = {u, delta, z, out};
+    for (const void* a : acts)
+      if (a && !aligned(a, need)) ok = false;
+    sh.vec_io = ok ? 1 : 0;
+  }
 
   ssm::FwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
 

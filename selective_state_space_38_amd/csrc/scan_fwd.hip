@@ -13,12 +13,13 @@
 //
 // Work decomposition.  A workgroup owns one (batch, block of 64 channels,
 // sequence segment).  Its NG waves split the N states of every channel into
-// groups of G (lane = channel, registers = the group's states), so B_t and C_t
-// slices are wave-uniform and come in through scalar loads, and no lane ever
-// exchanges data with another lane.  Time is walked serially inside the
+// groups of G (lane = channel, registers = the group's states), so every lane
+// of a wave reads the same B_t / C_t slice (an LDS broadcast) and no lane
+// ever exchanges data with another lane.  Time is walked serially inside the
 // segment in chunks of TC steps:
-//   P  (per chunk, steps t = w mod NG): coalesced loads of dt/u, Delta,
-//      Delta*u and D*u -> LDS (double buffered);
+//   P  (per chunk, one chunk ahead): coalesced loads of dt/u for steps
+//      t = w mod NG and of the chunk's B/C rows; Delta, Delta*u, D*u and
+//      float B/C -> LDS (double buffered);
 //   S  (all steps): per state exp2(Delta*A*log2 e), h = a*h + Delta*u*B,
 //      y_partial += C*h -> LDS;
 //   E  (steps t = w mod NG): sum the NG partials, add D*u, gate with SiLU(z),
@@ -47,18 +48,26 @@ __device__ unsigned g_carry_timeouts;
 enum : int { kEmpty = 0, kAggregate = 1, kInclusive = 2 };
 
 // Waits until *p >= need (need = kAggregate waits for any publication).
-// Returns the observed status, or kEmpty on timeout.
+// Polls with plain device-coherent loads and a growing sleep, then issues one
+// acquire fence, so waiting waves neither flood memory nor keep invalidating
+// the caches the computing waves use.  Returns the observed status, or
+// kEmpty when the bound is hit.
 __device__ __forceinline__ int wait_status(const int* p, int need, int limit) {
   int spins = 0;
-  int v = load_acquire(p);
+  int v = load_relaxed(p);
   while (v < need) {
     if (++spins > limit) {
       if ((threadIdx.x & 63) == 0) atomicAdd(&g_carry_timeouts, 1u);
       return kEmpty;
     }
-    __builtin_amdgcn_s_sleep(2);
-    v = load_acquire(p);
+    if (spins < 16) {
+      __builtin_amdgcn_s_sleep(2);
+    } else {
+      __builtin_amdgcn_s_sleep(32);
+    }
+    v = load_relaxed(p);
   }
+  acquire_fence();
   return v;
 }
 
@@ -71,21 +80,32 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
     const float* __restrict__ h0, T* __restrict__ out,
     float* __restrict__ last_state, FwdScratch sc, FwdShape sh) {
   constexpr int N = NG * G;
-  constexpr int K = TC / NG;  // steps per wave in the P and E phases
-  static_assert(TC % NG == 0, "chunk must split evenly over the groups");
+  constexpr int NT = 64 * NG;          // threads
+  constexpr int EPT = TC / NG;         // tile elements per thread (one row run)
+  constexpr int TPR = 64 / EPT;        // threads per tile row
+  static_assert(TC % NG == 0 && 64 % EPT == 0, "chunk must split evenly over the groups");
+  constexpr int ESZ = static_cast<int>(sizeof(T));
+  constexpr bool kBCWords = (N * ESZ) % 4 == 0;          // B/C chunk rows are dword granular
+  constexpr int BC_UNITS = kBCWords ? TC * N * ESZ / 4 : TC * N;
+  constexpr int BCPT = (BC_UNITS + NT - 1) / NT;          // B/C dwords (or elements) per thread
+  using TileRun = Run<T, EPT>;
 
   __shared__ float s_delta[2][TC][64];
   __shared__ float s_du[2][TC][64];
   __shared__ float s_skip[2][TC][64];
+  __shared__ float s_z[2][TC][64];
+  __shared__ __align__(16) float s_B[2][TC][N];
+  __shared__ __align__(16) float s_C[2][TC][N];
   __shared__ float s_y[NG][TC][64];
   __shared__ int s_ticket;
 
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   // wave-uniform values go through readfirstlane so the compiler keeps them
-  // (and every address built from them, e.g. the B/C slices) in SGPRs
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // (and addresses built from them) in SGPRs
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  if (threadIdx.x == 0) s_ticket = atomicAdd(sc.ticket, 1);
+  if (tid == 0) s_ticket = atomicAdd(sc.ticket, 1);
   __syncthreads();
   const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
   const int seg = ticket / sh.chains;
@@ -95,45 +115,156 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
 
   const int64_t L = sh.seqlen;
   const int64_t dim = sh.dim;
-  const int64_t d = static_cast<int64_t>(cblk) * 64 + lane;
+  const int64_t ch0 = static_cast<int64_t>(cblk) * 64;
+  const int64_t d = ch0 + lane;                 // scan lane's channel
   const bool dvalid = d < dim;
-  const int64_t dc = dvalid ? d : dim - 1;  // tail lanes read a valid channel, never store
+  const int64_t dc = dvalid ? d : dim - 1;      // tail lanes read a valid channel, never store
 
   float A2[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) A2[g] = A[dc * N + w * G + g] * kLog2e;
-  const float Dd = sh.has_D ? Dv[dc] : 0.0f;
-  const float bs = sh.has_bias ? bias[dc] : 0.0f;
   const bool use_sp = sh.softplus != 0;
+
+  // tile role of this thread in the P and E phases: row tr, channels tc..tc+EPT
+  const int tr = tid / TPR;
+  const int tc = (tid - tr * TPR) * EPT;
+  const int64_t tch = ch0 + tc;                       // first channel of the run
+  const bool run_valid = tch < dim;                   // any channel of the run inside
+  const int run_last = run_valid ? static_cast<int>((dim - 1 - tch) < (EPT - 1) ? (dim - 1 - tch)
+                                                                                : (EPT - 1))
+                                 : 0;
+  // vector IO needs the whole run in range and aligned; the host guarantees
+  // alignment when sh.vec_io is set (dim % EPT == 0, aligned pointers)
+  const bool run_vec = TileRun::kCanVec && sh.vec_io != 0 && run_valid;
+  const int64_t tch_c = run_valid ? tch : (dim - 1);  // clamp for loads of dead runs
+  float rD[EPT], rbias[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int64_t ck = tch_c + (k < run_last ? k : run_last);
+    rD[k] = sh.has_D ? Dv[ck] : 0.0f;
+    rbias[k] = sh.has_bias ? bias[ck] : 0.0f;
+  }
 
   const int64_t t_begin = static_cast<int64_t>(seg) * sh.seg_len;
   const int64_t t_end = (t_begin + sh.seg_len < L) ? t_begin + sh.seg_len : L;
   const int64_t row0 = static_cast<int64_t>(b) * L;  // row of (b, t=0)
   const int rec = chain * sh.n_seg + seg;
 
-  auto act = [&](int64_t t) { return (row0 + t) * dim + dc; };
-
-  // ---- phase P helpers -------------------------------------------------
-  auto load_p = [&](int64_t c0, int n, float (&rdt)[K], float (&ru)[K]) {
+  // ---- phase P: loads one chunk ahead, LDS operands after the scan --------
+  struct Prefetch {
+    TileRun dt, uu, zz;
+    uint32_t bc[2][BCPT];
+  };
+  auto load_p = [&](int64_t c0, int n, bool out_mode, Prefetch& pf) {
+    const int r = tr < n ? tr : n - 1;                 // ragged chunk: clamp the row
+    const int64_t off = (row0 + c0 + r) * dim + tch_c;
+    if (run_vec) {
+      pf.dt.load_vec(dtp + off);
+      pf.uu.load_vec(u + off);
+      if (out_mode && sh.has_z) pf.zz.load_vec(zp + off);
+    } else {
+      pf.dt.load_elems(dtp + off, run_last);
+      pf.uu.load_elems(u + off, run_last);
+      if (out_mode && sh.has_z) pf.zz.load_elems(zp + off, run_last);
+    }
+    const int64_t base = (row0 + c0) * N;  // first B/C element of the chunk
+    if constexpr (kBCWords) {
+      const int nw = n * N * ESZ / 4;
+      const uint32_t* qb = reinterpret_cast<const uint32_t*>(Bm + base);
+      const uint32_t* qc = reinterpret_cast<const uint32_t*>(Cm + base);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int lt = w + k * NG;
-      if (lt < n) {
-        rdt[k] = to_f32(dtp[act(c0 + lt)]);
-        ru[k] = to_f32(u[act(c0 + lt)]);
+      for (int k = 0; k < BCPT; ++k) {
+        const int e = tid + k * NT;
+        const int ec = e < nw ? e : nw - 1;
+        pf.bc[0][k] = qb[ec];
+        if (out_mode) pf.bc[1][k] = qc[ec];
+      }
+    } else {
+      const int ne = n * N;
+#pragma unroll
+      for (int k = 0; k < BCPT; ++k) {
+        const int e = tid + k * NT;
+        const int ec = e < ne ? e : ne - 1;
+        pf.bc[0][k] = static_cast<uint32_t>(Bm[base + ec]);
+        if (out_mode) pf.bc[1][k] = static_cast<uint32_t>(Cm[base + ec]);
       }
     }
   };
-  auto compute_p = [&](int buf, int n, const float (&rdt)[K], const float (&ru)[K]) {
+  auto bc_float = [&](uint32_t word, int half) -> float {
+    if constexpr (ESZ == 4) {
+      return __uint_as_float(word);
+    } else {
+      return __uint_as_float(half ? (word & 0xffff0000u) : (word << 16));
+    }
+  };
+  // Every prefetched register is consumed unconditionally (only the LDS
+  // writes are predicated), so no load of this chunk can still be counted as
+  // in flight when the next chunk's loads reuse the registers.
+  auto compute_p = [&](int buf, int n, bool out_mode, const Prefetch& pf) {
+    pf.dt.consume_all();
+    pf.uu.consume_all();
+    if (out_mode && sh.has_z) pf.zz.consume_all();
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int lt = w + k * NG;
-      if (lt < n) {
-        const float s = rdt[k] + bs;
-        const float dl = use_sp ? softplus_f32(s) : s;
-        s_delta[buf][lt][lane] = dl;
-        s_du[buf][lt][lane] = dl * ru[k];
-        s_skip[buf][lt][lane] = Dd * ru[k];
+    for (int k = 0; k < BCPT; ++k) {
+      consume(pf.bc[0][k]);
+      if (out_mode) consume(pf.bc[1][k]);
+    }
+    float dl[EPT], du[EPT], sk[EPT], zf[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const float uv = pf.uu.get(k);
+      const float s = pf.dt.get(k) + rbias[k];
+      dl[k] = use_sp ? softplus_f32(s) : s;
+      du[k] = dl[k] * uv;
+      sk[k] = rD[k] * uv;
+      zf[k] = (out_mode && sh.has_z) ? pf.zz.get(k) : 0.0f;
+    }
+    if (tr < n) {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) {
+        s_delta[buf][tr][tc + k] = dl[k];
+        s_du[buf][tr][tc + k] = du[k];
+        if (out_mode) {
+          s_skip[buf][tr][tc + k] = sk[k];
+          s_z[buf][tr][tc + k] = zf[k];
+        }
+      }
+    }
+    float* sb = &s_B[buf][0][0];
+    float* scc = &s_C[buf][0][0];
+    if constexpr (kBCWords) {
+      const int nw = n * N * ESZ / 4;
+#pragma unroll
+      for (int k = 0; k < BCPT; ++k) {
+        const int e = tid + k * NT;
+        const float b0 = bc_float(pf.bc[0][k], 0), b1 = bc_float(pf.bc[0][k], 1);
+        const float c0v = out_mode ? bc_float(pf.bc[1][k], 0) : 0.0f;
+        const float c1v = out_mode ? bc_float(pf.bc[1][k], 1) : 0.0f;
+        if (e < nw) {
+          if constexpr (ESZ == 4) {
+            sb[e] = b0;
+            if (out_mode) scc[e] = c0v;
+          } else {
+            sb[2 * e] = b0;
+            sb[2 * e + 1] = b1;
+            if (out_mode) {
+              scc[2 * e] = c0v;
+              scc[2 * e + 1] = c1v;
+            }
+          }
+        }
+      }
+    } else {
+      const int ne = n * N;
+#pragma unroll
+      for (int k = 0; k < BCPT; ++k) {
+        const int e = tid + k * NT;
+        const float bv = to_f32(static_cast<T>(pf.bc[0][k]));
+        const float cv = out_mode ? to_f32(static_cast<T>(pf.bc[1][k])) : 0.0f;
+        if (e < ne) {
+          sb[e] = bv;
+          if (out_mode) scc[e] = cv;
+        }
       }
     }
   };
@@ -143,32 +274,40 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g) hA[g] = 0.0f;
     sum_delta = 0.0f;
-    float rdt[K], ru[K];
+    Prefetch pf;
     int64_t c0 = t_begin;
     int n0 = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
-    load_p(c0, n0, rdt, ru);
-    compute_p(0, n0, rdt, ru);
-    __syncthreads();
+    load_p(c0, n0, false, pf);
+    compute_p(0, n0, false, pf);
+    drain_vmem();
+    lds_barrier();
     int buf = 0;
     while (c0 < t_end) {
       const int n = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
       const int64_t c1 = c0 + n;
       const int n1 = static_cast<int>((t_end - c1 < TC) ? t_end - c1 : TC);
-      if (n1 > 0) load_p(c1, n1, rdt, ru);
-      for (int lt = 0; lt < n; ++lt) {
+      // the last chunk reloads itself instead of skipping the prefetch, so
+      // loads and their consumption are unconditional in the loop body
+      load_p(n1 > 0 ? c1 : c0, n1 > 0 ? n1 : n, false, pf);
+      auto step = [&](int lt) {
         const float dl = s_delta[buf][lt][lane];
         const float du = s_du[buf][lt][lane];
-        float bv[G];
-        load_slice<G>(Bm + ((row0 + c0 + lt) * N + w * G), bv);
+        const float* bv = &s_B[buf][lt][w * G];
         sum_delta += dl;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float a = exp2_hw(dl * A2[g]);
           hA[g] = fmaf(a, hA[g], du * bv[g]);
         }
+      };
+      if (n == TC) {
+#pragma unroll
+        for (int lt = 0; lt < TC; ++lt) step(lt);
+      } else {
+        for (int lt = 0; lt < n; ++lt) step(lt);
       }
-      if (n1 > 0) compute_p(buf ^ 1, n1, rdt, ru);
-      __syncthreads();
+      compute_p(buf ^ 1, n1 > 0 ? n1 : 0, false, pf);
+      lds_barrier();
       buf ^= 1;
       c0 = c1;
     }
@@ -176,33 +315,28 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
 
   // ---- output pass: from carry-in h, produce out and the final state -----
   auto output_pass = [&](float (&h)[G]) {
-    float rdt[K], ru[K], rz[K];
+    Prefetch pf;
     int64_t c0 = t_begin;
     int n0 = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
-    load_p(c0, n0, rdt, ru);
-    compute_p(0, n0, rdt, ru);
-    __syncthreads();
+    load_p(c0, n0, true, pf);
+    compute_p(0, n0, true, pf);
+    drain_vmem();
+    lds_barrier();
     int buf = 0;
     while (c0 < t_end) {
       const int n = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
       const int64_t c1 = c0 + n;
       const int n1 = static_cast<int>((t_end - c1 < TC) ? t_end - c1 : TC);
-      if (n1 > 0) load_p(c1, n1, rdt, ru);
-      if (sh.has_z) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const int lt = w + k * NG;
-          if (lt < n) rz[k] = to_f32(zp[act(c0 + lt)]);
-        }
-      }
-      // phase S
-      for (int lt = 0; lt < n; ++lt) {
+      // every global load of the iteration is issued here, one chunk ahead,
+      // and consumed by compute_p after the scan of the current chunk
+      load_p(n1 > 0 ? c1 : c0, n1 > 0 ? n1 : n, true, pf);
+      // phase S: a full chunk is unrolled completely, so the scheduler can
+      // read the LDS operands of later steps while earlier steps compute
+      auto step = [&](int lt) {
         const float dl = s_delta[buf][lt][lane];
         const float du = s_du[buf][lt][lane];
-        const int64_t brow = (row0 + c0 + lt) * N + w * G;
-        float bv[G], cv[G];
-        load_slice<G>(Bm + brow, bv);
-        load_slice<G>(Cm + brow, cv);
+        const float* bv = &s_B[buf][lt][w * G];
+        const float* cv = &s_C[buf][lt][w * G];
         float y = 0.0f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -211,23 +345,59 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
           y = fmaf(cv[g], h[g], y);
         }
         s_y[w][lt][lane] = y;
+      };
+      if (n == TC) {
+#pragma unroll
+        for (int lt = 0; lt < TC; ++lt) step(lt);
+      } else {
+        for (int lt = 0; lt < n; ++lt) step(lt);
       }
-      __syncthreads();
-      if (n1 > 0) compute_p(buf ^ 1, n1, rdt, ru);
-      // phase E
+      lds_barrier();
+      compute_p(buf ^ 1, n1 > 0 ? n1 : 0, true, pf);
+      // phase E: this thread's run of the tile
+      if (tr < n && run_valid) {
+        float yv[EPT];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int lt = w + k * NG;
-        if (lt < n) {
-          float y = s_y[0][lt][lane];
+        for (int k = 0; k < EPT; ++k) {
+          float y = s_y[0][tr][tc + k];
 #pragma unroll
-          for (int q = 1; q < NG; ++q) y += s_y[q][lt][lane];
-          y += s_skip[buf][lt][lane];
-          if (sh.has_z) y = silu_gate(y, rz[k]);
-          if (dvalid) store_act(out, act(c0 + lt), y);
+          for (int q = 1; q < NG; ++q) y += s_y[q][tr][tc + k];
+          y += s_skip[buf][tr][tc + k];
+          if (sh.has_z) y = silu_gate(y, s_z[buf][tr][tc + k]);
+          yv[k] = y;
+        }
+        T* op = out + (row0 + c0 + tr) * dim + tch;
+        if (run_vec) {
+          TileRun o;
+#pragma unroll
+          for (int k = 0; k < TileRun::NW; ++k) o.w[k] = 0;
+#pragma unroll
+          for (int k = 0; k < EPT; ++k) {
+            T v;
+            store_act(&v, 0, yv[k]);
+            if constexpr (ESZ == 4) {
+              o.w[k] = __builtin_bit_cast(uint32_t, v);
+            } else {
+              o.w[k / 2] |= static_cast<uint32_t>(v) << (16 * (k % 2));
+            }
+          }
+          uint32_t* q = reinterpret_cast<uint32_t*>(op);
+          if constexpr (TileRun::NW >= 4) {
+#pragma unroll
+            for (int i = 0; i < TileRun::NW; i += 4)
+              *reinterpret_cast<uint4*>(q + i) = make_uint4(o.w[i], o.w[i + 1], o.w[i + 2], o.w[i + 3]);
+          } else if constexpr (TileRun::NW == 2) {
+            *reinterpret_cast<uint2*>(q) = make_uint2(o.w[0], o.w[1]);
+          } else {
+            q[0] = o.w[0];
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < EPT; ++k)
+            if (k <= run_last) store_act(op, k, yv[k]);
         }
       }
-      __syncthreads();
+      lds_barrier();
       buf ^= 1;
       c0 = c1;
     }

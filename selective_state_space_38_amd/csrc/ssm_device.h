@@ -72,8 +72,89 @@ __device__ __forceinline__ float silu_gate(float y, float z) {
   return y * (z * rcp_hw(1.0f + exp2_hw(-z * kLog2e)));
 }
 
-__device__ __forceinline__ int load_acquire(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also waits for
+// every outstanding global load and store of the wave (its fence covers
+// global memory), which would stall on the loads prefetched for the next
+// chunk; here only LDS operations (lgkmcnt) are drained.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_s_barrier();
+}
+
+// Waits for every outstanding global load of the wave.  Used once before a
+// long loop so that values loaded in its set-up are not treated as possibly
+// in flight inside every iteration.
+__device__ __forceinline__ void drain_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), lgkmcnt/expcnt untouched
+}
+
+// Marks a register as used here.  Placed on prefetched values at the point
+// where they are consumed, it stops the compiler from sinking the use into a
+// predicated block, which would leave the load looking in flight on the other
+// path (and force a full memory wait at the top of the next loop iteration).
+__device__ __forceinline__ void consume(uint32_t x) { asm volatile("" : : "v"(x)); }
+
+// A run of EPT consecutive activations (one row of a chunk tile) in their
+// storage format, packed in dwords.  Vector loads and stores are used when
+// the run is aligned (the caller decides); otherwise element by element.
+template <typename T, int EPT>
+struct Run {
+  static constexpr int kBytes = EPT * static_cast<int>(sizeof(T));
+  static constexpr int NW = kBytes >= 4 ? kBytes / 4 : 1;
+  static constexpr bool kCanVec = kBytes >= 4;
+  uint32_t w[NW];
+
+  __device__ __forceinline__ void load_vec(const T* p) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    if constexpr (NW >= 4) {
+#pragma unroll
+      for (int i = 0; i < NW; i += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(q + i);
+        w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+      }
+    } else if constexpr (NW == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(q);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+      w[0] = q[0];
+    }
+  }
+  // element path: element k comes from p[min(k, last)]
+  __device__ __forceinline__ void load_elems(const T* p, int last) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = 0;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const T v = p[k < last ? k : last];
+      if constexpr (sizeof(T) == 4) {
+        w[k] = __builtin_bit_cast(uint32_t, v);
+      } else {
+        w[k / 2] |= static_cast<uint32_t>(v) << (16 * (k % 2));
+      }
+    }
+  }
+  __device__ __forceinline__ void consume_all() const {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) consume(w[i]);
+  }
+  __device__ __forceinline__ float get(int k) const {
+    if constexpr (sizeof(T) == 4) {
+      return __uint_as_float(w[k]);
+    } else {
+      const uint32_t word = w[k / 2];
+      return __uint_as_float((k % 2) ? (word & 0xffff0000u) : (word << 16));
+    }
+  }
+};
+
+// Polling load: coherent at device scope but without the cache invalidation
+// an acquire carries; pair with acquire_fence() once the value is seen.
+__device__ __forceinline__ int load_relaxed(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void acquire_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 __device__ __forceinline__ void store_release(int* p, int v) {

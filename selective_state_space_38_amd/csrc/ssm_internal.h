@@ -29,6 +29,7 @@ struct FwdShape {
   int32_t softplus;
   int32_t lookback;  // 1: decoupled look-back over aggregates, 0: chained
   int32_t has_bias, has_D, has_z, has_h0, has_last;
+  int32_t vec_io;    // activation rows may be moved in aligned vector runs
 };
 
 struct FwdPtrs {
