@@ -6,8 +6,8 @@ One step = one selective_scan_fwd over the Mamba-2.8B-shaped layer
 state and arithmetic) followed by one selective_state_update over the decode
 workload (256 sequences x 5120 channels x 16 states).  Inputs are seeded
 synthetic data (synth.make) already resident in HBM; decode states rotate
-over three buffers so the 256 MB Infinity Cache cannot hold them between
-steps.
+over six buffers (504 MB) so the 256 MB Infinity Cache cannot hold them
+between steps.
 
 Prints one JSON line.  `value` is tokens*channels processed per second over
 the whole step (forward B*L*D plus decode B*D).  `roofline` describes the
@@ -139,7 +139,7 @@ def main():
     A, Dv, bias = up(x["A"]), up(x["D"]), up(x["dt_bias"])
     out = torch.empty_like(u)
     last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
-    n_rot = 3
+    n_rot = 6  # 6 x 84 MB of decode state: twice the 256 MB Infinity Cache
     states = [up(dec["state"]) for _ in range(n_rot)]
     dx, ddt, dz = up(dec["u"], dact), up(dec["delta"], dact), up(dec["z"], dact)
     dB, dC = up(dec["B"], dact), up(dec["C"], dact)

@@ -44,13 +44,17 @@ int states_per_group(int64_t n) {
 }
 
 // Chooses state groups, segments and the carry mode for a forward call.
-// Chained segments cost no extra arithmetic but only one segment per channel
-// block runs at a time; look-back segments all run at once but each (except
-// the first) scans its inputs twice.  Chained mode is used when the channel
-// blocks alone give at least half the chip's SIMDs a wave.
+// When the channel blocks alone give at least half the chip's SIMDs a wave,
+// each channel block is scanned by one workgroup over the whole sequence (a
+// single segment: measured faster than chained segments, whose waiting
+// workgroups occupy CU slots).  Otherwise the sequence is cut into segments
+// that run concurrently and exchange carries by decoupled look-back; a
+// segment whose predecessor has already published its final state skips its
+// own aggregate pass.
 void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
   const int g = states_per_group(d.dstate);
   const int groups = static_cast<int>(d.dstate / g);
+  const int chunk = ssm::chunk_for_groups(groups);
   const int64_t cblk = div_up(d.dim, 64);
   const int64_t chains = d.batch * cblk;
   const int64_t waves_per_slice = chains * groups;
@@ -60,12 +64,14 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
 
   int64_t seg_len;
   if (!lookback) {
-    seg_len = 1024;  // hand-off granularity that lets idle CUs pick up work
+    seg_len = d.seqlen;
   } else {
-    // enough segments for ~4096 waves, each at least 256 steps
+    // enough segments for ~4096 waves, each at least 8192 steps when the
+    // sequence allows (the best measured trade of parallelism against the
+    // extra aggregate pass)
     const int64_t want = div_up(4096, waves_per_slice);
     seg_len = div_up(d.seqlen, want);
-    if (seg_len < 256) seg_len = 256;
+    if (seg_len < 8192) seg_len = 8192;
   }
   const int force_seg = env_int("SSM_FORCE_SEGMENT", 0);
   if (force_seg > 0) seg_len = force_seg;
@@ -79,7 +85,7 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
   p->segments = static_cast<int32_t>(n_seg);
   p->segment_len = static_cast<int32_t>(seg_len);
   p->lookback = lookback;
-  p->chunk = ssm::kChunk;
+  p->chunk = chunk;
   p->workgroups = chains * n_seg;
 }
 
@@ -89,9 +95,10 @@ int check_dims(const ssm_dims* dims) {
   if (dims->batch <= 0 || dims->seqlen <= 0 || dims->dim <= 0 || dims->dstate <= 0)
     return SSM_EINVAL;
   if (!valid_dstate(dims->dstate)) return SSM_EINVAL;
-  // 32-bit limits of the launch arithmetic
+  // 32-bit limits of the launch arithmetic (segment length, channel blocks)
   const int64_t cblk = div_up(dims->dim, 64);
   if (dims->batch * cblk > (1LL << 30)) return SSM_EINVAL;
+  if (dims->seqlen > (1LL << 31) - 1024) return SSM_EINVAL;
   return SSM_OK;
 }
 
@@ -160,7 +167,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.has_last = last_state != nullptr;
   {
     // per-thread runs of the chunk tile: kChunk / groups consecutive channels
-    const int64_t ept = ssm::kChunk / plan.state_groups;
+    const int64_t ept = plan.chunk / plan.state_groups;
     const int64_t esz = dims->dtype == SSM_BF16 ? 2 : 4;
     const uintptr_t need = static_cast<uintptr_t>(ept * esz >= 16 ? 16 : ept * esz);
     bool ok = ept * esz >= 4 && dims->dim % ept == 0;

@@ -35,6 +35,9 @@
 //                     then walks back over predecessors' aggregates until it
 //                     finds a published final state, combines, publishes its
 //                     own final state and only then produces its outputs.
+//                     If the predecessor's final state is already published
+//                     when the segment starts, it skips straight to its
+//                     outputs (and publishes its final state at the end).
 // Every wait is bounded; a wait that hits the bound bumps a device error
 // counter and continues with the carry gathered so far.
 
@@ -90,10 +93,10 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   constexpr int BCPT = (BC_UNITS + NT - 1) / NT;          // B/C dwords (or elements) per thread
   using TileRun = Run<T, EPT>;
 
+
+
   __shared__ float s_delta[2][TC][64];
   __shared__ float s_du[2][TC][64];
-  __shared__ float s_skip[2][TC][64];
-  __shared__ float s_z[2][TC][64];
   __shared__ __align__(16) float s_B[2][TC][N];
   __shared__ __align__(16) float s_C[2][TC][N];
   __shared__ float s_y[NG][TC][64];
@@ -200,7 +203,10 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   // Every prefetched register is consumed unconditionally (only the LDS
   // writes are predicated), so no load of this chunk can still be counted as
   // in flight when the next chunk's loads reuse the registers.
-  auto compute_p = [&](int buf, int n, bool out_mode, const Prefetch& pf) {
+  // D*u and z of the chunk's tile run stay in the P/E thread's registers
+  // (sk, zf): the thread that prepares a run is the one that gates it.
+  auto compute_p = [&](int buf, int n, bool out_mode, const Prefetch& pf, float (&sk)[EPT],
+                       float (&zf)[EPT]) {
     pf.dt.consume_all();
     pf.uu.consume_all();
     if (out_mode && sh.has_z) pf.zz.consume_all();
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       consume(pf.bc[0][k]);
       if (out_mode) consume(pf.bc[1][k]);
     }
-    float dl[EPT], du[EPT], sk[EPT], zf[EPT];
+    float dl[EPT], du[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
       const float uv = pf.uu.get(k);
@@ -224,10 +230,6 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       for (int k = 0; k < EPT; ++k) {
         s_delta[buf][tr][tc + k] = dl[k];
         s_du[buf][tr][tc + k] = du[k];
-        if (out_mode) {
-          s_skip[buf][tr][tc + k] = sk[k];
-          s_z[buf][tr][tc + k] = zf[k];
-        }
       }
     }
     float* sb = &s_B[buf][0][0];
@@ -275,10 +277,11 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
     for (int g = 0; g < G; ++g) hA[g] = 0.0f;
     sum_delta = 0.0f;
     Prefetch pf;
+    float sk[EPT], zf[EPT];
     int64_t c0 = t_begin;
     int n0 = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
     load_p(c0, n0, false, pf);
-    compute_p(0, n0, false, pf);
+    compute_p(0, n0, false, pf, sk, zf);
     drain_vmem();
     lds_barrier();
     int buf = 0;
@@ -292,7 +295,9 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       auto step = [&](int lt) {
         const float dl = s_delta[buf][lt][lane];
         const float du = s_du[buf][lt][lane];
-        const float* bv = &s_B[buf][lt][w * G];
+        float bv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) bv[g] = s_B[buf][lt][w * G + g];
         sum_delta += dl;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -306,7 +311,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       } else {
         for (int lt = 0; lt < n; ++lt) step(lt);
       }
-      compute_p(buf ^ 1, n1 > 0 ? n1 : 0, false, pf);
+      compute_p(buf ^ 1, n1 > 0 ? n1 : 0, false, pf, sk, zf);
       lds_barrier();
       buf ^= 1;
       c0 = c1;
@@ -316,10 +321,11 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   // ---- output pass: from carry-in h, produce out and the final state -----
   auto output_pass = [&](float (&h)[G]) {
     Prefetch pf;
+    float sk[EPT], zf[EPT], sk_next[EPT], zf_next[EPT];
     int64_t c0 = t_begin;
     int n0 = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
     load_p(c0, n0, true, pf);
-    compute_p(0, n0, true, pf);
+    compute_p(0, n0, true, pf, sk, zf);
     drain_vmem();
     lds_barrier();
     int buf = 0;
@@ -335,8 +341,12 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       auto step = [&](int lt) {
         const float dl = s_delta[buf][lt][lane];
         const float du = s_du[buf][lt][lane];
-        const float* bv = &s_B[buf][lt][w * G];
-        const float* cv = &s_C[buf][lt][w * G];
+        float bv[G], cv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          bv[g] = s_B[buf][lt][w * G + g];
+          cv[g] = s_C[buf][lt][w * G + g];
+        }
         float y = 0.0f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -353,7 +363,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
         for (int lt = 0; lt < n; ++lt) step(lt);
       }
       lds_barrier();
-      compute_p(buf ^ 1, n1 > 0 ? n1 : 0, true, pf);
+      compute_p(buf ^ 1, n1 > 0 ? n1 : 0, true, pf, sk_next, zf_next);
       // phase E: this thread's run of the tile
       if (tr < n && run_valid) {
         float yv[EPT];
@@ -362,8 +372,8 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
           float y = s_y[0][tr][tc + k];
 #pragma unroll
           for (int q = 1; q < NG; ++q) y += s_y[q][tr][tc + k];
-          y += s_skip[buf][tr][tc + k];
-          if (sh.has_z) y = silu_gate(y, s_z[buf][tr][tc + k]);
+          y += sk[k];
+          if (sh.has_z) y = silu_gate(y, zf[k]);
           yv[k] = y;
         }
         T* op = out + (row0 + c0 + tr) * dim + tch;
@@ -397,6 +407,11 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
             if (k <= run_last) store_act(op, k, yv[k]);
         }
       }
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) {
+        sk[k] = sk_next[k];
+        zf[k] = zf_next[k];
+      }
       lds_barrier();
       buf ^= 1;
       c0 = c1;
@@ -419,6 +434,13 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g)
       h[g] = (st == kInclusive) ? sc.inc[ps + (gidx + g) * 64 + lane] : 0.0f;
+  } else if (load_relaxed(&sc.status[(rec - 1) * NG + w]) == kInclusive) {
+    // look-back mode, but the predecessor already published its final state:
+    // no aggregate pass needed, behave like a chained segment
+    acquire_fence();
+    const int64_t ps = static_cast<int64_t>(rec - 1) * N * 64;
+#pragma unroll
+    for (int g = 0; g < G; ++g) h[g] = sc.inc[ps + (gidx + g) * 64 + lane];
   } else {
     float hA[G];
     float sum_delta;
@@ -498,7 +520,7 @@ hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t stream) {
 template <typename T, int NG, int G>
 static hipError_t launch_typed(const FwdPtrs& p, const FwdScratch& s, const FwdShape& sh,
                                int64_t workgroups, hipStream_t stream) {
-  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, kChunk>), dim3(static_cast<unsigned>(workgroups)),
+  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, chunk_for_groups(NG)>), dim3(static_cast<unsigned>(workgroups)),
                      dim3(64 * NG), 0, stream, static_cast<const T*>(p.u),
                      static_cast<const T*>(p.delta), p.A, static_cast<const T*>(p.B),
                      static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), p.dt_bias,

@@ -24,31 +24,6 @@ __device__ __forceinline__ void store_act(bf16_t* p, int64_t i, float v) {
   p[i] = __builtin_bit_cast(bf16_t, r);
 }
 
-// Loads G consecutive activations of a wave-uniform row slice (B_t or C_t)
-// as float.  The address is uniform, so these become scalar loads; bfloat16
-// pairs are fetched as dwords and split with scalar shifts, which keeps the
-// unpacking off the vector ALU.  Callers guarantee 4-byte alignment of the
-// slice for G >= 2 (even offsets into a 4-byte aligned array).
-template <int G>
-__device__ __forceinline__ void load_slice(const float* p, float (&v)[G]) {
-#pragma unroll
-  for (int g = 0; g < G; ++g) v[g] = p[g];
-}
-template <int G>
-__device__ __forceinline__ void load_slice(const bf16_t* p, float (&v)[G]) {
-  if constexpr (G == 1) {
-    v[0] = to_f32(p[0]);  // a lone 16-bit value: no dword to share
-  } else {
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-#pragma unroll
-    for (int k = 0; k < G / 2; ++k) {
-      const uint32_t word = q[k];
-      v[2 * k] = __uint_as_float(word << 16);
-      v[2 * k + 1] = __uint_as_float(word & 0xffff0000u);
-    }
-  }
-}
-
 // Hardware transcendentals (v_exp_f32 / v_log_f32 / v_rcp_f32, base 2).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }

@@ -46,8 +46,11 @@ struct FwdPtrs {
   float* last_state;
 };
 
-// Chunk length (timesteps staged through LDS per step of the segment loop).
-constexpr int kChunk = 16;
+// Chunk length (timesteps staged through LDS per step of the segment loop):
+// 32 for up to four state groups, 16 for eight or more (LDS holds the partial
+// readouts of every group).  Segments are a multiple of the largest chunk.
+constexpr int kChunk = 32;
+constexpr int chunk_for_groups(int groups) { return groups >= 8 ? 16 : 32; }
 
 // Launches the forward kernel instance for (dtype, groups, states/group).
 // Returns hipErrorInvalidValue for an unsupported combination.

@@ -6,15 +6,23 @@
 // S6; "Mamba / MambaMini" Q&A on Delta*B and SiLU; CSDN "Mamba" 3(1) for D).
 //
 // The step is a pure read-modify-write stream over the float32 state, so it
-// is laid out for HBM: each lane owns Q = min(N, 4) consecutive states of one
-// channel (one 16-byte load and store), the N/Q lanes of a channel are
-// neighbours, and the readout C . h is reduced across them with shuffles.
+// is laid out for HBM (see the kernel comment).  The shuffle partners of a
+// lane are always in range: total = B*D*LPC is a multiple of LPC, which
+// divides 64.
 
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
 namespace ssm {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One lane owns Q = min(N, 8) consecutive states of one channel (two 16-byte
+// vector loads and stores), the N/Q lanes of a channel are neighbours and
+// reduce the readout C . h with shuffles.  The state is streamed once, so it
+// is read and written with non-temporal hints.  (4 and 16 states per lane
+// measured slower: 16 makes the per-instruction accesses of a wave strided.)
+constexpr int kDecodeStatesPerLane = 8;
 template <typename T, int N>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ x, const T* __restrict__ dtp,
@@ -22,57 +30,87 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     const float* __restrict__ Dv, const T* __restrict__ zp,
     const float* __restrict__ bias, int softplus, T* __restrict__ out,
     int64_t batch, int64_t dim) {
-  constexpr int Q = N < 4 ? N : 4;   // states per lane
-  constexpr int LPC = N / Q;         // lanes per channel
+  constexpr int Q = N < kDecodeStatesPerLane ? N : kDecodeStatesPerLane;
+  constexpr int LPC = N / Q;               // lanes per channel
+  constexpr int NV = Q >= 4 ? Q / 4 : 0;   // 16-byte vectors per lane
   const int64_t total = batch * dim * LPC;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const bool valid = i < total;
-  const int64_t ic = valid ? i : total - 1;
-  const int64_t bd = ic / LPC;               // (b, d) flattened
+  const int64_t ic = i < total ? i : total - 1;
+  const int64_t bd = ic / LPC;
   const int q = static_cast<int>(ic - bd * LPC);
   const int64_t b = bd / dim;
   const int64_t d = bd - b * dim;
 
-  float s = to_f32(dtp[bd]) + (bias ? bias[d] : 0.0f);
+  float h[Q];
+  float* hp = state + bd * N + q * Q;
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const f32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp) + v);
+      h[4 * v] = hv.x; h[4 * v + 1] = hv.y; h[4 * v + 2] = hv.z; h[4 * v + 3] = hv.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < Q; ++j) h[j] = __builtin_nontemporal_load(hp + j);
+  }
+  const float s = to_f32(dtp[bd]) + (bias ? bias[d] : 0.0f);
   const float dl = softplus ? softplus_f32(s) : s;
   const float xv = to_f32(x[bd]);
   const float du = dl * xv;
-
-  float* hp = state + bd * N + q * Q;
   const float* ap = A + d * N + q * Q;
   const T* bp = Bm + b * N + q * Q;
   const T* cp = Cm + b * N + q * Q;
-
-  float h[Q];
-  float a2[Q];
-  if constexpr (Q == 4) {
-    const float4 hv = *reinterpret_cast<const float4*>(hp);
-    const float4 av = *reinterpret_cast<const float4*>(ap);
-    h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
-    a2[0] = av.x; a2[1] = av.y; a2[2] = av.z; a2[3] = av.w;
+  float a2[Q], bv[Q], cv[Q];
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const float4 av = reinterpret_cast<const float4*>(ap)[v];
+      a2[4 * v] = av.x; a2[4 * v + 1] = av.y; a2[4 * v + 2] = av.z; a2[4 * v + 3] = av.w;
+      if constexpr (sizeof(T) == 2) {
+        const uint2 bw = reinterpret_cast<const uint2*>(bp)[v];
+        const uint2 cw = reinterpret_cast<const uint2*>(cp)[v];
+        bv[4 * v] = __uint_as_float(bw.x << 16); bv[4 * v + 1] = __uint_as_float(bw.x & 0xffff0000u);
+        bv[4 * v + 2] = __uint_as_float(bw.y << 16); bv[4 * v + 3] = __uint_as_float(bw.y & 0xffff0000u);
+        cv[4 * v] = __uint_as_float(cw.x << 16); cv[4 * v + 1] = __uint_as_float(cw.x & 0xffff0000u);
+        cv[4 * v + 2] = __uint_as_float(cw.y << 16); cv[4 * v + 3] = __uint_as_float(cw.y & 0xffff0000u);
+      } else {
+        const float4 bw = reinterpret_cast<const float4*>(bp)[v];
+        const float4 cw = reinterpret_cast<const float4*>(cp)[v];
+        bv[4 * v] = bw.x; bv[4 * v + 1] = bw.y; bv[4 * v + 2] = bw.z; bv[4 * v + 3] = bw.w;
+        cv[4 * v] = cw.x; cv[4 * v + 1] = cw.y; cv[4 * v + 2] = cw.z; cv[4 * v + 3] = cw.w;
+      }
+    }
   } else {
 #pragma unroll
-    for (int j = 0; j < Q; ++j) { h[j] = hp[j]; a2[j] = ap[j]; }
+    for (int j = 0; j < Q; ++j) {
+      a2[j] = ap[j];
+      bv[j] = to_f32(bp[j]);
+      cv[j] = to_f32(cp[j]);
+    }
   }
   float y = 0.0f;
 #pragma unroll
   for (int j = 0; j < Q; ++j) {
     const float a = exp2_hw(dl * (a2[j] * kLog2e));
-    h[j] = fmaf(a, h[j], du * to_f32(bp[j]));
-    y = fmaf(to_f32(cp[j]), h[j], y);
+    h[j] = fmaf(a, h[j], du * bv[j]);
+    y = fmaf(cv[j], h[j], y);
   }
-  if (valid) {
-    if constexpr (Q == 4) {
-      *reinterpret_cast<float4*>(hp) = make_float4(h[0], h[1], h[2], h[3]);
+  if (i < total) {
+    if constexpr (NV > 0) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const f32x4 hv = {h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
+        __builtin_nontemporal_store(hv, reinterpret_cast<f32x4*>(hp) + v);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < Q; ++j) hp[j] = h[j];
+      for (int j = 0; j < Q; ++j) __builtin_nontemporal_store(h[j], hp + j);
     }
   }
   // reduce the partial readouts of the channel's LPC neighbouring lanes
 #pragma unroll
   for (int off = 1; off < LPC; off <<= 1) y += __shfl_xor(y, off, 64);
-  if (valid && q == 0) {
+  if (i < total && q == 0) {
     y += (Dv ? Dv[d] : 0.0f) * xv;
     if (zp) y = silu_gate(y, to_f32(zp[bd]));
     store_act(out, bd, y);
@@ -84,8 +122,8 @@ static hipError_t launch_n(int n, float* state, const void* x, const void* dt, c
                            const void* B, const void* C, const float* D, const void* z,
                            const float* bias, int softplus, void* out, int64_t batch,
                            int64_t dim, hipStream_t stream) {
-  const int lpc = n < 4 ? 1 : n / 4;
-  const int64_t total = batch * dim * lpc;
+  const int q = n < kDecodeStatesPerLane ? n : kDecodeStatesPerLane;
+  const int64_t total = batch * dim * (n / q);
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
   const dim3 grid(static_cast<unsigned>(blocks));
