@@ -59,19 +59,49 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate host time budget of the oracle baseline")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="before timing, run one plain device copy of this many MiB "
+                        "(a known-size reference for hardware byte counters)")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_traffic_mamba2p8b.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_38_amd", "csrc", f)
+                  for f in ("scan_fwd.hip", "ssm_device.h", "ssm_internal.h", "api.hip")]
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per forward launch from the committed counter summary, or None
+    when it was taken on another workload or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(x, w, dec, budget_s):
     """Times the oracle (as it stands) on a bounded prefix of the workload:
-    batch row 0, all channels, the first L' steps, sized to ~budget_s; plus
-    one decode step on a 32-sequence slice of the decode workload."""
+    every batch row and channel, the first L' steps, L' sized to ~budget_s;
+    plus one decode step on a 32-sequence slice of the decode workload."""
     import oracle
 
     def sample(L):
         sl = slice(0, L)
-        return (x["u"][:1, sl], x["delta"][:1, sl], x["A"], x["B"][:1, sl], x["C"][:1, sl],
-                x["D"], x["z"][:1, sl], x["dt_bias"])
+        return (x["u"][:, sl], x["delta"][:, sl], x["A"], x["B"][:, sl], x["C"][:, sl],
+                x["D"], x["z"][:, sl], x["dt_bias"])
 
     t0 = time.perf_counter()
     oracle.scan_fwd(*sample(8))
@@ -86,7 +116,7 @@ def cpu_baseline(x, w, dec, budget_s):
                         dec["B"][:nb], dec["C"][:nb], dec["D"], dec["z"][:nb],
                         dec["dt_bias"])
     t_dec = time.perf_counter() - t0
-    tokch = L * w.dim + nb * dec_dim(dec)
+    tokch = w.batch * L * w.dim + nb * dec_dim(dec)
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -97,9 +127,9 @@ def cpu_baseline(x, w, dec, budget_s):
         "unit": "tokens·channels/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"float64 NumPy oracle, single-threaded ufuncs: forward on batch row 0, "
-                   f"{L} of {w.seqlen} steps, all {w.dim} channels ({t_fwd:.1f} s) + one "
-                   f"decode step on {nb} sequences ({t_dec:.2f} s)"),
+        "sample": (f"float64 NumPy oracle, single-threaded ufuncs: forward on all {w.batch} "
+                   f"batch rows and {w.dim} channels, first {L} of {w.seqlen} steps "
+                   f"({t_fwd:.1f} s) + one decode step on {nb} sequences ({t_dec:.2f} s)"),
         "host_cpus_available": len(os.sched_getaffinity(0)),
         "blas_threads_idle": blas_threads,
     }
@@ -146,6 +176,16 @@ def main():
     dA, dD, dbias = up(dec["A"]), up(dec["D"]), up(dec["dt_bias"])
     dout = torch.empty_like(dx)
     torch.cuda.synchronize()
+    if args.copy_calibration_mb > 0:
+        nbytes = args.copy_calibration_mb << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: copy calibration {nbytes} bytes read + {nbytes} bytes written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     def fwd():
         selective_scan_fwd(u, dt, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, delta_softplus=True,
@@ -219,7 +259,7 @@ def main():
             "peak": VALU_PEAK_TOPS,
             "unit": "TFLOP/s",
             "frac": achieved_t / VALU_PEAK_TOPS,
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "kernel": "scan_fwd_kernel",
             "ops_per_unit": f"{valu_slots_per_token_channel(w.dstate)} fp32 VALU issue slots "
                             "per token*channel",
