@@ -336,8 +336,8 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       // every global load of the iteration is issued here, one chunk ahead,
       // and consumed by compute_p after the scan of the current chunk
       load_p(n1 > 0 ? c1 : c0, n1 > 0 ? n1 : n, true, pf);
-      // phase S: a full chunk is unrolled completely, so the scheduler can
-      // read the LDS operands of later steps while earlier steps compute
+      // phase S: the recurrence over the chunk, one step per time index; a
+      // ragged last chunk runs the plain loop below
       auto step = [&](int lt) {
         const float dl = s_delta[buf][lt][lane];
         const float du = s_du[buf][lt][lane];
@@ -357,8 +357,38 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
         s_y[w][lt][lane] = y;
       };
       if (n == TC) {
+        // software-pipelined: the LDS operands of step lt + PD are read while
+        // step lt computes, and scheduling barriers keep the compiler from
+        // sinking the reads back next to their uses (about 2% over leaving
+        // the placement to the scheduler)
+        constexpr int PD = 2;
+        float pdl[PD + 1], pdu[PD + 1], pb[PD + 1][G], pc[PD + 1][G];
+        auto rd = [&](int lt, int slot) {
+          pdl[slot] = s_delta[buf][lt][lane];
+          pdu[slot] = s_du[buf][lt][lane];
 #pragma unroll
-        for (int lt = 0; lt < TC; ++lt) step(lt);
+          for (int g = 0; g < G; ++g) {
+            pb[slot][g] = s_B[buf][lt][w * G + g];
+            pc[slot][g] = s_C[buf][lt][w * G + g];
+          }
+        };
+#pragma unroll
+        for (int k = 0; k < PD; ++k) rd(k, k);
+#pragma unroll
+        for (int lt = 0; lt < TC; ++lt) {
+          if (lt + PD < TC) rd(lt + PD, (lt + PD) % (PD + 1));
+          __builtin_amdgcn_sched_barrier(0);
+          const int slot = lt % (PD + 1);
+          float y = 0.0f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float a = exp2_hw(pdl[slot] * A2[g]);
+            h[g] = fmaf(a, h[g], pdu[slot] * pb[slot][g]);
+            y = fmaf(pc[slot][g], h[g], y);
+          }
+          s_y[w][lt][lane] = y;
+          __builtin_amdgcn_sched_barrier(0);
+        }
       } else {
         for (int lt = 0; lt < n; ++lt) step(lt);
       }
