@@ -33,18 +33,29 @@ import synth  # noqa: E402
 # vector lane-operations per second without packed math (the published
 # 157.3 TFLOP/s counts an FMA as 2 flops and packed pairs as 2 lanes).
 HBM_PEAK_GBS = 8000.0
+# v_exp_f32 throughput measured on gfx950 with 4 waves per SIMD (half the
+# FMA rate); the transcendental roofline of the forward
+EXP_PEAK_TPS = 18.47
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 METRIC = "selective-scan fwd tokens·channels/s and achieved HBM GB/s (% of peak), 1 GPU"
 
 
-def valu_slots_per_token_channel(n):
+def valu_slots_per_token_channel(n, bbar="delta"):
     """Algorithmic fp32 VALU issue slots per token*channel of the forward:
     per state mul(Delta*A), exp, mul(Delta*u*B), fma(h), fma(y) = 6 slots with
     the transcendental at half rate (2 slots); per channel step softplus
     (exp, log, rcp + 5 ops = 11), gate (exp, rcp + 3 ops = 7), Delta*u and
-    D*u (2): 20 slots."""
-    return 6 * n + 20
+    D*u (2): 20 slots.  The zero-order-hold input adds per state the
+    coefficient (exp(Delta A) - 1)/A: a 5-term series and its scaling (6),
+    the difference form (1), the choice between them (2) and one more
+    product (1): 16 slots per state."""
+    return (16 if bbar == "zoh" else 6) * n + 20
+
+
+def transcendentals_per_token_channel(n):
+    """exp per state, plus exp/log/rcp of softplus and exp/rcp of the gate."""
+    return n + 5
 
 
 def parse():
@@ -56,9 +67,14 @@ def parse():
                    choices=["mamba130m", "mamba2p8b", "seq1m"],
                    help="forward workload of the step (default: the 2.8B-shaped layer)")
     p.add_argument("--no-decode", action="store_true", help="time the forward alone")
+    p.add_argument("--bbar", default="delta", choices=["delta", "zoh"],
+                   help="input discretisation of forward and decode (default Delta*B)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate host time budget of the oracle baseline")
+    p.add_argument("--l-sweep", action="store_true",
+                   help="instead of the step: time the forward alone over L = 2^10 .. 2^20 "
+                        "at B=1, D=256, N=16, float32 (one JSON line per L)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before timing, run one plain device copy of this many MiB "
                         "(a known-size reference for hardware byte counters)")
@@ -92,7 +108,7 @@ def measured_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, w, dec, budget_s):
+def cpu_baseline(x, w, dec, budget_s, bbar="delta"):
     """Times the oracle (as it stands) on a bounded prefix of the workload:
     every batch row and channel, the first L' steps, L' sized to ~budget_s;
     plus one decode step on a 32-sequence slice of the decode workload."""
@@ -104,17 +120,17 @@ def cpu_baseline(x, w, dec, budget_s):
                 x["D"], x["z"][:, sl], x["dt_bias"])
 
     t0 = time.perf_counter()
-    oracle.scan_fwd(*sample(8))
+    oracle.scan_fwd(*sample(8), bbar=bbar)
     per_step = (time.perf_counter() - t0) / 8
     L = int(max(8, min(w.seqlen, budget_s / max(per_step, 1e-6))))
     t0 = time.perf_counter()
-    oracle.scan_fwd(*sample(L))
+    oracle.scan_fwd(*sample(L), bbar=bbar)
     t_fwd = time.perf_counter() - t0
     nb = 32
     t0 = time.perf_counter()
     oracle.state_update(dec["state"][:nb], dec["u"][:nb], dec["delta"][:nb], dec["A"],
                         dec["B"][:nb], dec["C"][:nb], dec["D"], dec["z"][:nb],
-                        dec["dt_bias"])
+                        dec["dt_bias"], bbar=bbar)
     t_dec = time.perf_counter() - t0
     tokch = w.batch * L * w.dim + nb * dec_dim(dec)
     try:
@@ -139,6 +155,56 @@ def dec_dim(dec):
     return dec["u"].shape[1]
 
 
+def l_sweep(args, torch, dev):
+    """Forward time against sequence length at the million-token shape's width:
+    the work is linear in L, so tokens*channels/s should level off, not fall."""
+    from selective_state_space_38_amd import check_device_errors, fwd_plan, selective_scan_fwd
+
+    w = synth.WORKLOADS["seq1m"]
+    print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = synth.make(w)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=torch.float32)
+
+    full = {k: up(x[k]) for k in ("u", "delta", "z", "B", "C")}
+    A, Dv, bias = up(x["A"]), up(x["D"]), up(x["dt_bias"])
+    for lg in range(10, 21):
+        L = 1 << lg
+        u, dt, z = (full[k][:, :L] for k in ("u", "delta", "z"))
+        Bm, Cm = full["B"][:, :L], full["C"][:, :L]
+        out = torch.empty_like(u)
+        last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+        def fwd():
+            selective_scan_fwd(u, dt, A, Bm, Cm, D=Dv, z=z, delta_bias=bias,
+                               delta_softplus=True, return_last_state=True, out=out,
+                               last_state=last)
+
+        for _ in range(args.warmup):
+            fwd()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+              for _ in range(args.steps)]
+        for e in ev:
+            e[0].record()
+            fwd()
+            e[1].record()
+        torch.cuda.synchronize()
+        check_device_errors(dev)
+        ms = [e[0].elapsed_time(e[1]) for e in ev]
+        med = float(np.median(ms))
+        tokch = w.batch * L * w.dim
+        slots = valu_slots_per_token_channel(w.dstate) * tokch
+        print(json.dumps({
+            "l_sweep": True, "batch": w.batch, "seqlen": L, "dim": w.dim, "dstate": w.dstate,
+            "dtype": "f32", "median_ms": med, "min_ms": float(np.min(ms)),
+            "tokens_channels_per_s": tokch / (med / 1e3),
+            "alu_frac": slots / (med / 1e3) / 1e12 / VALU_PEAK_TOPS,
+            "plan": fwd_plan(w.batch, L, w.dim, w.dstate, torch.float32),
+        }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -153,6 +219,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.l_sweep:
+        l_sweep(args, torch, dev)
+        return
     w = synth.WORKLOADS[args.workload]
     dw = synth.WORKLOADS["decode"]
     act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -189,11 +258,11 @@ def main():
 
     def fwd():
         selective_scan_fwd(u, dt, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, delta_softplus=True,
-                           return_last_state=True, out=out, last_state=last)
+                           return_last_state=True, out=out, last_state=last, bbar=args.bbar)
 
     def decode(i):
         selective_state_update(states[i % n_rot], dx, ddt, dA, dB, dC, D=dD, z=dz,
-                               dt_bias=dbias, dt_softplus=True, out=dout)
+                               dt_bias=dbias, dt_softplus=True, out=dout, bbar=args.bbar)
 
     for i in range(args.warmup):
         fwd()
@@ -221,13 +290,15 @@ def main():
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
     fwd_avg = float(np.mean(fwd_ms))
     dec_avg = float(np.mean(dec_ms))
+    trans_rate = (transcendentals_per_token_channel(w.dstate) * w.batch * w.seqlen * w.dim
+                  / (fwd_avg / 1e3) / 1e12)
 
     tokch_fwd = w.batch * w.seqlen * w.dim
     tokch_dec = 0 if args.no_decode else dw.batch * dw.dim
     value = (tokch_fwd + tokch_dec) / (ms_per_step / 1e3)
     fwd_bytes = synth.algorithmic_bytes(w)
     dec_bytes = synth.algorithmic_bytes(dw)
-    slots = valu_slots_per_token_channel(w.dstate) * tokch_fwd
+    slots = valu_slots_per_token_channel(w.dstate, args.bbar) * tokch_fwd
     achieved_t = slots / (fwd_avg / 1e3) / 1e12
     plan = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate, act)
 
@@ -251,6 +322,7 @@ def main():
                             f" + decode update (B={dw.batch}, D={dw.dim}, N={dw.dstate}, "
                             f"{dw.dtype})")),
             "io_dtype": w.dtype,
+            "bbar": args.bbar,
             "forward_plan": plan,
         },
         "roofline": {
@@ -259,12 +331,20 @@ def main():
             "peak": VALU_PEAK_TOPS,
             "unit": "TFLOP/s",
             "frac": achieved_t / VALU_PEAK_TOPS,
-            "traffic": measured_traffic(w.name),
+            "traffic": measured_traffic(w.name) if args.bbar == "delta" else None,
             "kernel": "scan_fwd_kernel",
-            "ops_per_unit": f"{valu_slots_per_token_channel(w.dstate)} fp32 VALU issue slots "
-                            "per token*channel",
+            "ops_per_unit": f"{valu_slots_per_token_channel(w.dstate, args.bbar)} fp32 VALU "
+                            "issue slots per token*channel",
             "units_per_launch": tokch_fwd,
             "avg_launch_ms": fwd_avg,
+            "median_launch_ms": float(np.median(fwd_ms)),
+            "min_launch_ms": float(np.min(fwd_ms)),
+            "transcendentals": {
+                "per_token_channel": transcendentals_per_token_channel(w.dstate),
+                "achieved_T_per_s": trans_rate,
+                "measured_v_exp_peak_T_per_s": EXP_PEAK_TPS,
+                "frac": trans_rate / EXP_PEAK_TPS,
+            },
         },
         "hbm": {
             "forward_GBps": fwd_bytes / (fwd_avg / 1e3) / 1e9,
@@ -276,12 +356,14 @@ def main():
                                      dec_bytes / (dec_avg / 1e3) / 1e9 / HBM_PEAK_GBS),
             "decode_algorithmic_bytes": dec_bytes,
             "decode_avg_launch_ms": None if args.no_decode else dec_avg,
+            "decode_median_launch_ms": None if args.no_decode else float(np.median(dec_ms)),
+            "decode_min_launch_ms": None if args.no_decode else float(np.min(dec_ms)),
         },
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(x, w, dec, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(x, w, dec, args.cpu_seconds, args.bbar)
     print(json.dumps(line), flush=True)
 
 

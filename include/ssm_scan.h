@@ -17,6 +17,13 @@
  *   selective_state_update One decode step of the same recurrence on a stored
  *                          state (reading guide FAQ: fixed D x N state per
  *                          layer, constant time per token, no KV cache).
+ *   selective_scan_fwd_ex, selective_state_update_ex
+ *                          The same operations with a choice of input
+ *                          discretisation: Delta*B (as above) or the exact
+ *                          zero-order hold of the reading guide's Method,
+ *                          Bbar = (Delta A)^-1 (exp(Delta A) - 1) Delta B,
+ *                          which for the diagonal A is (exp(Delta A) - 1)/A * B
+ *                          (limit Delta*B where A = 0).
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library
@@ -65,6 +72,12 @@ typedef enum {
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
+/* Input discretisation Bbar of the _ex entry points. */
+typedef enum {
+  SSM_BBAR_DELTA = 0,  /* Bbar = Delta * B */
+  SSM_BBAR_ZOH = 1     /* Bbar = (exp(Delta A) - 1) / A * B, Delta * B where A = 0 */
+} ssm_bbar;
+
 typedef struct {
   int64_t batch;   /* B */
   int64_t seqlen;  /* L (must be 1 for selective_state_update) */
@@ -102,6 +115,20 @@ int selective_scan_fwd_h0(const void* u, const void* delta, const float* A,
                           const ssm_dims* dims, void* stream);
 
 /*
+ * As selective_scan_fwd_h0 with the input discretisation `bbar` (an
+ * ssm_bbar; any other value returns SSM_EINVAL).  With SSM_BBAR_DELTA it is
+ * selective_scan_fwd_h0 exactly.  With SSM_BBAR_ZOH the per-state input
+ * coefficient (exp(Delta A) - 1)/A is evaluated without cancellation near
+ * Delta A = 0 (a series there), at roughly 2.5x the arithmetic of Delta*B.
+ */
+int selective_scan_fwd_ex(const void* u, const void* delta, const float* A,
+                          const void* B, const void* C, const float* D,
+                          const void* z, const float* dt_bias, int softplus,
+                          const float* h0, int bbar, void* out,
+                          float* last_state, const ssm_dims* dims,
+                          void* stream);
+
+/*
  * One decode step, in place on `state`.
  *   state       : [B][D][N] float32, read and overwritten with the new state
  *   x, dt, z    : [B][D] of dtype (z nullable)
@@ -116,6 +143,17 @@ int selective_state_update(float* state, const void* x, const void* dt,
                            const float* dt_bias, int softplus, void* out,
                            const ssm_dims* dims, void* stream);
 
+/*
+ * As selective_state_update with the input discretisation `bbar` (an
+ * ssm_bbar; any other value returns SSM_EINVAL).  L successive calls with
+ * SSM_BBAR_ZOH reproduce selective_scan_fwd_ex with SSM_BBAR_ZOH.
+ */
+int selective_state_update_ex(float* state, const void* x, const void* dt,
+                              const float* A, const void* B, const void* C,
+                              const float* D, const void* z,
+                              const float* dt_bias, int softplus, int bbar,
+                              void* out, const ssm_dims* dims, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* ssm_status_string(int status);
 
@@ -129,10 +167,12 @@ int ssm_check_device_errors(void* stream);
 
 /*
  * Launch plan the forward would use for `dims` (host only, no GPU call):
- * lanes_per_channel = waves sharing one channel block (state groups),
- * segments = sequence segments, lookback = 1 if segments exchange partial
+ * state_groups = waves sharing one block of 64 channels, each holding
+ * states_per_group of the N states of every channel; segments = sequence
+ * segments of segment_len steps; lookback = 1 if segments exchange partial
  * aggregates (decoupled look-back), 0 if each waits for its predecessor's
- * final state.  Returns SSM_OK or a validation error.
+ * final state; chunk = steps staged through LDS at a time; workgroups = the
+ * launch's grid.  Returns SSM_OK or a validation error.
  */
 typedef struct {
   int32_t state_groups;

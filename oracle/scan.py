@@ -64,12 +64,12 @@ def discretise(delta, A, B_t, u_t, bbar="delta"):
     Abar = exp(Delta * A): Gu & Dao reading guide, "Method" (zero-order hold).
     Bbar * x:
       * bbar="delta": Delta * B * x, the simplified input discretisation of
-        "Mamba / MambaMini" Q&A (Delta multiplies B elementwise).  This is
-        what the GPU path computes.
+        "Mamba / MambaMini" Q&A (Delta multiplies B elementwise).  The
+        default of the GPU entry points.
       * bbar="zoh": the exact ZOH input matrix of the reading guide's
         "Method", (Delta A)^-1 (exp(Delta A) - 1) Delta B, which for diagonal
-        A is expm1(Delta A) / A * B (limit Delta * B as A -> 0).  Used only
-        by the gated-RNN special-case test.
+        A is expm1(Delta A) / A * B (limit Delta * B as A -> 0).  The GPU's
+        optional zero-order-hold mode.
     """
     dA = delta[..., :, None] * A
     Abar = np.exp(dA)
@@ -141,7 +141,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None,
 
 
 def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
-                 dt_softplus=True):
+                 dt_softplus=True, bbar="delta"):
     """Single-token decode: one step of the same recurrence on a stored state.
 
     Reading guide FAQ (no KV cache): generation keeps only a fixed D x N state
@@ -151,7 +151,7 @@ def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
     """
     state, x, dt, A, B, C = map(_f64, (state, x, dt, A, B, C))
     D, z, dt_bias = map(_f64, (D, z, dt_bias))
-    h, y = _step(state, x, dt, A, B, C, D, z, dt_bias, dt_softplus, "delta")
+    h, y = _step(state, x, dt, A, B, C, D, z, dt_bias, dt_softplus, bbar)
     return y, h
 
 

@@ -13,10 +13,15 @@ LIB_PATH = os.path.join(HERE, "libssm_scan.so")
 SSM_F32 = 0
 SSM_BF16 = 1
 
+SSM_BBAR_DELTA = 0
+SSM_BBAR_ZOH = 1
+
 EXPORTED = (
     "selective_scan_fwd",
     "selective_scan_fwd_h0",
+    "selective_scan_fwd_ex",
     "selective_state_update",
+    "selective_state_update_ex",
     "ssm_status_string",
     "ssm_check_device_errors",
     "ssm_fwd_plan_for",
@@ -66,9 +71,15 @@ def load():
     lib.selective_scan_fwd_h0.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                           vp, vp, vp, dims_p, vp]
     lib.selective_scan_fwd_h0.restype = ctypes.c_int
+    lib.selective_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                          vp, ctypes.c_int, vp, vp, dims_p, vp]
+    lib.selective_scan_fwd_ex.restype = ctypes.c_int
     lib.selective_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                            vp, dims_p, vp]
     lib.selective_state_update.restype = ctypes.c_int
+    lib.selective_state_update_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              ctypes.c_int, ctypes.c_int, vp, dims_p, vp]
+    lib.selective_state_update_ex.restype = ctypes.c_int
     lib.ssm_status_string.argtypes = [ctypes.c_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_check_device_errors.argtypes = [vp]

@@ -53,16 +53,26 @@ def fwd_plan(batch, seqlen, dim, dstate, dtype=torch.float32):
     return {f: getattr(plan, f) for f, _ in plan._fields_}
 
 
+def _bbar_code(bbar):
+    codes = {"delta": _lib.SSM_BBAR_DELTA, "zoh": _lib.SSM_BBAR_ZOH}
+    if bbar not in codes:
+        raise ValueError(f"bbar must be 'delta' or 'zoh', not {bbar!r}")
+    return codes[bbar]
+
+
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                        delta_softplus=True, return_last_state=False, h0=None,
-                       out=None, last_state=None):
+                       out=None, last_state=None, bbar="delta"):
     """Selective-scan forward on the GPU.
 
     u, delta, z: [batch, L, dim]; B, C: [batch, L, dstate] (float32 or
     bfloat16, all the same); A: [dim, dstate], D, delta_bias: [dim] and
     h0: [batch, dim, dstate] float32.  Returns out (same dtype as u) and, with
     return_last_state, the float32 final state [batch, dim, dstate].
+    bbar: "delta" (Bbar = Delta*B) or "zoh" (exact zero-order hold,
+    (exp(Delta A) - 1)/A * B).
     """
+    code = _bbar_code(bbar)
     if u.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {u.dtype}")
     bsz, L, dim = u.shape
@@ -87,22 +97,30 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     dims = _lib.SsmDims(bsz, L, dim, dstate, _DTYPES[act])
     lib = _lib.load()
     with torch.cuda.device(dev):
-        rc = lib.selective_scan_fwd_h0(
-            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-            _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(out),
-            _ptr(last_state), ctypes.byref(dims), _stream(dev))
+        if code == _lib.SSM_BBAR_DELTA:
+            rc = lib.selective_scan_fwd_h0(
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(out),
+                _ptr(last_state), ctypes.byref(dims), _stream(dev))
+        else:
+            rc = lib.selective_scan_fwd_ex(
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), code, _ptr(out),
+                _ptr(last_state), ctypes.byref(dims), _stream(dev))
     _raise(rc)
     return (out, last_state) if return_last_state else out
 
 
 def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
-                           dt_softplus=True, out=None):
+                           dt_softplus=True, out=None, bbar="delta"):
     """One decode step on the GPU, updating ``state`` in place.
 
     state: [batch, dim, dstate] float32; x, dt, z: [batch, dim] and
     B, C: [batch, dstate] (float32 or bfloat16, all the same); A, D, dt_bias
-    as in the forward.  Returns out [batch, dim] in the activation dtype.
+    and bbar as in the forward.  Returns out [batch, dim] in the activation
+    dtype.
     """
+    code = _bbar_code(bbar)
     if x.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {x.dtype}")
     bsz, dim = x.shape
@@ -124,10 +142,16 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
     dims = _lib.SsmDims(bsz, 1, dim, dstate, _DTYPES[act])
     lib = _lib.load()
     with torch.cuda.device(dev):
-        rc = lib.selective_state_update(
-            _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-            _ptr(dt_bias), 1 if dt_softplus else 0, _ptr(out), ctypes.byref(dims),
-            _stream(dev))
+        if code == _lib.SSM_BBAR_DELTA:
+            rc = lib.selective_state_update(
+                _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(dt_bias), 1 if dt_softplus else 0, _ptr(out), ctypes.byref(dims),
+                _stream(dev))
+        else:
+            rc = lib.selective_state_update_ex(
+                _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(dt_bias), 1 if dt_softplus else 0, code, _ptr(out), ctypes.byref(dims),
+                _stream(dev))
     _raise(rc)
     return out
 

@@ -104,9 +104,10 @@ int check_dims(const ssm_dims* dims) {
 
 int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
              const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
-             void* out, float* last_state, const ssm_dims* dims, void* stream) {
+             int bbar, void* out, float* last_state, const ssm_dims* dims, void* stream) {
   int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
+  if (bbar != SSM_BBAR_DELTA && bbar != SSM_BBAR_ZOH) return SSM_EINVAL;
   if (!u || !delta || !A || !B || !C || !out) return SSM_EINVAL;
   const void* ptrs[] = {u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
   for (const void* p : ptrs)
@@ -165,6 +166,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.has_z = z != nullptr;
   sh.has_h0 = h0 != nullptr;
   sh.has_last = last_state != nullptr;
+  sh.zoh = bbar == SSM_BBAR_ZOH ? 1 : 0;
   {
     // per-thread runs of the chunk tile: kChunk / groups consecutive channels
     const int64_t ept = plan.chunk / plan.state_groups;
@@ -189,32 +191,13 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   return rc;
 }
 
-}  // namespace
-
-extern "C" {
-
-int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
-                       const void* C, const float* D, const void* z, const float* dt_bias,
-                       int softplus, void* out, float* last_state, const ssm_dims* dims,
-                       void* stream) {
-  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, nullptr, out, last_state, dims,
-                  stream);
-}
-
-int selective_scan_fwd_h0(const void* u, const void* delta, const float* A, const void* B,
-                          const void* C, const float* D, const void* z, const float* dt_bias,
-                          int softplus, const float* h0, void* out, float* last_state,
-                          const ssm_dims* dims, void* stream) {
-  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, out, last_state, dims,
-                  stream);
-}
-
-int selective_state_update(float* state, const void* x, const void* dt, const float* A,
-                           const void* B, const void* C, const float* D, const void* z,
-                           const float* dt_bias, int softplus, void* out, const ssm_dims* dims,
-                           void* stream) {
+int state_update_impl(float* state, const void* x, const void* dt, const float* A,
+                      const void* B, const void* C, const float* D, const void* z,
+                      const float* dt_bias, int softplus, int bbar, void* out,
+                      const ssm_dims* dims, void* stream) {
   int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
+  if (bbar != SSM_BBAR_DELTA && bbar != SSM_BBAR_ZOH) return SSM_EINVAL;
   if (dims->seqlen != 1) return SSM_EINVAL;
   if (!state || !x || !dt || !A || !B || !C || !out) return SSM_EINVAL;
   const void* ptrs[] = {state, x, dt, A, B, C, D, z, dt_bias, out};
@@ -226,10 +209,55 @@ int selective_state_update(float* state, const void* x, const void* dt, const fl
     if (p == out) return SSM_EINVAL;
   if (dims->batch * dims->dim * dims->dstate > (1LL << 40)) return SSM_EINVAL;
   if (ssm::launch_state_update(dims->dtype, static_cast<int>(dims->dstate), state, x, dt, A, B,
-                               C, D, z, dt_bias, softplus ? 1 : 0, out, dims->batch, dims->dim,
+                               C, D, z, dt_bias, softplus ? 1 : 0, bbar == SSM_BBAR_ZOH ? 1 : 0,
+                               out, dims->batch, dims->dim,
                                static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSM_ELAUNCH;
   return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                       const void* C, const float* D, const void* z, const float* dt_bias,
+                       int softplus, void* out, float* last_state, const ssm_dims* dims,
+                       void* stream) {
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, nullptr, SSM_BBAR_DELTA, out,
+                  last_state, dims, stream);
+}
+
+int selective_scan_fwd_h0(const void* u, const void* delta, const float* A, const void* B,
+                          const void* C, const float* D, const void* z, const float* dt_bias,
+                          int softplus, const float* h0, void* out, float* last_state,
+                          const ssm_dims* dims, void* stream) {
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, SSM_BBAR_DELTA, out,
+                  last_state, dims, stream);
+}
+
+int selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                          const void* C, const float* D, const void* z, const float* dt_bias,
+                          int softplus, const float* h0, int bbar, void* out,
+                          float* last_state, const ssm_dims* dims, void* stream) {
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, bbar, out, last_state, dims,
+                  stream);
+}
+
+int selective_state_update(float* state, const void* x, const void* dt, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* dt_bias, int softplus, void* out, const ssm_dims* dims,
+                           void* stream) {
+  return state_update_impl(state, x, dt, A, B, C, D, z, dt_bias, softplus, SSM_BBAR_DELTA, out,
+                           dims, stream);
+}
+
+int selective_state_update_ex(float* state, const void* x, const void* dt, const float* A,
+                              const void* B, const void* C, const float* D, const void* z,
+                              const float* dt_bias, int softplus, int bbar, void* out,
+                              const ssm_dims* dims, void* stream) {
+  return state_update_impl(state, x, dt, A, B, C, D, z, dt_bias, softplus, bbar, out, dims,
+                           stream);
 }
 
 const char* ssm_status_string(int status) {

@@ -4,6 +4,9 @@
 //   Delta_t = softplus(dt_t + dt_bias)          reading guide, Selection mechanism (S6)
 //   Abar_t  = exp(Delta_t * A), Bbar_t x_t = Delta_t * B_t * x_t
 //                                                reading guide, Method; "Mamba / MambaMini" Q&A
+//             or, with ZOH, the exact zero-order-hold input
+//             Bbar_t x_t = (exp(Delta_t A) - 1) / A * B_t * x_t
+//                                                reading guide, Method
 //   h_t = Abar_t * h_{t-1} + Bbar_t x_t          reading guide, Method
 //   y_t = C_t . h_t + D * x_t, out = y_t * SiLU(z_t)
 //                                                reading guide, Method; CSDN "Mamba" 3(1);
@@ -74,7 +77,7 @@ __device__ __forceinline__ int wait_status(const int* p, int need, int limit) {
   return v;
 }
 
-template <typename T, int NG, int G, int TC>
+template <typename T, int NG, int G, int TC, bool ZOH>
 __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
     const T* __restrict__ u, const T* __restrict__ dtp,
     const float* __restrict__ A, const T* __restrict__ Bm,
@@ -123,9 +126,22 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   const bool dvalid = d < dim;
   const int64_t dc = dvalid ? d : dim - 1;      // tail lanes read a valid channel, never store
 
-  float A2[G];
+  float A2[G], iA[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) A2[g] = A[dc * N + w * G + g] * kLog2e;
+  for (int g = 0; g < G; ++g) {
+    const float av = A[dc * N + w * G + g];
+    A2[g] = av * kLog2e;
+    iA[g] = ZOH ? 1.0f / av : 0.0f;
+  }
+  // input term of state g: Delta*u*B (du holds Delta*u), or with ZOH
+  // (exp(Delta A) - 1)/A * u*B (du holds u); x2 = Delta*A*log2 e, a = exp2(x2)
+  auto input_term = [&](int g, float dl, float x2, float a, float du, float bv) -> float {
+    if constexpr (ZOH) {
+      return zoh_coef(x2, a, dl, iA[g]) * (du * bv);
+    } else {
+      return du * bv;
+    }
+  };
   const bool use_sp = sh.softplus != 0;
 
   // tile role of this thread in the P and E phases: row tr, channels tc..tc+EPT
@@ -221,7 +237,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       const float uv = pf.uu.get(k);
       const float s = pf.dt.get(k) + rbias[k];
       dl[k] = use_sp ? softplus_f32(s) : s;
-      du[k] = dl[k] * uv;
+      du[k] = ZOH ? uv : dl[k] * uv;
       sk[k] = rD[k] * uv;
       zf[k] = (out_mode && sh.has_z) ? pf.zz.get(k) : 0.0f;
     }
@@ -301,8 +317,9 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
         sum_delta += dl;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float a = exp2_hw(dl * A2[g]);
-          hA[g] = fmaf(a, hA[g], du * bv[g]);
+          const float x2 = dl * A2[g];
+          const float a = exp2_hw(x2);
+          hA[g] = fmaf(a, hA[g], input_term(g, dl, x2, a, du, bv[g]));
         }
       };
       if (n == TC) {
@@ -350,8 +367,9 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
         float y = 0.0f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float a = exp2_hw(dl * A2[g]);
-          h[g] = fmaf(a, h[g], du * bv[g]);
+          const float x2 = dl * A2[g];
+          const float a = exp2_hw(x2);
+          h[g] = fmaf(a, h[g], input_term(g, dl, x2, a, du, bv[g]));
           y = fmaf(cv[g], h[g], y);
         }
         s_y[w][lt][lane] = y;
@@ -382,8 +400,9 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
           float y = 0.0f;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            const float a = exp2_hw(pdl[slot] * A2[g]);
-            h[g] = fmaf(a, h[g], pdu[slot] * pb[slot][g]);
+            const float x2 = pdl[slot] * A2[g];
+            const float a = exp2_hw(x2);
+            h[g] = fmaf(a, h[g], input_term(g, pdl[slot], x2, a, pdu[slot], pb[slot][g]));
             y = fmaf(pc[slot][g], h[g], y);
           }
           s_y[w][lt][lane] = y;
@@ -550,11 +569,20 @@ hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t stream) {
 template <typename T, int NG, int G>
 static hipError_t launch_typed(const FwdPtrs& p, const FwdScratch& s, const FwdShape& sh,
                                int64_t workgroups, hipStream_t stream) {
-  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, chunk_for_groups(NG)>), dim3(static_cast<unsigned>(workgroups)),
-                     dim3(64 * NG), 0, stream, static_cast<const T*>(p.u),
-                     static_cast<const T*>(p.delta), p.A, static_cast<const T*>(p.B),
-                     static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), p.dt_bias,
-                     p.h0, static_cast<T*>(p.out), p.last_state, s, sh);
+  constexpr int TC = chunk_for_groups(NG);
+  const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * NG);
+#define SSM_LAUNCH_FWD(Z)                                                                    \
+  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, TC, Z>), grid, block, 0, stream,              \
+                     static_cast<const T*>(p.u), static_cast<const T*>(p.delta), p.A,         \
+                     static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,             \
+                     static_cast<const T*>(p.z), p.dt_bias, p.h0, static_cast<T*>(p.out),     \
+                     p.last_state, s, sh)
+  if (sh.zoh) {
+    SSM_LAUNCH_FWD(true);
+  } else {
+    SSM_LAUNCH_FWD(false);
+  }
+#undef SSM_LAUNCH_FWD
   return hipGetLastError();
 }
 

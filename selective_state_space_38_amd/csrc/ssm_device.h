@@ -42,6 +42,27 @@ __device__ __forceinline__ float softplus_f32(float s) {
   return fmaxf(s, 0.0f) + lp;
 }
 
+// Input coefficient of the exact zero-order-hold discretisation for a
+// diagonal A: Bbar / B = (exp(Delta A) - 1) / A = Delta * phi(x) with
+// x = Delta A and phi(x) = (e^x - 1) / x = sum_k x^k / (k+1)!.  Near x = 0
+// the difference a - 1 loses digits, so |x| < 1/4 uses the series up to x^5
+// (truncation below 5e-8 relative); elsewhere (a - 1) / A loses at most
+// ~4e-7 relative to the rounding of a.  x2 = x log2(e) is the argument the
+// hardware exp took, a = exp(x), inv_a = 1 / A.  A = 0 takes the series
+// (x = 0) and gives the limit Delta; the other branch is not used there.
+__device__ __forceinline__ float zoh_coef(float x2, float a, float delta, float inv_a) {
+  // coefficients ln(2)^k / (k+1)! of the series in x2
+  float p = 2.2222597e-4f;
+  p = fmaf(p, x2, 1.9236258e-3f);
+  p = fmaf(p, x2, 1.3876027e-2f);
+  p = fmaf(p, x2, 8.0075502e-2f);
+  p = fmaf(p, x2, 3.4657359e-1f);
+  p = fmaf(p, x2, 1.0f);
+  const float series = delta * p;
+  const float diff = fmaf(a, inv_a, -inv_a);
+  return fabsf(x2) < 0.36067376f ? series : diff;
+}
+
 // y * SiLU(z) = y * z / (1 + e^-z)
 __device__ __forceinline__ float silu_gate(float y, float z) {
   return y * (z * rcp_hw(1.0f + exp2_hw(-z * kLog2e)));

@@ -30,6 +30,7 @@ struct FwdShape {
   int32_t lookback;  // 1: decoupled look-back over aggregates, 0: chained
   int32_t has_bias, has_D, has_z, has_h0, has_last;
   int32_t vec_io;    // activation rows may be moved in aligned vector runs
+  int32_t zoh;       // 1: exact zero-order-hold input term, 0: Delta * B
 };
 
 struct FwdPtrs {
@@ -65,7 +66,7 @@ hipError_t launch_state_update(int dtype, int dstate, float* state,
                                const void* x, const void* dt, const float* A,
                                const void* B, const void* C, const float* D,
                                const void* z, const float* dt_bias,
-                               int softplus, void* out, int64_t batch,
+                               int softplus, int zoh, void* out, int64_t batch,
                                int64_t dim, hipStream_t stream);
 
 // Reads and clears this device's count of carry waits that timed out.

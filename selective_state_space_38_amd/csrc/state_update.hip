@@ -4,6 +4,8 @@
 // D x N state per layer, constant time per token, no KV cache), with the same
 // discretisation, readout and gate as the forward (reading guide, Method and
 // S6; "Mamba / MambaMini" Q&A on Delta*B and SiLU; CSDN "Mamba" 3(1) for D).
+// With ZOH the input term is the exact zero-order-hold one of the reading
+// guide's Method, (exp(Delta A) - 1) / A * B * x.
 //
 // The step is a pure read-modify-write stream over the float32 state, so it
 // is laid out for HBM (see the kernel comment).  The shuffle partners of a
@@ -23,7 +25,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // is read and written with non-temporal hints.  (4 and 16 states per lane
 // measured slower: 16 makes the per-instruction accesses of a wave strided.)
 constexpr int kDecodeStatesPerLane = 8;
-template <typename T, int N>
+template <typename T, int N, bool ZOH>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ x, const T* __restrict__ dtp,
     const float* __restrict__ A, const T* __restrict__ Bm, const T* __restrict__ Cm,
@@ -91,8 +93,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   float y = 0.0f;
 #pragma unroll
   for (int j = 0; j < Q; ++j) {
-    const float a = exp2_hw(dl * (a2[j] * kLog2e));
-    h[j] = fmaf(a, h[j], du * bv[j]);
+    const float x2 = dl * (a2[j] * kLog2e);
+    const float a = exp2_hw(x2);
+    if constexpr (ZOH) {
+      h[j] = fmaf(a, h[j], zoh_coef(x2, a, dl, 1.0f / a2[j]) * (xv * bv[j]));
+    } else {
+      h[j] = fmaf(a, h[j], du * bv[j]);
+    }
     y = fmaf(cv[j], h[j], y);
   }
   if (i < total) {
@@ -120,18 +127,24 @@ __global__ __launch_bounds__(256) void state_update_kernel(
 template <typename T>
 static hipError_t launch_n(int n, float* state, const void* x, const void* dt, const float* A,
                            const void* B, const void* C, const float* D, const void* z,
-                           const float* bias, int softplus, void* out, int64_t batch,
+                           const float* bias, int softplus, int zoh, void* out, int64_t batch,
                            int64_t dim, hipStream_t stream) {
   const int q = n < kDecodeStatesPerLane ? n : kDecodeStatesPerLane;
   const int64_t total = batch * dim * (n / q);
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
   const dim3 grid(static_cast<unsigned>(blocks));
-#define SSM_LAUNCH_SU(NN)                                                                       \
-  hipLaunchKernelGGL((state_update_kernel<T, NN>), grid, dim3(threads), 0, stream, state,       \
+#define SSM_LAUNCH_SU_Z(NN, Z)                                                                  \
+  hipLaunchKernelGGL((state_update_kernel<T, NN, Z>), grid, dim3(threads), 0, stream, state,    \
                      static_cast<const T*>(x), static_cast<const T*>(dt), A,                    \
                      static_cast<const T*>(B), static_cast<const T*>(C), D,                     \
                      static_cast<const T*>(z), bias, softplus, static_cast<T*>(out), batch, dim)
+#define SSM_LAUNCH_SU(NN)         \
+  if (zoh) {                      \
+    SSM_LAUNCH_SU_Z(NN, true);    \
+  } else {                        \
+    SSM_LAUNCH_SU_Z(NN, false);   \
+  }
   switch (n) {
     case 1: SSM_LAUNCH_SU(1); break;
     case 2: SSM_LAUNCH_SU(2); break;
@@ -143,19 +156,20 @@ static hipError_t launch_n(int n, float* state, const void* x, const void* dt, c
     default: return hipErrorInvalidValue;
   }
 #undef SSM_LAUNCH_SU
+#undef SSM_LAUNCH_SU_Z
   return hipGetLastError();
 }
 
 hipError_t launch_state_update(int dtype, int dstate, float* state, const void* x,
                                const void* dt, const float* A, const void* B, const void* C,
                                const float* D, const void* z, const float* dt_bias,
-                               int softplus, void* out, int64_t batch, int64_t dim,
+                               int softplus, int zoh, void* out, int64_t batch, int64_t dim,
                                hipStream_t stream) {
   if (dtype == 0)
-    return launch_n<float>(dstate, state, x, dt, A, B, C, D, z, dt_bias, softplus, out, batch,
-                           dim, stream);
-  return launch_n<bf16_t>(dstate, state, x, dt, A, B, C, D, z, dt_bias, softplus, out, batch,
-                          dim, stream);
+    return launch_n<float>(dstate, state, x, dt, A, B, C, D, z, dt_bias, softplus, zoh, out,
+                           batch, dim, stream);
+  return launch_n<bf16_t>(dstate, state, x, dt, A, B, C, D, z, dt_bias, softplus, zoh, out,
+                          batch, dim, stream);
 }
 
 }  // namespace ssm

@@ -54,7 +54,7 @@ def act_dtype(tag):
 
 
 def gpu_forward(x, tag, *, D=True, z=True, bias=True, softplus=True, h0=None,
-                last=True):
+                last=True, bbar="delta"):
     from selective_state_space_38_amd import selective_scan_fwd
     dt = act_dtype(tag)
     res = selective_scan_fwd(
@@ -64,7 +64,7 @@ def gpu_forward(x, tag, *, D=True, z=True, bias=True, softplus=True, h0=None,
         z=to_dev(x["z"], dt) if z else None,
         delta_bias=to_dev(x["dt_bias"], torch.float32) if bias else None,
         delta_softplus=softplus, return_last_state=last,
-        h0=to_dev(h0, torch.float32) if h0 is not None else None)
+        h0=to_dev(h0, torch.float32) if h0 is not None else None, bbar=bbar)
     torch.cuda.synchronize()
     if last:
         out, st = res
@@ -73,14 +73,14 @@ def gpu_forward(x, tag, *, D=True, z=True, bias=True, softplus=True, h0=None,
 
 
 def oracle_forward(x, *, D=True, z=True, bias=True, softplus=True, h0=None,
-                   cols=None):
+                   cols=None, bbar="delta"):
     """Oracle outputs; with ``cols`` (list of (b, d)) only those columns:
     returns arrays [len(cols), L] and [len(cols), N]."""
     if cols is None:
         return oracle.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"],
                                x["D"] if D else None, x["z"] if z else None,
                                x["dt_bias"] if bias else None,
-                               delta_softplus=softplus, h0=h0)
+                               delta_softplus=softplus, h0=h0, bbar=bbar)
     outs, states = [], []
     by_b = {}
     for i, (b, d) in enumerate(cols):
@@ -94,7 +94,7 @@ def oracle_forward(x, *, D=True, z=True, bias=True, softplus=True, h0=None,
             x["B"][b:b + 1], x["C"][b:b + 1], x["D"][ds] if D else None,
             x["z"][b:b + 1][:, :, ds] if z else None,
             x["dt_bias"][ds] if bias else None, delta_softplus=softplus,
-            h0=None if h0 is None else h0[b:b + 1][:, ds])
+            h0=None if h0 is None else h0[b:b + 1][:, ds], bbar=bbar)
         for k, (i, _) in enumerate(items):
             res_o[i] = o[0, :, k]
             res_s[i] = s[0, k]

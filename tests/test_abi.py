@@ -131,3 +131,30 @@ def test_plan_covers_every_supported_state_size():
                                         ctypes.byref(plan)) == SSM_OK
             assert plan.state_groups * plan.states_per_group == n
             assert (plan.segments - 1) * plan.segment_len < L <= plan.segments * plan.segment_len
+
+
+@pytest.mark.parametrize("bbar", [-1, 2, 7])
+def test_ex_entry_points_reject_unknown_bbar(bbar):
+    lib = _lib.load()
+    d = _dims()
+    rc = lib.selective_scan_fwd_ex(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None,
+                                   bbar, P[5], None, ctypes.byref(d), None)
+    assert rc == SSM_EINVAL
+    d1 = _dims(L=1)
+    rc = lib.selective_state_update_ex(P[0], P[1], P[2], P[3], P[4], P[5], None, None, None,
+                                       1, bbar, P[6], ctypes.byref(d1), None)
+    assert rc == SSM_EINVAL
+
+
+def test_ex_entry_points_validate_like_the_plain_ones():
+    lib = _lib.load()
+    d = _dims(n=3)
+    rc = lib.selective_scan_fwd_ex(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None,
+                                   1, P[5], None, ctypes.byref(d), None)
+    assert rc == SSM_EINVAL
+    rc = lib.selective_scan_fwd_ex(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None,
+                                   1, P[0], None, ctypes.byref(_dims()), None)
+    assert rc == SSM_EINVAL  # out aliases u
+    rc = lib.selective_state_update_ex(P[0], P[1], P[2], P[3], P[4], P[5], None, None, None,
+                                       1, 1, P[6], ctypes.byref(_dims(L=2)), None)
+    assert rc == SSM_EINVAL  # seqlen must be 1

@@ -382,3 +382,56 @@ def test_silu_closed_form():
     z = np.linspace(-30, 30, 121)
     np.testing.assert_allclose(oracle.silu(z), z * expit(z), rtol=1e-15, atol=1e-300)
     assert oracle.silu(np.array([0.0]))[0] == 0.0
+
+
+# --- P13: exact zero-order hold (reading guide, Method) ---------------------
+# With the input held constant, the ZOH step is the exact solution of
+# h' = A h + B x over the step, so steps compose: after any split of a total
+# time T into steps Delta_t, h = e^{A T} h0 + (e^{A T} - 1)/A * B x.  The
+# simplified Delta*B input does not have this property, so the test also
+# tells the two modes apart.
+
+def test_zoh_exact_for_held_input():
+    r = _rng(130)
+    b, L, d, n = 2, 40, 3, 5
+    A = -np.exp(r.normal(0, 2, (d, n)))          # from ~1e-3 to ~50 in size
+    A[0, 0] = -1e-9                               # near the A -> 0 limit
+    dt = r.uniform(1e-3, 0.2, (b, L, d))          # softplus off: Delta = dt
+    Bv = r.standard_normal((b, 1, n))
+    x = r.standard_normal((b, 1, d))
+    h0 = r.standard_normal((b, d, n))
+    u = np.broadcast_to(x, (b, L, d))
+    Bm = np.broadcast_to(Bv, (b, L, n))
+    C = r.standard_normal((b, L, n))
+    _, last = oracle.scan_fwd(u, dt, A, Bm, C, delta_softplus=False, h0=h0, bbar="zoh")
+    T = dt.sum(axis=1)[:, :, None]                                  # [b, d, 1]
+    decay = np.exp(A[None] * T)
+    ref = decay * h0 + np.expm1(A[None] * T) / A[None] * Bv[:, 0, None, :] * x[:, 0, :, None]
+    np.testing.assert_allclose(last, ref, rtol=1e-12, atol=1e-13)
+    _, last_delta = oracle.scan_fwd(u, dt, A, Bm, C, delta_softplus=False, h0=h0)
+    assert np.max(np.abs(last_delta - ref)) > 1e-3 * np.max(np.abs(ref))
+
+
+def test_zoh_zero_A_is_integrator():
+    r = _rng(131)
+    b, L, d, n = 1, 12, 2, 3
+    A = np.zeros((d, n))
+    dt = r.uniform(0.01, 0.5, (b, L, d))
+    u = r.standard_normal((b, L, d))
+    Bm = r.standard_normal((b, L, n))
+    C = r.standard_normal((b, L, n))
+    _, last = oracle.scan_fwd(u, dt, A, Bm, C, delta_softplus=False, bbar="zoh")
+    ref = np.einsum("bld,bln->bdn", dt * u, Bm)       # h = sum_t Delta_t x_t B_t
+    np.testing.assert_allclose(last, ref, rtol=1e-13, atol=1e-14)
+
+
+def test_zoh_decode_loop_equals_forward_bitwise():
+    c = _random_case(132, b=2, L=9, d=3, n=4, gate=True, h0=True)
+    out, last = oracle.scan_fwd(**c, bbar="zoh")
+    st = c["h0"].copy()
+    for t in range(9):
+        y, st = oracle.state_update(st, c["u"][:, t], c["delta"][:, t], c["A"],
+                                    c["B"][:, t], c["C"][:, t], c["D"],
+                                    c["z"][:, t], c["dt_bias"], bbar="zoh")
+        assert np.array_equal(y, out[:, t])
+    assert np.array_equal(st, last)
