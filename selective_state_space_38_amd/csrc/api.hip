@@ -66,12 +66,14 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
   if (!lookback) {
     seg_len = d.seqlen;
   } else {
-    // enough segments for ~4096 waves, each at least 8192 steps when the
-    // sequence allows (the best measured trade of parallelism against the
-    // extra aggregate pass)
-    const int64_t want = div_up(4096, waves_per_slice);
+    // enough segments for ~2048 waves (two per SIMD), each at least 128
+    // steps (512 from 16K steps on): the measured best trade of parallelism
+    // against the extra aggregate pass, the per-segment start-up and the
+    // look-back walk at 256 channels, from 4K to 1M steps
+    const int64_t want = div_up(2048, waves_per_slice);
+    const int64_t min_seg = d.seqlen >= 16384 ? 512 : 128;
     seg_len = div_up(d.seqlen, want);
-    if (seg_len < 8192) seg_len = 8192;
+    if (seg_len < min_seg) seg_len = min_seg;
   }
   const int force_seg = env_int("SSM_FORCE_SEGMENT", 0);
   if (force_seg > 0) seg_len = force_seg;

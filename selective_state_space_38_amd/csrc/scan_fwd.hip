@@ -500,31 +500,74 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
     if (lane == 0) store_release(&sc.status[rec * NG + w], kAggregate);
 
     // Walk back: acc = (exp2(A2 * acc_s), acc_b) is the combination of the
-    // segments between the one being inspected and this one.
+    // segments between the one being inspected and this one.  The walk moves
+    // in windows of kWin predecessors: lane i polls the status of record
+    // j - i, so one round trip shows which of the nearest kWin records are
+    // published, and the records of the ready run (up to and including the
+    // first final state) are fetched together before they are combined,
+    // nearest first.
     float acc_s = 0.0f;
     float acc_b[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc_b[g] = 0.0f;
     const int rec0 = chain * sh.n_seg;
-    for (int j = rec - 1; j >= rec0; --j) {
-      const int st = wait_status(&sc.status[j * NG + w], kAggregate, sc.spin_limit);
-      const int64_t js = static_cast<int64_t>(j) * N * 64;
-      if (st == kInclusive) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float carry = sc.inc[js + (gidx + g) * 64 + lane];
-          acc_b[g] = fmaf(exp2_hw(A2[g] * acc_s), carry, acc_b[g]);
+    constexpr int kWin = 8;
+    int j = rec - 1;
+    int spins = 0;
+    while (j >= rec0) {
+      const int W = (j - rec0 + 1 < kWin) ? j - rec0 + 1 : kWin;
+      const int st = lane < W ? load_relaxed(&sc.status[(j - lane) * NG + w]) : kEmpty;
+      const uint64_t ready = __ballot(st >= kAggregate);
+      const uint64_t incl = __ballot(st == kInclusive);
+      // contiguous published run from the nearest record, cut after the first
+      // final state in it
+      const int run = static_cast<int>(__builtin_ctzll(~ready));  // ready has bit 63 clear
+      const uint64_t run_mask = (1ull << run) - 1ull;
+      const uint64_t inc_in_run = incl & run_mask;
+      const int take = inc_in_run ? static_cast<int>(__builtin_ctzll(inc_in_run)) + 1 : run;
+      if (take == 0) {
+        if (++spins > sc.spin_limit) {
+          if (lane == 0) atomicAdd(&g_carry_timeouts, 1u);
+          break;  // timed out: continue with what was gathered
         }
-        break;
+        if (spins < 16) {
+          __builtin_amdgcn_s_sleep(2);
+        } else {
+          __builtin_amdgcn_s_sleep(32);
+        }
+        continue;
       }
-      if (st == kEmpty) break;  // timed out: continue with what was gathered
-      const float sj = sc.agg_s[(static_cast<int64_t>(j) * NG + w) * 64 + lane];
+      acquire_fence();
+      // the aggregates of the run (slots past it re-read record j), and the
+      // final state that ends it, if any
+      float rb[kWin][G], rs[kWin], ri[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float bj = sc.agg_b[js + (gidx + g) * 64 + lane];
-        acc_b[g] = fmaf(exp2_hw(A2[g] * acc_s), bj, acc_b[g]);
+      for (int k = 0; k < kWin; ++k) {
+        const int jj = j - (k < take ? k : 0);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          rb[k][g] = sc.agg_b[(static_cast<int64_t>(jj) * N + gidx + g) * 64 + lane];
+        rs[k] = sc.agg_s[(static_cast<int64_t>(jj) * NG + w) * 64 + lane];
       }
-      acc_s += sj;
+      {
+        const int ji = j - take + 1;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          ri[g] = inc_in_run ? sc.inc[(static_cast<int64_t>(ji) * N + gidx + g) * 64 + lane] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < kWin; ++k) {
+        if (k < take) {
+          const bool last_inc = inc_in_run && k == take - 1;
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            acc_b[g] = fmaf(exp2_hw(A2[g] * acc_s), last_inc ? ri[g] : rb[k][g], acc_b[g]);
+          acc_s += rs[k];  // unused after a final state
+        }
+      }
+      if (inc_in_run) break;
+      j -= take;
+      spins = 0;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) h[g] = acc_b[g];

@@ -181,6 +181,24 @@ def test_carry_wait_bound_reports_timeout():
     check_device_errors()  # a normal call leaves the counter at zero
 
 
+def test_lookback_wait_bound_reports_timeout():
+    """The same for the windowed look-back walk: predecessors not yet
+    published at the first poll end the walk, the kernel exits and the error
+    counter reports it."""
+    from selective_state_space_38_amd import check_device_errors
+    x = _case("mamba130m", batch=1, seqlen=4096, dim=64, dstate=16, a_init="random")
+    check_device_errors()  # clear
+    with env(SSM_FORCE_LOOKBACK=1, SSM_FORCE_SEGMENT=16, SSM_TEST_SPIN_LIMIT=0):
+        gpu_forward(x, "f32")
+    with pytest.raises(RuntimeError, match="SSM_ETIMEOUT"):
+        check_device_errors()
+    with env(SSM_FORCE_LOOKBACK=1, SSM_FORCE_SEGMENT=16):
+        got, st = gpu_forward(x, "f32")
+    check_device_errors()
+    ref, ref_st = oracle_forward(x)
+    check_forward(x, "f32", got, st, ref, ref_st)
+
+
 # ------------------------------------------------------- full-size workloads --
 
 def test_workload_mamba130m_full():
