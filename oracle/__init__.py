@@ -29,3 +29,4 @@ from .scan import (  # noqa: F401
     state_update,
     scan_pairs_blelloch,
 )
+from .scan_bwd import scan_bwd  # noqa: F401

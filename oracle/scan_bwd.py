@@ -1,0 +1,101 @@
+"""Plain float64 gradients of the selective scan (TEST INFRASTRUCTURE ONLY).
+
+The pages name the backward pass only through its memory plan: intermediate
+states are recomputed on chip during back-propagation instead of being kept
+in HBM (reading guide, Hardware-aware state expansion; the aigcdaily article
+"Mamba：我们所知的ChatGPT时代的终结者？", Mamba block).  What it computes is
+the derivative of the forward of ``scan.py``, so this oracle is that
+derivative written out by the chain rule through the recurrence: one forward
+pass that keeps every state (the oracle may store what the GPU recomputes),
+then one reverse-time pass with the adjoint state
+
+    lambda_t = dL/dh_t = dy_t * C_t + Abar_{t+1} * lambda_{t+1},
+    lambda_{L-1} = dy_{L-1} * C_{L-1} + dlast,
+
+which is the same linear recurrence as the forward run backwards in time,
+with decays Abar_{t+1} and inputs dy_t C_t.
+
+Shapes as in ``scan.py``; ``dout`` [batch, L, dim] is the gradient of the
+output and ``dlast`` [batch, dim, dstate] (optional) that of the final state.
+Only the Delta*B input (bbar="delta") is differentiated.
+"""
+
+import numpy as np
+
+from .scan import _f64, softplus, silu
+
+
+def _sigmoid(x):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, delta_softplus=True,
+             h0=None, dout=None, dlast=None):
+    """Gradients of sum(dout * out) + sum(dlast * last_state).
+
+    Returns a dict with du, ddelta (gradient of the raw dt), dA, dB, dC and,
+    for the inputs that were given, dD, dz, ddt_bias, dh0.
+    """
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, dt_bias, h0 = map(_f64, (D, z, dt_bias, h0))
+    dout, dlast = _f64(dout), _f64(dlast)
+    bsz, L, dim = u.shape
+    n = A.shape[1]
+
+    # forward, keeping every state: H[t] = h_t, Hp[t] = h_{t-1}
+    s = delta if dt_bias is None else delta + dt_bias
+    dl = softplus(s) if delta_softplus else s                 # Delta [b, L, d]
+    h = np.zeros((bsz, dim, n)) if h0 is None else h0.copy()
+    H = np.empty((bsz, L, dim, n))
+    Hp = np.empty((bsz, L, dim, n))
+    Abar = np.empty((bsz, L, dim, n))
+    y = np.empty((bsz, L, dim))
+    for t in range(L):
+        Hp[:, t] = h
+        Abar[:, t] = np.exp(dl[:, t, :, None] * A)
+        h = Abar[:, t] * h + (dl[:, t] * u[:, t])[:, :, None] * B[:, t, None, :]
+        H[:, t] = h
+        y[:, t] = np.sum(h * C[:, t, None, :], axis=-1)
+    if D is not None:
+        y = y + D * u
+
+    # gate: out = y * SiLU(z); d SiLU/dz = sigma(z) (1 + z (1 - sigma(z)))
+    if z is not None:
+        sg = _sigmoid(z)
+        dy = dout * silu(z)
+        dz = dout * y * sg * (1.0 + z * (1.0 - sg))
+    else:
+        dy = dout.copy()
+        dz = None
+
+    du = np.empty((bsz, L, dim))
+    dDelta = np.empty((bsz, L, dim))
+    dB = np.empty((bsz, L, n))
+    dC = np.empty((bsz, L, n))
+    dA = np.zeros((dim, n))
+    lam_next = np.zeros((bsz, dim, n)) if dlast is None else dlast.copy()  # Abar_{t+1} lambda_{t+1}
+    for t in range(L - 1, -1, -1):
+        lam = dy[:, t, :, None] * C[:, t, None, :] + lam_next          # lambda_t
+        dC[:, t] = np.sum(dy[:, t, :, None] * H[:, t], axis=1)         # y_t = C_t . h_t
+        dB[:, t] = np.sum(lam * (dl[:, t] * u[:, t])[:, :, None], axis=1)
+        s1 = np.sum(lam * B[:, t, None, :], axis=-1)                   # sum_n lambda B
+        q = Abar[:, t] * Hp[:, t]                                      # Abar_t h_{t-1}
+        du[:, t] = dl[:, t] * s1
+        # h_t depends on Delta through Abar_t = exp(Delta A) and Delta u B
+        dDelta[:, t] = u[:, t] * s1 + np.sum(lam * q * A, axis=-1)
+        dA += np.sum(lam * q * dl[:, t, :, None], axis=0)
+        lam_next = Abar[:, t] * lam
+    if D is not None:
+        du = du + D * dy
+    ds = dDelta * _sigmoid(s) if delta_softplus else dDelta          # softplus' = sigma
+    res = dict(du=du, ddelta=ds, dA=dA, dB=dB, dC=dC)
+    if D is not None:
+        res["dD"] = np.sum(dy * u, axis=(0, 1))
+    if z is not None:
+        res["dz"] = dz
+    if dt_bias is not None:
+        res["ddt_bias"] = np.sum(ds, axis=(0, 1))
+    if h0 is not None:
+        res["dh0"] = lam_next                                          # Abar_0 lambda_0
+    return res
