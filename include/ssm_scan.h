@@ -154,6 +154,37 @@ int selective_state_update_ex(float* state, const void* x, const void* dt,
                               const float* dt_bias, int softplus, int bbar,
                               void* out, const ssm_dims* dims, void* stream);
 
+/*
+ * Backward of selective_scan_fwd_h0 (Delta*B input): the gradients of
+ *   sum(dout * out) + sum(dlast * last_state)
+ * with respect to every input, by the chain rule through the recurrence with
+ * the adjoint state run backwards in time.  The intermediate states are not
+ * stored: one state per 8-step chunk is kept in scratch and the states inside
+ * a chunk are recomputed on chip (reading guide, Hardware-aware state
+ * expansion; aigcdaily "Mamba：我们所知的ChatGPT时代的终结者？", Mamba block).
+ *   u, delta, A, B, C, D, z, dt_bias, softplus, h0 : the forward's inputs
+ *   dout        : [B][L][D] of dtype, gradient of out
+ *   dlast       : [B][D][N] float32 (nullable = zeros), gradient of last_state
+ * Outputs (overwritten, never accumulated into):
+ *   du, ddelta  : [B][L][D] of dtype (ddelta is the gradient of the raw dt)
+ *   dA          : [D][N] float32          dB, dC : [B][L][N] of dtype
+ *   dD, ddt_bias: [D] float32 (nullable: not written; a null D or dt_bias
+ *                 input still has a gradient, taken at zero)
+ *   dz          : [B][L][D] of dtype (nullable; must be NULL when z is NULL)
+ *   dh0         : [B][D][N] float32 (nullable), gradient of the initial state
+ * Outputs must not alias inputs or each other (SSM_EINVAL).  Scratch of
+ * about 4*N*(64*B*ceil(D/64)*ceil(L/8) + 2*ceil(D/64)*B*L) bytes is allocated
+ * stream-ordered and freed on the stream (SSM_ENOMEM on failure).  Sums over
+ * channel blocks and batch rows are done in a fixed order (deterministic).
+ */
+int selective_scan_bwd(const void* u, const void* delta, const float* A,
+                       const void* B, const void* C, const float* D,
+                       const void* z, const float* dt_bias, int softplus,
+                       const float* h0, const void* dout, const float* dlast,
+                       void* du, void* ddelta, float* dA, void* dB, void* dC,
+                       float* dD, void* dz, float* ddt_bias, float* dh0,
+                       const ssm_dims* dims, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* ssm_status_string(int status);
 

@@ -3,6 +3,7 @@ with hand-written HIP kernels, and a thin PyTorch binding."""
 
 from .api import (  # noqa: F401
     selective_scan_fwd,
+    selective_scan_bwd,
     selective_state_update,
     check_device_errors,
     fwd_plan,

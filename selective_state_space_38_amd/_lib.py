@@ -20,6 +20,7 @@ EXPORTED = (
     "selective_scan_fwd",
     "selective_scan_fwd_h0",
     "selective_scan_fwd_ex",
+    "selective_scan_bwd",
     "selective_state_update",
     "selective_state_update_ex",
     "ssm_status_string",
@@ -74,6 +75,9 @@ def load():
     lib.selective_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                           vp, ctypes.c_int, vp, vp, dims_p, vp]
     lib.selective_scan_fwd_ex.restype = ctypes.c_int
+    lib.selective_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                       vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp]
+    lib.selective_scan_bwd.restype = ctypes.c_int
     lib.selective_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                            vp, dims_p, vp]
     lib.selective_state_update.restype = ctypes.c_int

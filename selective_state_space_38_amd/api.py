@@ -111,6 +111,58 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return (out, last_state) if return_last_state else out
 
 
+def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, h0=None, dlast=None):
+    """Backward of selective_scan_fwd (Delta*B input) on the GPU.
+
+    Inputs as in the forward, plus dout [batch, L, dim] (activation dtype),
+    the gradient of the output, and dlast [batch, dim, dstate] float32
+    (optional), the gradient of the final state.  Returns a dict of gradients:
+    du, ddelta (of the raw dt), dz (if z is given) in the activation dtype;
+    dB, dC [batch, L, dstate] in the activation dtype; dA [dim, dstate] and,
+    for given D / delta_bias / h0, dD, ddt_bias, dh0 in float32.
+    """
+    if u.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {u.dtype}")
+    bsz, L, dim = u.shape
+    dstate = A.shape[1]
+    dev = u.device
+    act = u.dtype
+    for t, name, dt_, shp in ((u, "u", act, (bsz, L, dim)), (delta, "delta", act, (bsz, L, dim)),
+                              (z, "z", act, (bsz, L, dim)), (dout, "dout", act, (bsz, L, dim)),
+                              (B, "B", act, (bsz, L, dstate)), (C, "C", act, (bsz, L, dstate)),
+                              (A, "A", torch.float32, (dim, dstate)),
+                              (D, "D", torch.float32, (dim,)),
+                              (delta_bias, "delta_bias", torch.float32, (dim,)),
+                              (h0, "h0", torch.float32, (bsz, dim, dstate)),
+                              (dlast, "dlast", torch.float32, (bsz, dim, dstate))):
+        _check(t, name, dt_, shp, dev)
+    if dout is None:
+        raise ValueError("dout is required")
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u),
+             dA=torch.empty((dim, dstate), dtype=torch.float32, device=dev),
+             dB=torch.empty_like(B), dC=torch.empty_like(C))
+    if D is not None:
+        g["dD"] = torch.empty((dim,), dtype=torch.float32, device=dev)
+    if z is not None:
+        g["dz"] = torch.empty_like(z)
+    if delta_bias is not None:
+        g["ddt_bias"] = torch.empty((dim,), dtype=torch.float32, device=dev)
+    if h0 is not None:
+        g["dh0"] = torch.empty((bsz, dim, dstate), dtype=torch.float32, device=dev)
+    dims = _lib.SsmDims(bsz, L, dim, dstate, _DTYPES[act])
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.selective_scan_bwd(
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            1 if delta_softplus else 0, _ptr(h0), _ptr(dout), _ptr(dlast),
+            _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+            _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddt_bias")), _ptr(g.get("dh0")),
+            ctypes.byref(dims), _stream(dev))
+    _raise(rc)
+    return g
+
+
 def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
                            dt_softplus=True, out=None, bbar="delta"):
     """One decode step on the GPU, updating ``state`` in place.

@@ -11,7 +11,15 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm_scan.so")
-SOURCES = ["api.hip", "scan_fwd.hip", "state_update.hip"]
+# (source, object name, extra flags): the forward is compiled once per
+# activation type so the two halves build in parallel
+SOURCES = [
+    ("api.hip", "api", []),
+    ("scan_fwd.hip", "scan_fwd_f32", ["-DSSM_FWD_DTYPE=0"]),
+    ("scan_fwd.hip", "scan_fwd_bf16", ["-DSSM_FWD_DTYPE=1"]),
+    ("scan_bwd.hip", "scan_bwd", []),
+    ("state_update.hip", "state_update", []),
+]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -33,18 +41,38 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
-                     if "packed-fp32-ops" not in line)
-    if r.returncode != 0:
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _check(proc, verbose):
+    out, _ = proc.communicate()
+    msgs = "\n".join(line for line in out.splitlines() if "packed-fp32-ops" not in line)
+    if proc.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + msgs)
     if verbose and msgs.strip():
         print(msgs)
+
+
+def build(verbose=False):
+    """Compiles every source to an object in parallel, then links the
+    shared library (replacing the old one only on success)."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objs, procs = [], []
+    for src, name, extra in SOURCES:
+        obj = os.path.join(objdir, name + ".o")
+        objs.append(obj)
+        procs.append(_run([hipcc()] + compile_flags + extra +
+                          ["-c", os.path.join(CSRC, src), "-o", obj], verbose))
+    for proc in procs:
+        _check(proc, verbose)
+    tmp = LIB + ".tmp"
+    _check(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
+                verbose), verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -184,11 +184,18 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   ssm::FwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
 
   rc = SSM_OK;
-  if (ssm::launch_fill_zero(sc.ticket, n_int, st) != hipSuccess) rc = SSM_ELAUNCH;
-  if (rc == SSM_OK &&
-      ssm::launch_scan_fwd(dims->dtype, plan.state_groups, plan.states_per_group, p, sc, sh,
-                           plan.workgroups, st) != hipSuccess)
-    rc = SSM_ELAUNCH;
+  const bool f32 = dims->dtype == SSM_F32;
+  const hipError_t ez = f32 ? ssm::fwd_f32::launch_fill_zero(sc.ticket, n_int, st)
+                            : ssm::fwd_bf16::launch_fill_zero(sc.ticket, n_int, st);
+  if (ez != hipSuccess) rc = SSM_ELAUNCH;
+  if (rc == SSM_OK) {
+    const hipError_t el =
+        f32 ? ssm::fwd_f32::launch_scan_fwd(plan.state_groups, plan.states_per_group, p, sc, sh,
+                                            plan.workgroups, st)
+            : ssm::fwd_bf16::launch_scan_fwd(plan.state_groups, plan.states_per_group, p, sc,
+                                             sh, plan.workgroups, st);
+    if (el != hipSuccess) rc = SSM_ELAUNCH;
+  }
   if (hipFreeAsync(scratch, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
   return rc;
 }
@@ -216,6 +223,99 @@ int state_update_impl(float* state, const void* x, const void* dt, const float* 
                                static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSM_ELAUNCH;
   return SSM_OK;
+}
+
+// waves per workgroup of the backward kernel for N states (as its dispatch)
+int bwd_groups(int64_t n) {
+  switch (n) {
+    case 8: return 2;
+    case 16: return 4;
+    case 32:
+    case 64: return 8;
+    default: return 1;
+  }
+}
+
+int bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+             const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
+             const void* dout, const float* dlast, void* du, void* ddelta, float* dA, void* dB,
+             void* dC, float* dD, void* dz, float* ddt_bias, float* dh0, const ssm_dims* dims,
+             void* stream) {
+  int rc = check_dims(dims);
+  if (rc != SSM_OK) return rc;
+  if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
+    return SSM_EINVAL;
+  if (dz && !z) return SSM_EINVAL;  // no gate, no gate gradient
+  const void* ins[] = {u, delta, A, B, C, D, z, dt_bias, h0, dout, dlast};
+  const void* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddt_bias, dh0};
+  for (const void* q : ins)
+    if (q && !aligned(q, 4)) return SSM_EALIGN;
+  for (const void* q : outs)
+    if (q && !aligned(q, 4)) return SSM_EALIGN;
+  for (const void* o : outs) {
+    if (!o) continue;
+    for (const void* i : ins)
+      if (i == o) return SSM_EINVAL;
+    int same = 0;
+    for (const void* o2 : outs) same += (o2 == o);
+    if (same > 1) return SSM_EINVAL;
+  }
+
+  const int64_t N = dims->dstate;
+  const int64_t cblk = div_up(dims->dim, 64);
+  const int64_t nck = div_up(dims->seqlen, ssm::kBwdChunk);
+  auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
+  const int64_t b_ckpt = up256(dims->batch * cblk * nck * N * 64 * 4);
+  const int64_t b_bc = up256(cblk * dims->batch * dims->seqlen * 2 * N * 4);
+  const int64_t b_a = up256(dims->batch * dims->dim * N * 4);
+  const int64_t b_d = up256(dims->batch * dims->dim * 4);
+  const int64_t total = b_ckpt + b_bc + b_a + 2 * b_d;
+  if (total > (1LL << 40)) return SSM_EINVAL;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (env_int("SSM_TEST_FAIL_ALLOC", 0) == 1) return SSM_ENOMEM;
+  char* scratch = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&scratch), static_cast<size_t>(total), st) !=
+          hipSuccess ||
+      !scratch)
+    return SSM_ENOMEM;
+
+  ssm::BwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, dout, dlast, du, ddelta, dA, dB, dC,
+                 dD, dz, ddt_bias, dh0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  p.ckpt = reinterpret_cast<float*>(scratch);
+  p.part_bc = reinterpret_cast<float*>(scratch + b_ckpt);
+  p.part_a = reinterpret_cast<float*>(scratch + b_ckpt + b_bc);
+  p.part_d = reinterpret_cast<float*>(scratch + b_ckpt + b_bc + b_a);
+  p.part_bias = reinterpret_cast<float*>(scratch + b_ckpt + b_bc + b_a + b_d);
+
+  ssm::BwdShape sh;
+  sh.batch = dims->batch;
+  sh.seqlen = dims->seqlen;
+  sh.dim = dims->dim;
+  sh.n_cblk = static_cast<int32_t>(cblk);
+  sh.nchunks = nck;
+  sh.softplus = softplus ? 1 : 0;
+  sh.has_D = D != nullptr;
+  sh.has_z = z != nullptr;
+  sh.has_bias = dt_bias != nullptr;
+  sh.has_h0 = h0 != nullptr;
+  sh.has_dlast = dlast != nullptr;
+  {
+    const int64_t ept = ssm::kBwdChunk / bwd_groups(N);
+    const int64_t esz = dims->dtype == SSM_BF16 ? 2 : 4;
+    const uintptr_t need = static_cast<uintptr_t>(ept * esz >= 16 ? 16 : ept * esz);
+    bool ok = ept * esz >= 4 && dims->dim % ept == 0;
+    const void* acts[] = {u, delta, z, dout, du, ddelta, dz};
+    for (const void* a : acts)
+      if (a && !aligned(a, need)) ok = false;
+    sh.vec_io = ok ? 1 : 0;
+  }
+
+  rc = SSM_OK;
+  if (ssm::launch_scan_bwd(dims->dtype, static_cast<int>(N), p, sh, st) != hipSuccess)
+    rc = SSM_ELAUNCH;
+  if (hipFreeAsync(scratch, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
+  return rc;
 }
 
 }  // namespace
@@ -262,6 +362,16 @@ int selective_state_update_ex(float* state, const void* x, const void* dt, const
                            stream);
 }
 
+int selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                       const void* C, const float* D, const void* z, const float* dt_bias,
+                       int softplus, const float* h0, const void* dout, const float* dlast,
+                       void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                       void* dz, float* ddt_bias, float* dh0, const ssm_dims* dims,
+                       void* stream) {
+  return bwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, dout, dlast, du, ddelta, dA,
+                  dB, dC, dD, dz, ddt_bias, dh0, dims, stream);
+}
+
 const char* ssm_status_string(int status) {
   switch (status) {
     case SSM_OK: return "SSM_OK: success";
@@ -276,10 +386,12 @@ const char* ssm_status_string(int status) {
 }
 
 int ssm_check_device_errors(void* stream) {
-  unsigned count = 0;
-  if (ssm::read_and_clear_errors(static_cast<hipStream_t>(stream), &count) != hipSuccess)
+  unsigned c32 = 0, c16 = 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (ssm::fwd_f32::read_and_clear_errors(st, &c32) != hipSuccess ||
+      ssm::fwd_bf16::read_and_clear_errors(st, &c16) != hipSuccess)
     return SSM_ELAUNCH;
-  return count ? SSM_ETIMEOUT : SSM_OK;
+  return (c32 || c16) ? SSM_ETIMEOUT : SSM_OK;
 }
 
 int ssm_fwd_plan_for(const ssm_dims* dims, ssm_fwd_plan* plan) {

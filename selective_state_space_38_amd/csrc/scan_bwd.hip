@@ -1,0 +1,474 @@
+// Backward of the selective scan (S6) for gfx950.
+//
+// The gradient of sum(dout * out) + sum(dlast * last_state) with respect to
+// every input of the forward (reading guide, Method and Selection mechanism
+// (S6) for the forward it differentiates).  The pages fix the memory plan:
+// the intermediate states are recomputed on chip during the backward pass
+// instead of being stored in HBM (reading guide, Hardware-aware state
+// expansion; aigcdaily "Mamba：我们所知的ChatGPT时代的终结者？", Mamba block).
+// Here only one state per TC-step chunk is kept (the checkpoint, N floats per
+// channel per chunk); the states inside a chunk are recomputed into
+// registers.
+//
+// Chain rule through h_t = Abar_t h_{t-1} + Delta_t u_t B_t, y_t = C_t . h_t
+// + D u_t, out_t = y_t SiLU(z_t), with the adjoint lambda_t = dL/dh_t:
+//   dy_t      = dout_t SiLU(z_t),   dz_t = dout_t y_t SiLU'(z_t)
+//   lambda_t  = dy_t C_t + Abar_{t+1} lambda_{t+1},  lambda_{L-1} += dlast
+//   dC_t[n]   = sum_d dy_t h_t[n]            dB_t[n] = sum_d lambda_t[n] Delta_t u_t
+//   du_t      = Delta_t sum_n lambda_t B_t + D dy_t
+//   dDelta_t  = u_t sum_n lambda_t B_t + sum_n lambda_t Abar_t h_{t-1} A
+//   dA[n]     = sum_{b,t} lambda_t Abar_t h_{t-1} Delta_t
+//   ddt_t     = dDelta_t softplus'(s_t) = dDelta_t sigmoid(s_t)
+//   dh0       = Abar_0 lambda_0
+// The adjoint is the forward's linear recurrence run backwards in time with
+// decays Abar_{t+1}, the pair operator of "Mamba / MambaMini" Step 2 in
+// reverse order.
+//
+// Work decomposition.  One workgroup per (batch, block of 64 channels); NG
+// waves split the N states into groups of G as in the forward (lane =
+// channel).  Phase F walks the sequence forwards and stores the state at the
+// start of every chunk (checkpoint).  Phase R walks the chunks backwards: it
+// reloads the chunk's inputs, recomputes the chunk's states and decays into
+// registers from the checkpoint, forms dy and dz, runs the adjoint over the
+// chunk, and reduces the per-channel terms:
+//   over states (du, dDelta): per-wave partials through LDS, as the forward's
+//     readout;
+//   over channels (dB, dC): quad sums by DPP, then 16 quads per (t, n) in
+//     LDS, written as this channel block's partial; a second kernel adds the
+//     channel blocks (deterministic, no atomics);
+//   over batch (dA, dD, ddt_bias): per-batch partials, added by the second
+//     kernel.
+// Rows of a ragged last chunk are padded with Delta = 0, Delta*u = 0, B = C =
+// 0 and dy = 0, which makes them identity steps of both recurrences, so
+// every chunk runs the same fully unrolled code.
+
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+
+template <typename T, int NG, int G, int TC>
+__global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
+  constexpr int N = NG * G;
+  constexpr int NT = 64 * NG;
+  constexpr int EPT = TC / NG;        // tile elements per thread (one row run)
+  constexpr int TPR = 64 / EPT;       // threads per tile row
+  constexpr int NQ = 16;              // quads per wave
+  static_assert(TC % NG == 0 && EPT >= 1 && 64 % EPT == 0, "tile must split over the waves");
+  static_assert(NT % TC == 0, "tile rows must split over the threads");
+  constexpr int BCE = (TC * N + NT - 1) / NT;  // B/C (or dB/dC) elements per thread
+  using TileRun = Run<T, EPT>;
+
+  __shared__ float s_dl[TC][64];
+  __shared__ float s_du[TC][64];
+  __shared__ float s_dy[TC][64];
+  __shared__ __align__(16) float s_B[TC][N];
+  __shared__ __align__(16) float s_C[TC][N];
+  __shared__ float s_p1[NG][TC][64];                    // partial y, then partial sum lambda B
+  __shared__ float s_p2[NG][TC][64];                    // partial sum lambda Abar h A
+  __shared__ __align__(16) float s_rB[TC][NQ][N];      // quad sums of lambda Delta u
+  __shared__ __align__(16) float s_rC[TC][NQ][N];      // quad sums of dy h
+
+  const T* const xu = static_cast<const T*>(p.u);
+  const T* const xdt = static_cast<const T*>(p.delta);
+  const T* const xB = static_cast<const T*>(p.B);
+  const T* const xC = static_cast<const T*>(p.C);
+  const T* const xz = static_cast<const T*>(p.z);
+  const T* const xdo = static_cast<const T*>(p.dout);
+  T* const gdu = static_cast<T*>(p.du);
+  T* const gddl = static_cast<T*>(p.ddelta);
+  T* const gdz = static_cast<T*>(p.dz);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = static_cast<int>(blockIdx.x);
+  const int b = wg / sh.n_cblk;
+  const int cblk = wg - b * sh.n_cblk;
+  const int64_t L = sh.seqlen;
+  const int64_t dim = sh.dim;
+  const int64_t bsz = sh.batch;
+  const int64_t ch0 = static_cast<int64_t>(cblk) * 64;
+  const int64_t d = ch0 + lane;
+  const bool dvalid = d < dim;
+  const int64_t dc = dvalid ? d : dim - 1;
+  const int gidx = w * G;
+
+  float Af[G], A2[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    Af[g] = p.A[dc * N + gidx + g];
+    A2[g] = Af[g] * kLog2e;
+  }
+
+  // tile role: row tr, channels tch .. tch + EPT - 1
+  const int tr = tid / TPR;
+  const int tc = (tid - tr * TPR) * EPT;
+  const int64_t tch = ch0 + tc;
+  const bool run_valid = tch < dim;
+  const int run_last = run_valid ? static_cast<int>((dim - 1 - tch) < (EPT - 1) ? (dim - 1 - tch)
+                                                                                : (EPT - 1))
+                                 : -1;
+  const bool run_vec = TileRun::kCanVec && sh.vec_io != 0 && run_valid;
+  const int64_t tch_c = run_valid ? tch : dim - 1;
+  float rD[EPT], rbias[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int64_t ck = tch_c + (k < run_last ? k : (run_last > 0 ? run_last : 0));
+    rD[k] = sh.has_D ? p.D[ck] : 0.0f;
+    rbias[k] = sh.has_bias ? p.dt_bias[ck] : 0.0f;
+  }
+  const int64_t row0 = static_cast<int64_t>(b) * L;
+  const int64_t nck = sh.nchunks;
+  float* ckpt = p.ckpt + (static_cast<int64_t>(wg) * nck) * N * 64;
+
+  auto load_run = [&](TileRun& r, const T* base, int64_t off) {
+    if (run_vec) {
+      r.load_vec(base + off);
+    } else {
+      r.load_elems(base + off, run_last > 0 ? run_last : 0);
+    }
+  };
+  // Chunk inputs for the scan lanes: Delta, Delta*u (zero on padded rows and
+  // channels past dim) and B (and C); the thread keeps its run's raw values.
+  struct RunVals {
+    float u[EPT], dl[EPT], sig[EPT];
+  };
+  auto stage = [&](int64_t c0, int n, bool with_c, RunVals& rv) {
+    const int r = tr < n ? tr : n - 1;
+    const int64_t off = (row0 + c0 + r) * dim + tch_c;
+    TileRun rdt, ru;
+    load_run(rdt, xdt, off);
+    load_run(ru, xu, off);
+    const bool row_ok = tr < n;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const bool ok = row_ok && k <= run_last;
+      const float s = rdt.get(k) + rbias[k];
+      const float dl = sh.softplus ? softplus_f32(s) : s;
+      rv.u[k] = ru.get(k);
+      rv.dl[k] = ok ? dl : 0.0f;
+      rv.sig[k] = sh.softplus ? sigmoid_f32(s) : 1.0f;
+      s_dl[tr][tc + k] = rv.dl[k];
+      s_du[tr][tc + k] = ok ? dl * rv.u[k] : 0.0f;
+    }
+    const int64_t base = (row0 + c0) * N;
+#pragma unroll
+    for (int k = 0; k < BCE; ++k) {
+      const int e = tid + k * NT;
+      if (e < TC * N) {
+        const int row = e / N;
+        const int ec = row < n ? e : 0;
+        const float bv = to_f32(xB[base + ec]);
+        s_B[row][e - row * N] = row < n ? bv : 0.0f;
+        if (with_c) {
+          const float cv = to_f32(xC[base + ec]);
+          s_C[row][e - row * N] = row < n ? cv : 0.0f;
+        }
+      }
+    }
+  };
+
+  // ---- phase F: checkpoints ----------------------------------------------
+  float h[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    h[g] = (sh.has_h0 && dvalid) ? p.h0[(static_cast<int64_t>(b) * dim + d) * N + gidx + g] : 0.0f;
+  for (int64_t c = 0; c < nck; ++c) {
+    const int64_t c0 = c * TC;
+    const int n = static_cast<int>((L - c0 < TC) ? L - c0 : TC);
+    RunVals rv;
+    stage(c0, n, false, rv);
+    lds_barrier();
+#pragma unroll
+    for (int g = 0; g < G; ++g) ckpt[(c * N + gidx + g) * 64 + lane] = h[g];
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+      const float dl = s_dl[t][lane];
+      const float du = s_du[t][lane];
+#pragma unroll
+      for (int g = 0; g < G; ++g) h[g] = fmaf(exp2_hw(dl * A2[g]), h[g], du * s_B[t][gidx + g]);
+    }
+    lds_barrier();
+  }
+
+  // ---- phase R: chunks in reverse ------------------------------------------
+  float lamn[G], dA_acc[G];   // lamn = Abar_{t+1} lambda_{t+1}
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    lamn[g] = (sh.has_dlast && dvalid) ? p.dlast[(static_cast<int64_t>(b) * dim + d) * N + gidx + g]
+                                       : 0.0f;
+    dA_acc[g] = 0.0f;
+  }
+  float dD_acc[EPT], dbias_acc[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    dD_acc[k] = 0.0f;
+    dbias_acc[k] = 0.0f;
+  }
+  float* part_bc = p.part_bc + (static_cast<int64_t>(cblk) * bsz + b) * L * (2 * N);
+
+  for (int64_t c = nck - 1; c >= 0; --c) {
+    const int64_t c0 = c * TC;
+    const int n = static_cast<int>((L - c0 < TC) ? L - c0 : TC);
+    const bool row_ok = tr < n;
+    RunVals rv;
+    stage(c0, n, true, rv);
+    const int r = tr < n ? tr : n - 1;
+    const int64_t off = (row0 + c0 + r) * dim + tch_c;
+    TileRun rz, rdo;
+    if (sh.has_z) load_run(rz, xz, off);
+    load_run(rdo, xdo, off);
+    lds_barrier();
+
+    // recompute the chunk's states and decays from its checkpoint
+    float hstart[G], hs[TC][G], as[TC][G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      hstart[g] = ckpt[(c * N + gidx + g) * 64 + lane];
+      h[g] = hstart[g];
+    }
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+      const float dl = s_dl[t][lane];
+      const float du = s_du[t][lane];
+      float y = 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float a = exp2_hw(dl * A2[g]);
+        h[g] = fmaf(a, h[g], du * s_B[t][gidx + g]);
+        as[t][g] = a;
+        hs[t][g] = h[g];
+        y = fmaf(s_C[t][gidx + g], h[g], y);
+      }
+      s_p1[w][t][lane] = y;
+    }
+    lds_barrier();
+
+    // dy, dz for this thread's run
+    float dy[EPT];
+    {
+      float dzv[EPT];
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) {
+        const bool ok = row_ok && k <= run_last;
+        float y = s_p1[0][tr][tc + k];
+#pragma unroll
+        for (int q = 1; q < NG; ++q) y += s_p1[q][tr][tc + k];
+        y += rD[k] * rv.u[k];
+        const float go = rdo.get(k);
+        float dyk = go;
+        dzv[k] = 0.0f;
+        if (sh.has_z) {
+          const float zv = rz.get(k);
+          const float sg = sigmoid_f32(zv);
+          dyk = go * (zv * sg);
+          dzv[k] = go * y * (sg * fmaf(zv, 1.0f - sg, 1.0f));
+        }
+        dy[k] = ok ? dyk : 0.0f;
+        s_dy[tr][tc + k] = dy[k];
+        dD_acc[k] = fmaf(dy[k], rv.u[k], dD_acc[k]);
+      }
+      if (sh.has_z && gdz && row_ok && run_valid)
+        store_run<T, EPT>(gdz + (row0 + c0 + tr) * dim + tch, dzv, run_vec, run_last);
+    }
+    lds_barrier();
+
+    // adjoint over the chunk, last step first
+#pragma unroll
+    for (int t = TC - 1; t >= 0; --t) {
+      const float dl = s_dl[t][lane];
+      const float du = s_du[t][lane];
+      const float dyt = s_dy[t][lane];
+      float s1 = 0.0f, s2 = 0.0f;
+      float pB[G], pC[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float lam = fmaf(dyt, s_C[t][gidx + g], lamn[g]);
+        pC[g] = dyt * hs[t][g];
+        pB[g] = lam * du;
+        s1 = fmaf(lam, s_B[t][gidx + g], s1);
+        const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][g] : hstart[g];
+        const float lq = lam * (as[t][g] * hp);
+        s2 = fmaf(lq, Af[g], s2);
+        dA_acc[g] = fmaf(lq, dl, dA_acc[g]);
+        lamn[g] = as[t][g] * lam;
+      }
+      s_p1[w][t][lane] = s1;
+      s_p2[w][t][lane] = s2;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        pB[g] = quad_sum(pB[g]);
+        pC[g] = quad_sum(pC[g]);
+      }
+      if ((lane & 3) == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          s_rB[t][lane >> 2][gidx + g] = pB[g];
+          s_rC[t][lane >> 2][gidx + g] = pC[g];
+        }
+      }
+    }
+    lds_barrier();
+
+    // du, ddelta for this thread's run
+    {
+      float duv[EPT], ddv[EPT];
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) {
+        const bool ok = row_ok && k <= run_last;
+        float S1 = s_p1[0][tr][tc + k];
+        float S2 = s_p2[0][tr][tc + k];
+#pragma unroll
+        for (int q = 1; q < NG; ++q) {
+          S1 += s_p1[q][tr][tc + k];
+          S2 += s_p2[q][tr][tc + k];
+        }
+        duv[k] = fmaf(rv.dl[k], S1, rD[k] * dy[k]);
+        const float ddl = fmaf(rv.u[k], S1, S2);
+        ddv[k] = ddl * rv.sig[k];
+        dbias_acc[k] += ok ? ddv[k] : 0.0f;
+      }
+      if (row_ok && run_valid) {
+        const int64_t o = (row0 + c0 + tr) * dim + tch;
+        store_run<T, EPT>(gdu + o, duv, run_vec, run_last);
+        store_run<T, EPT>(gddl + o, ddv, run_vec, run_last);
+      }
+    }
+    // this channel block's dB / dC rows: add the 16 quad sums
+#pragma unroll
+    for (int k = 0; k < BCE; ++k) {
+      const int e = tid + k * NT;
+      if (e < TC * N) {
+        const int row = e / N;
+        const int nn = e - row * N;
+        float sb = 0.0f, scv = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          sb += s_rB[row][q][nn];
+          scv += s_rC[row][q][nn];
+        }
+        if (row < n) {
+          float* pr = part_bc + (c0 + row) * (2 * N);
+          pr[nn] = sb;
+          pr[N + nn] = scv;
+        }
+      }
+    }
+    lds_barrier();
+  }
+
+  // ---- per-batch partials of dA, dD, ddt_bias; dh0 --------------------------
+  if (dvalid) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t i = (static_cast<int64_t>(b) * dim + d) * N + gidx + g;
+      p.part_a[i] = dA_acc[g];
+      if (p.dh0) p.dh0[i] = lamn[g];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    s_p1[0][tr][tc + k] = dD_acc[k];
+    s_p2[0][tr][tc + k] = dbias_acc[k];
+  }
+  lds_barrier();
+  if (tid < 64 && ch0 + tid < dim) {
+    float sd = 0.0f, sbias = 0.0f;
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+      sd += s_p1[0][t][tid];
+      sbias += s_p2[0][t][tid];
+    }
+    p.part_d[static_cast<int64_t>(b) * dim + ch0 + tid] = sd;
+    p.part_bias[static_cast<int64_t>(b) * dim + ch0 + tid] = sbias;
+  }
+}
+
+// dB[r][n] = sum_k part[k][r][n], dC[r][n] = sum_k part[k][r][N + n] over the
+// channel blocks k, for r = (b, t).
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_bc_kernel(const float* __restrict__ part,
+                                                        T* __restrict__ dB, T* __restrict__ dC,
+                                                        int64_t rows, int n, int blocks) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= rows * n) return;
+  const int64_t r = i / n;
+  const int64_t nn = i - r * n;
+  const int64_t stride = rows * 2 * n;
+  const float* q = part + r * 2 * n + nn;
+  float sb = 0.0f, sc = 0.0f;
+  for (int k = 0; k < blocks; ++k) {
+    sb += q[k * stride];
+    sc += q[k * stride + n];
+  }
+  store_act(dB, i, sb);
+  store_act(dC, i, sc);
+}
+
+// out[i] = sum_k part[k * count + i]
+__global__ __launch_bounds__(256) void reduce_sum_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ out, int64_t count,
+                                                         int parts) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float s = 0.0f;
+  for (int k = 0; k < parts; ++k) s += part[k * count + i];
+  out[i] = s;
+}
+
+static dim3 grid_for(int64_t count) {
+  return dim3(static_cast<unsigned>((count + 255) / 256));
+}
+
+template <typename T, int NG, int G>
+static hipError_t launch_bwd_typed(const BwdPtrs& p, const BwdShape& sh, hipStream_t st) {
+  constexpr int TC = kBwdChunk;
+  const dim3 grid(static_cast<unsigned>(sh.batch * sh.n_cblk)), block(64 * NG);
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, TC>), grid, block, 0, st, p, sh);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int N = NG * G;
+  const int64_t rows = sh.batch * sh.seqlen;
+  hipLaunchKernelGGL(reduce_bc_kernel<T>, grid_for(rows * N), dim3(256), 0, st, p.part_bc,
+                     static_cast<T*>(p.dB), static_cast<T*>(p.dC), rows, N, sh.n_cblk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int parts = static_cast<int>(sh.batch);
+  hipLaunchKernelGGL(reduce_sum_kernel, grid_for(sh.dim * N), dim3(256), 0, st, p.part_a, p.dA,
+                     sh.dim * N, parts);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.dD) {
+    hipLaunchKernelGGL(reduce_sum_kernel, grid_for(sh.dim), dim3(256), 0, st, p.part_d, p.dD,
+                       sh.dim, parts);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (p.ddt_bias) {
+    hipLaunchKernelGGL(reduce_sum_kernel, grid_for(sh.dim), dim3(256), 0, st, p.part_bias,
+                       p.ddt_bias, sh.dim, parts);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T>
+static hipError_t dispatch_bwd(int dstate, const BwdPtrs& p, const BwdShape& sh,
+                               hipStream_t st) {
+  switch (dstate) {
+    case 1: return launch_bwd_typed<T, 1, 1>(p, sh, st);
+    case 2: return launch_bwd_typed<T, 1, 2>(p, sh, st);
+    case 4: return launch_bwd_typed<T, 1, 4>(p, sh, st);
+    case 8: return launch_bwd_typed<T, 2, 4>(p, sh, st);
+    case 16: return launch_bwd_typed<T, 4, 4>(p, sh, st);
+    case 32: return launch_bwd_typed<T, 8, 4>(p, sh, st);
+    case 64: return launch_bwd_typed<T, 8, 8>(p, sh, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_scan_bwd(int dtype, int dstate, const BwdPtrs& p, const BwdShape& sh,
+                           hipStream_t stream) {
+  if (dtype == 0) return dispatch_bwd<float>(dstate, p, sh, stream);
+  return dispatch_bwd<bf16_t>(dstate, p, sh, stream);
+}
+
+}  // namespace ssm

@@ -47,7 +47,21 @@
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
+// This file is compiled once per activation type (-DSSM_FWD_DTYPE=0 for
+// float32, 1 for bfloat16) so the two halves build in parallel; each object
+// holds its own kernels and error counter in its own namespace.
+#if !defined(SSM_FWD_DTYPE)
+#error "compile with -DSSM_FWD_DTYPE=0 (float32) or -DSSM_FWD_DTYPE=1 (bfloat16)"
+#elif SSM_FWD_DTYPE == 0
+#define SSM_FWD_NS fwd_f32
+#define SSM_FWD_T float
+#else
+#define SSM_FWD_NS fwd_bf16
+#define SSM_FWD_T bf16_t
+#endif
+
 namespace ssm {
+namespace SSM_FWD_NS {
 
 __device__ unsigned g_carry_timeouts;
 
@@ -662,11 +676,9 @@ static hipError_t dispatch_groups(int groups, int per_group, const FwdPtrs& p,
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan_fwd(int dtype, int groups, int per_group, const FwdPtrs& p,
-                           const FwdScratch& s, const FwdShape& sh, int64_t workgroups,
-                           hipStream_t stream) {
-  if (dtype == 0) return dispatch_groups<float>(groups, per_group, p, s, sh, workgroups, stream);
-  return dispatch_groups<bf16_t>(groups, per_group, p, s, sh, workgroups, stream);
+hipError_t launch_scan_fwd(int groups, int per_group, const FwdPtrs& p, const FwdScratch& s,
+                           const FwdShape& sh, int64_t workgroups, hipStream_t stream) {
+  return dispatch_groups<SSM_FWD_T>(groups, per_group, p, s, sh, workgroups, stream);
 }
 
 hipError_t read_and_clear_errors(hipStream_t stream, unsigned* count) {
@@ -680,4 +692,5 @@ hipError_t read_and_clear_errors(hipStream_t stream, unsigned* count) {
                            hipMemcpyHostToDevice);
 }
 
+}  // namespace SSM_FWD_NS
 }  // namespace ssm

@@ -143,6 +143,57 @@ struct Run {
   }
 };
 
+// Stores EPT values (rounded to T) at p[0..EPT): one vector store when vec
+// (the caller guarantees alignment and a whole run in range), otherwise
+// element by element up to index last.
+template <typename T, int EPT>
+__device__ __forceinline__ void store_run(T* p, const float (&v)[EPT], bool vec, int last) {
+  using R = Run<T, EPT>;
+  if (R::kCanVec && vec) {
+    R o;
+#pragma unroll
+    for (int i = 0; i < R::NW; ++i) o.w[i] = 0;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      T t;
+      store_act(&t, 0, v[k]);
+      if constexpr (sizeof(T) == 4) {
+        o.w[k] = __builtin_bit_cast(uint32_t, t);
+      } else {
+        o.w[k / 2] |= static_cast<uint32_t>(t) << (16 * (k % 2));
+      }
+    }
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+    if constexpr (R::NW >= 4) {
+#pragma unroll
+      for (int i = 0; i < R::NW; i += 4)
+        *reinterpret_cast<uint4*>(q + i) = make_uint4(o.w[i], o.w[i + 1], o.w[i + 2], o.w[i + 3]);
+    } else if constexpr (R::NW == 2) {
+      *reinterpret_cast<uint2*>(q) = make_uint2(o.w[0], o.w[1]);
+    } else {
+      q[0] = o.w[0];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      if (k <= last) store_act(p, k, v[k]);
+  }
+}
+
+// Sum over the four lanes of a quad (lanes 4i .. 4i+3), returned in all four,
+// with two DPP exchanges (quad_perm [1,0,3,2] then [2,3,0,1]).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
+                                                          0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
+                                                          0xF, 0xF, true));
+  return v;
+}
+
+__device__ __forceinline__ float sigmoid_f32(float x) {
+  return rcp_hw(1.0f + exp2_hw(-x * kLog2e));
+}
+
 // Polling load: coherent at device scope but without the cache invalidation
 // an acquire carries; pair with acquire_fence() once the value is seen.
 __device__ __forceinline__ int load_relaxed(const int* p) {

@@ -53,14 +53,24 @@ struct FwdPtrs {
 constexpr int kChunk = 32;
 constexpr int chunk_for_groups(int groups) { return groups >= 8 ? 16 : 32; }
 
-// Launches the forward kernel instance for (dtype, groups, states/group).
-// Returns hipErrorInvalidValue for an unsupported combination.
-hipError_t launch_scan_fwd(int dtype, int groups, int per_group,
-                           const FwdPtrs& p, const FwdScratch& s,
-                           const FwdShape& sh, int64_t workgroups,
-                           hipStream_t stream);
-
-hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t stream);
+// The forward is built once per activation type; each build lives in its own
+// namespace (fwd_f32, fwd_bf16) with the same interface:
+//   launch_scan_fwd   the kernel instance for (groups, states/group), or
+//                     hipErrorInvalidValue for an unsupported combination;
+//   launch_fill_zero  zeroes the ticket/status words before a launch;
+//   read_and_clear_errors  reads and clears that build's count of carry
+//                     waits that timed out (synchronises the stream first).
+#define SSM_DECLARE_FWD(NS)                                                           \
+  namespace NS {                                                                      \
+  hipError_t launch_scan_fwd(int groups, int per_group, const FwdPtrs& p,             \
+                             const FwdScratch& s, const FwdShape& sh,                 \
+                             int64_t workgroups, hipStream_t stream);                 \
+  hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t stream);                 \
+  hipError_t read_and_clear_errors(hipStream_t stream, unsigned* count);              \
+  }
+SSM_DECLARE_FWD(fwd_f32)
+SSM_DECLARE_FWD(fwd_bf16)
+#undef SSM_DECLARE_FWD
 
 hipError_t launch_state_update(int dtype, int dstate, float* state,
                                const void* x, const void* dt, const float* A,
@@ -69,7 +79,58 @@ hipError_t launch_state_update(int dtype, int dstate, float* state,
                                int softplus, int zoh, void* out, int64_t batch,
                                int64_t dim, hipStream_t stream);
 
-// Reads and clears this device's count of carry waits that timed out.
-hipError_t read_and_clear_errors(hipStream_t stream, unsigned* count);
+// Backward: inputs, outputs and scratch of one call.  Activations and their
+// gradients (u, delta, z, dout, du, ddelta, dz, B, C, dB, dC) are of the call's
+// dtype; everything else is float32.  Nullable: D, z, dt_bias, h0, dlast
+// (inputs) and dD, dz, ddt_bias, dh0 (outputs).
+struct BwdPtrs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  const float* h0;
+  const void* dout;
+  const float* dlast;
+  void* du;
+  void* ddelta;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;
+  void* dz;
+  float* ddt_bias;
+  float* dh0;
+  // scratch
+  float* ckpt;       // [batch * channel blocks][chunks][N][64] chunk-start states
+  float* part_bc;    // [channel blocks][batch][L][2N] per-block dB | dC rows
+  float* part_a;     // [batch][dim][N] per-batch dA
+  float* part_d;     // [batch][dim] per-batch dD
+  float* part_bias;  // [batch][dim] per-batch ddt_bias
+};
+
+struct BwdShape {
+  int64_t batch;
+  int64_t seqlen;
+  int64_t dim;
+  int32_t n_cblk;    // channel blocks of 64
+  int64_t nchunks;   // ceil(seqlen / kBwdChunk)
+  int32_t softplus;
+  int32_t has_D, has_z, has_bias, has_h0, has_dlast;
+  int32_t vec_io;    // activation rows may be moved in aligned vector runs
+};
+
+// Steps per chunk of the backward (one checkpoint per chunk; the chunk's
+// states and decays are recomputed into registers).
+constexpr int kBwdChunk = 8;
+
+// Launches the backward kernel for (dtype, N) and the reductions over channel
+// blocks and batch.  Returns hipErrorInvalidValue for an unsupported N.
+hipError_t launch_scan_bwd(int dtype, int dstate, const BwdPtrs& p, const BwdShape& sh,
+                           hipStream_t stream);
+
 
 }  // namespace ssm
