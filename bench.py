@@ -53,6 +53,27 @@ def valu_slots_per_token_channel(n, bbar="delta"):
     return (16 if bbar == "zoh" else 6) * n + 20
 
 
+def bwd_valu_slots_per_token_channel(n):
+    """Algorithmic fp32 VALU issue slots per token*channel of the backward
+    with recomputation: per state the recomputed step and readout (mul, exp
+    (2), mul, fma, fma = 6), the adjoint (lambda fma, dC and dB products,
+    sum lambda B fma, Abar h_{t-1} and its product with lambda, sum with A,
+    dA fma, the carried Abar lambda = 9) and the two channel sums of dB and
+    dC (2): 17 slots; per channel step softplus and its derivative (14), the
+    gate and its derivative (12), du and dDelta (4): 30 slots."""
+    return 17 * n + 30
+
+
+def bwd_algorithmic_bytes(w):
+    """Reads u, dt, z, dout, B, C and the parameters; writes du, ddt, dz, dB,
+    dC and the parameter gradients."""
+    e = 2 if w.dtype == "bf16" else 4
+    blD = w.batch * w.seqlen * w.dim
+    blN = w.batch * w.seqlen * w.dstate
+    params = 4 * (w.dim * w.dstate + 2 * w.dim)
+    return 7 * e * blD + 4 * e * blN + 2 * params
+
+
 def transcendentals_per_token_channel(n):
     """exp per state, plus exp/log/rcp of softplus and exp/rcp of the gate."""
     return n + 5
@@ -72,6 +93,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate host time budget of the oracle baseline")
+    p.add_argument("--bwd", action="store_true",
+                   help="instead of the step: time the backward (selective_scan_bwd) on the "
+                        "forward workload; one JSON line with its own roofline and CPU baseline")
     p.add_argument("--l-sweep", action="store_true",
                    help="instead of the step: time the forward alone over L = 2^10 .. 2^20 "
                         "at B=1, D=256, N=16, float32 (one JSON line per L)")
@@ -155,6 +179,97 @@ def dec_dim(dec):
     return dec["u"].shape[1]
 
 
+def bwd_bench(args, torch, dev):
+    """Times selective_scan_bwd on the workload's forward inputs with a
+    seeded N(0,1) output gradient."""
+    from selective_state_space_38_amd import check_device_errors, selective_scan_bwd
+
+    w = synth.WORKLOADS[args.workload]
+    act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = synth.make(w)
+    dout_np = np.random.default_rng(w.seed + 100).standard_normal(x["u"].shape).astype(np.float32)
+    if w.dtype == "bf16":
+        dout_np = synth.round_bf16(dout_np)
+
+    def up(a, dtype=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dtype)
+
+    u, dt, z, dout = up(x["u"], act), up(x["delta"], act), up(x["z"], act), up(dout_np, act)
+    Bm, Cm = up(x["B"], act), up(x["C"], act)
+    A, Dv, bias = up(x["A"]), up(x["D"]), up(x["dt_bias"])
+
+    def bwd():
+        return selective_scan_bwd(u, dt, A, Bm, Cm, dout, D=Dv, z=z, delta_bias=bias)
+
+    for _ in range(args.warmup):
+        bwd()
+    torch.cuda.synchronize()
+    check_device_errors(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        bwd()
+        e[1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    avg = float(np.mean(ms))
+    tokch = w.batch * w.seqlen * w.dim
+    slots = bwd_valu_slots_per_token_channel(w.dstate) * tokch
+    achieved = slots / (avg / 1e3) / 1e12
+    nbytes = bwd_algorithmic_bytes(w)
+    line = {
+        "metric": "selective-scan bwd tokens·channels/s, 1 GPU",
+        "value": tokch / (avg / 1e3),
+        "unit": "tokens·channels/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded N(0,1) activations and output gradient)",
+        "config": {"workload": (f"{w.name} backward (B={w.batch}, L={w.seqlen}, D={w.dim}, "
+                                f"N={w.dstate}, {w.dtype} activations)")},
+        "roofline": {
+            "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS, "unit": "TFLOP/s",
+            "frac": achieved / VALU_PEAK_TOPS, "traffic": None,
+            "kernel": "scan_bwd_kernel (+ reductions)",
+            "ops_per_unit": f"{bwd_valu_slots_per_token_channel(w.dstate)} fp32 VALU issue "
+                            "slots per token*channel",
+            "units_per_launch": tokch, "avg_launch_ms": avg,
+            "median_launch_ms": float(np.median(ms)), "min_launch_ms": float(np.min(ms)),
+        },
+        "hbm": {"algorithmic_bytes": nbytes, "GBps": nbytes / (avg / 1e3) / 1e9,
+                "frac_of_8TBps": nbytes / (avg / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        print("bench: timing the CPU oracle backward", file=sys.stderr, flush=True)
+
+        def sample(Lp):
+            sl = slice(0, Lp)
+            return dict(u=x["u"][:, sl], delta=x["delta"][:, sl], A=x["A"], B=x["B"][:, sl],
+                        C=x["C"][:, sl], D=x["D"], z=x["z"][:, sl], dt_bias=x["dt_bias"],
+                        dout=dout_np[:, sl])
+
+        t0 = time.perf_counter()
+        oracle.scan_bwd(**sample(4))
+        per_step = (time.perf_counter() - t0) / 4
+        Lp = int(max(4, min(w.seqlen, args.cpu_seconds / max(per_step, 1e-6))))
+        t0 = time.perf_counter()
+        oracle.scan_bwd(**sample(Lp))
+        tb = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": w.batch * Lp * w.dim / tb, "unit": "tokens·channels/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"float64 NumPy oracle backward, single-threaded ufuncs: all {w.batch} "
+                       f"batch rows and {w.dim} channels, first {Lp} of {w.seqlen} steps "
+                       f"({tb:.1f} s)"),
+        }
+    print(json.dumps(line), flush=True)
+
+
 def l_sweep(args, torch, dev):
     """Forward time against sequence length at the million-token shape's width:
     the work is linear in L, so tokens*channels/s should level off, not fall."""
@@ -221,6 +336,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.l_sweep:
         l_sweep(args, torch, dev)
+        return
+    if args.bwd:
+        bwd_bench(args, torch, dev)
         return
     w = synth.WORKLOADS[args.workload]
     dw = synth.WORKLOADS["decode"]

@@ -301,14 +301,19 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.has_h0 = h0 != nullptr;
   sh.has_dlast = dlast != nullptr;
   {
-    const int64_t ept = ssm::kBwdChunk / bwd_groups(N);
+    // a run of ept channels may move as one vector when every run is whole
+    // and aligned
     const int64_t esz = dims->dtype == SSM_BF16 ? 2 : 4;
-    const uintptr_t need = static_cast<uintptr_t>(ept * esz >= 16 ? 16 : ept * esz);
-    bool ok = ept * esz >= 4 && dims->dim % ept == 0;
-    const void* acts[] = {u, delta, z, dout, du, ddelta, dz};
-    for (const void* a : acts)
-      if (a && !aligned(a, need)) ok = false;
-    sh.vec_io = ok ? 1 : 0;
+    auto vec_ok = [&](int64_t ept) {
+      const uintptr_t need = static_cast<uintptr_t>(ept * esz >= 16 ? 16 : ept * esz);
+      bool ok = ept * esz >= 4 && dims->dim % ept == 0;
+      const void* acts[] = {u, delta, z, dout, du, ddelta, dz};
+      for (const void* a : acts)
+        if (a && !aligned(a, need)) ok = false;
+      return ok ? 1 : 0;
+    };
+    sh.vec_io = vec_ok(ssm::kBwdChunk / bwd_groups(N));
+    sh.vec_io_f = vec_ok(ssm::kBwdFwdChunk / bwd_groups(N));
   }
 
   rc = SSM_OK;

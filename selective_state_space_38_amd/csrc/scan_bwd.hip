@@ -47,27 +47,48 @@
 
 namespace ssm {
 
-template <typename T, int NG, int G, int TC>
+template <typename T, int NG, int G, int TC, int TCF>
 __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
   constexpr int N = NG * G;
   constexpr int NT = 64 * NG;
-  constexpr int EPT = TC / NG;        // tile elements per thread (one row run)
-  constexpr int TPR = 64 / EPT;       // threads per tile row
-  constexpr int NQ = 16;              // quads per wave
+  constexpr int NQ = 16;                       // quads per wave
+  constexpr int EPT = TC / NG;                 // phase R: tile elements per thread
+  constexpr int TPR = 64 / EPT;
+  constexpr int EPTF = TCF / NG;               // phase F: tile elements per thread
+  constexpr int TPRF = 64 / EPTF;
+  constexpr int SUB = TCF / TC;                // checkpoints per phase-F chunk
   static_assert(TC % NG == 0 && EPT >= 1 && 64 % EPT == 0, "tile must split over the waves");
-  static_assert(NT % TC == 0, "tile rows must split over the threads");
-  constexpr int BCE = (TC * N + NT - 1) / NT;  // B/C (or dB/dC) elements per thread
-  using TileRun = Run<T, EPT>;
+  static_assert(TCF % TC == 0 && 64 % EPTF == 0, "phase F chunk must hold whole chunks");
+  static_assert(NT % TC == 0 && NT % TCF == 0, "tile rows must split over the threads");
+  constexpr int BCE = (TC * N + NT - 1) / NT;   // B/C (or dB/dC) elements per thread, phase R
+  constexpr int BCEF = (TCF * N + NT - 1) / NT; // B elements per thread, phase F
+  using RunR = Run<T, EPT>;
+  using RunF = Run<T, EPTF>;
 
-  __shared__ float s_dl[TC][64];
-  __shared__ float s_du[TC][64];
-  __shared__ float s_dy[TC][64];
-  __shared__ __align__(16) float s_B[TC][N];
-  __shared__ __align__(16) float s_C[TC][N];
-  __shared__ float s_p1[NG][TC][64];                    // partial y, then partial sum lambda B
-  __shared__ float s_p2[NG][TC][64];                    // partial sum lambda Abar h A
-  __shared__ __align__(16) float s_rB[TC][NQ][N];      // quad sums of lambda Delta u
-  __shared__ __align__(16) float s_rC[TC][NQ][N];      // quad sums of dy h
+  // Phase F and phase R use the same LDS.
+  struct SmemR {
+    float dl[TC][64];
+    float du[TC][64];
+    float dy[TC][64];
+    float B[TC][N];
+    float C[TC][N];
+    float p1[NG][TC][64];      // partial y, then partial sum_n lambda B
+    float p2[NG][TC][64];      // partial sum_n lambda Abar h_{t-1} A
+    // quad sums of lambda Delta u and of dy h; rows padded to N + 1 words
+    // so the 16 quad leaders of a wave write to 16 different banks
+    float rB[TC][NQ][N + 1];
+    float rC[TC][NQ][N + 1];
+  };
+  struct SmemF {
+    float dl[2][TCF][64];
+    float du[2][TCF][64];
+    float B[2][TCF][N];
+  };
+  union Smem {
+    SmemR r;
+    SmemF f;
+  };
+  __shared__ __align__(16) Smem sm;
 
   const T* const xu = static_cast<const T*>(p.u);
   const T* const xdt = static_cast<const T*>(p.delta);
@@ -100,99 +121,197 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
     Af[g] = p.A[dc * N + gidx + g];
     A2[g] = Af[g] * kLog2e;
   }
-
-  // tile role: row tr, channels tch .. tch + EPT - 1
-  const int tr = tid / TPR;
-  const int tc = (tid - tr * TPR) * EPT;
-  const int64_t tch = ch0 + tc;
-  const bool run_valid = tch < dim;
-  const int run_last = run_valid ? static_cast<int>((dim - 1 - tch) < (EPT - 1) ? (dim - 1 - tch)
-                                                                                : (EPT - 1))
-                                 : -1;
-  const bool run_vec = TileRun::kCanVec && sh.vec_io != 0 && run_valid;
-  const int64_t tch_c = run_valid ? tch : dim - 1;
-  float rD[EPT], rbias[EPT];
-#pragma unroll
-  for (int k = 0; k < EPT; ++k) {
-    const int64_t ck = tch_c + (k < run_last ? k : (run_last > 0 ? run_last : 0));
-    rD[k] = sh.has_D ? p.D[ck] : 0.0f;
-    rbias[k] = sh.has_bias ? p.dt_bias[ck] : 0.0f;
-  }
   const int64_t row0 = static_cast<int64_t>(b) * L;
   const int64_t nck = sh.nchunks;
   float* ckpt = p.ckpt + (static_cast<int64_t>(wg) * nck) * N * 64;
 
-  auto load_run = [&](TileRun& r, const T* base, int64_t off) {
-    if (run_vec) {
-      r.load_vec(base + off);
-    } else {
-      r.load_elems(base + off, run_last > 0 ? run_last : 0);
-    }
+  // Tile roles: a thread owns one row of a chunk tile and a run of EPT (phase
+  // R) or EPTF (phase F) consecutive channels.  last = index of the run's
+  // last channel inside dim, -1 if none.
+  auto run_role = [&](int ept, int tpr, int& row, int& col, int& last) {
+    row = tid / tpr;
+    col = (tid - row * tpr) * ept;
+    const int64_t first = ch0 + col;
+    last = first < dim ? static_cast<int>((dim - 1 - first) < (ept - 1) ? (dim - 1 - first)
+                                                                     : (ept - 1))
+                       : -1;
   };
-  // Chunk inputs for the scan lanes: Delta, Delta*u (zero on padded rows and
-  // channels past dim) and B (and C); the thread keeps its run's raw values.
-  struct RunVals {
-    float u[EPT], dl[EPT], sig[EPT];
-  };
-  auto stage = [&](int64_t c0, int n, bool with_c, RunVals& rv) {
-    const int r = tr < n ? tr : n - 1;
-    const int64_t off = (row0 + c0 + r) * dim + tch_c;
-    TileRun rdt, ru;
-    load_run(rdt, xdt, off);
-    load_run(ru, xu, off);
-    const bool row_ok = tr < n;
+  int tr, tc, run_last, trf, tcf, run_last_f;
+  run_role(EPT, TPR, tr, tc, run_last);
+  run_role(EPTF, TPRF, trf, tcf, run_last_f);
+  const int64_t tch = ch0 + tc, tchf = ch0 + tcf;
+  const bool run_valid = run_last >= 0, run_valid_f = run_last_f >= 0;
+  const bool run_vec = RunR::kCanVec && sh.vec_io != 0 && run_valid;
+  const bool run_vec_f = RunF::kCanVec && sh.vec_io_f != 0 && run_valid_f;
+  const int64_t tch_c = run_valid ? tch : dim - 1;
+  const int64_t tchf_c = run_valid_f ? tchf : dim - 1;
+  const int elem_last = run_last > 0 ? run_last : 0;
+  const int elem_last_f = run_last_f > 0 ? run_last_f : 0;
+
+  // ---- phase F: checkpoints, with loads one chunk of TCF steps ahead -------
+  {
+    float rbias_f[EPTF];
 #pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      const bool ok = row_ok && k <= run_last;
-      const float s = rdt.get(k) + rbias[k];
-      const float dl = sh.softplus ? softplus_f32(s) : s;
-      rv.u[k] = ru.get(k);
-      rv.dl[k] = ok ? dl : 0.0f;
-      rv.sig[k] = sh.softplus ? sigmoid_f32(s) : 1.0f;
-      s_dl[tr][tc + k] = rv.dl[k];
-      s_du[tr][tc + k] = ok ? dl * rv.u[k] : 0.0f;
+    for (int k = 0; k < EPTF; ++k)
+      rbias_f[k] = sh.has_bias ? p.dt_bias[tchf_c + (k < elem_last_f ? k : elem_last_f)] : 0.0f;
+    struct RawF {
+      RunF dt, u;
+      T bb[BCEF];
+    };
+    auto load_f = [&](int64_t c0, int n, RawF& r) {
+      const int rr = trf < n ? trf : n - 1;
+      const int64_t off = (row0 + c0 + rr) * dim + tchf_c;
+      if (run_vec_f) {
+        r.dt.load_vec(xdt + off);
+        r.u.load_vec(xu + off);
+      } else {
+        r.dt.load_elems(xdt + off, elem_last_f);
+        r.u.load_elems(xu + off, elem_last_f);
+      }
+      const int64_t base = (row0 + c0) * N;
+#pragma unroll
+      for (int k = 0; k < BCEF; ++k) {
+        const int e = tid + k * NT;
+        r.bb[k] = xB[base + ((e < n * N) ? e : 0)];
+      }
+    };
+    auto stage_f = [&](int buf, int n, const RawF& r) {
+      r.dt.consume_all();
+      r.u.consume_all();
+#pragma unroll
+      for (int k = 0; k < EPTF; ++k) {
+        const bool ok = trf < n && k <= run_last_f;
+        const float s = r.dt.get(k) + rbias_f[k];
+        const float dl = sh.softplus ? softplus_f32(s) : s;
+        sm.f.dl[buf][trf][tcf + k] = ok ? dl : 0.0f;
+        sm.f.du[buf][trf][tcf + k] = ok ? dl * r.u.get(k) : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < BCEF; ++k) {
+        const int e = tid + k * NT;
+        const float bv = to_f32(r.bb[k]);
+        if (e < TCF * N) sm.f.B[buf][e / N][e % N] = e < n * N ? bv : 0.0f;
+      }
+    };
+    float h[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      h[g] = (sh.has_h0 && dvalid) ? p.h0[(static_cast<int64_t>(b) * dim + d) * N + gidx + g]
+                                   : 0.0f;
+    const int64_t nckf = (L + TCF - 1) / TCF;
+    RawF raw;
+    load_f(0, static_cast<int>(L < TCF ? L : TCF), raw);
+    stage_f(0, static_cast<int>(L < TCF ? L : TCF), raw);
+    drain_vmem();
+    lds_barrier();
+    int buf = 0;
+    for (int64_t cf = 0; cf < nckf; ++cf) {
+      const int64_t nx = cf + 1 < nckf ? cf + 1 : cf;   // the last chunk reloads itself
+      const int64_t nx0 = nx * TCF;
+      const int n_nx = static_cast<int>((L - nx0 < TCF) ? L - nx0 : TCF);
+      load_f(nx0, n_nx, raw);
+#pragma unroll
+      for (int sc = 0; sc < SUB; ++sc) {
+        const int64_t c = cf * SUB + sc;
+        if (c < nck) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) ckpt[(c * N + gidx + g) * 64 + lane] = h[g];
+        }
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+          const int row = sc * TC + t;
+          const float dl = sm.f.dl[buf][row][lane];
+          const float du = sm.f.du[buf][row][lane];
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            h[g] = fmaf(exp2_hw(dl * A2[g]), h[g], du * sm.f.B[buf][row][gidx + g]);
+        }
+      }
+      stage_f(buf ^ 1, n_nx, raw);
+      lds_barrier();
+      buf ^= 1;
+    }
+  }
+  __syncthreads();  // phase F's LDS is reused by phase R
+
+  // ---- phase R: chunks of TC steps in reverse, loads one chunk ahead -------
+  float rD[EPT], rbias[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int64_t ck = tch_c + (k < elem_last ? k : elem_last);
+    rD[k] = sh.has_D ? p.D[ck] : 0.0f;
+    rbias[k] = sh.has_bias ? p.dt_bias[ck] : 0.0f;
+  }
+  struct RawR {
+    RunR dt, u, z, dout;
+    T bb[BCE], cc[BCE];
+    float ck[G];
+  };
+  // the thread's run of a chunk, converted
+  struct RunVals {
+    float u[EPT], dl[EPT], sig[EPT], z[EPT], dout[EPT];
+  };
+  auto load_r = [&](int64_t c, RawR& r) {
+    const int64_t c0 = c * TC;
+    const int n = static_cast<int>((L - c0 < TC) ? L - c0 : TC);
+    const int rr = tr < n ? tr : n - 1;
+    const int64_t off = (row0 + c0 + rr) * dim + tch_c;
+    if (run_vec) {
+      r.dt.load_vec(xdt + off);
+      r.u.load_vec(xu + off);
+      if (sh.has_z) r.z.load_vec(xz + off);
+      r.dout.load_vec(xdo + off);
+    } else {
+      r.dt.load_elems(xdt + off, elem_last);
+      r.u.load_elems(xu + off, elem_last);
+      if (sh.has_z) r.z.load_elems(xz + off, elem_last);
+      r.dout.load_elems(xdo + off, elem_last);
     }
     const int64_t base = (row0 + c0) * N;
 #pragma unroll
     for (int k = 0; k < BCE; ++k) {
       const int e = tid + k * NT;
-      if (e < TC * N) {
-        const int row = e / N;
-        const int ec = row < n ? e : 0;
-        const float bv = to_f32(xB[base + ec]);
-        s_B[row][e - row * N] = row < n ? bv : 0.0f;
-        if (with_c) {
-          const float cv = to_f32(xC[base + ec]);
-          s_C[row][e - row * N] = row < n ? cv : 0.0f;
-        }
-      }
+      const int64_t ec = base + ((e < n * N) ? e : 0);
+      r.bb[k] = xB[ec];
+      r.cc[k] = xC[ec];
     }
-  };
-
-  // ---- phase F: checkpoints ----------------------------------------------
-  float h[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-    h[g] = (sh.has_h0 && dvalid) ? p.h0[(static_cast<int64_t>(b) * dim + d) * N + gidx + g] : 0.0f;
-  for (int64_t c = 0; c < nck; ++c) {
+    for (int g = 0; g < G; ++g) r.ck[g] = ckpt[(c * N + gidx + g) * 64 + lane];
+  };
+  auto stage_r = [&](int64_t c, const RawR& r, RunVals& rv, float (&hst)[G]) {
     const int64_t c0 = c * TC;
     const int n = static_cast<int>((L - c0 < TC) ? L - c0 : TC);
-    RunVals rv;
-    stage(c0, n, false, rv);
-    lds_barrier();
+    r.dt.consume_all();
+    r.u.consume_all();
+    if (sh.has_z) r.z.consume_all();
+    r.dout.consume_all();
 #pragma unroll
-    for (int g = 0; g < G; ++g) ckpt[(c * N + gidx + g) * 64 + lane] = h[g];
-#pragma unroll
-    for (int t = 0; t < TC; ++t) {
-      const float dl = s_dl[t][lane];
-      const float du = s_du[t][lane];
-#pragma unroll
-      for (int g = 0; g < G; ++g) h[g] = fmaf(exp2_hw(dl * A2[g]), h[g], du * s_B[t][gidx + g]);
+    for (int k = 0; k < EPT; ++k) {
+      const bool ok = tr < n && k <= run_last;
+      const float s = r.dt.get(k) + rbias[k];
+      const float dl = sh.softplus ? softplus_f32(s) : s;
+      rv.u[k] = r.u.get(k);
+      rv.dl[k] = ok ? dl : 0.0f;
+      rv.sig[k] = sh.softplus ? sigmoid_f32(s) : 1.0f;
+      rv.z[k] = sh.has_z ? r.z.get(k) : 0.0f;
+      rv.dout[k] = r.dout.get(k);
+      sm.r.dl[tr][tc + k] = rv.dl[k];
+      sm.r.du[tr][tc + k] = ok ? dl * rv.u[k] : 0.0f;
     }
-    lds_barrier();
-  }
+#pragma unroll
+    for (int k = 0; k < BCE; ++k) {
+      const int e = tid + k * NT;
+      const float bv = to_f32(r.bb[k]);
+      const float cv = to_f32(r.cc[k]);
+      if (e < TC * N) {
+        sm.r.B[e / N][e % N] = e < n * N ? bv : 0.0f;
+        sm.r.C[e / N][e % N] = e < n * N ? cv : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) hst[g] = r.ck[g];
+  };
 
-  // ---- phase R: chunks in reverse ------------------------------------------
   float lamn[G], dA_acc[G];   // lamn = Abar_{t+1} lambda_{t+1}
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -208,40 +327,38 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
   }
   float* part_bc = p.part_bc + (static_cast<int64_t>(cblk) * bsz + b) * L * (2 * N);
 
+  RawR raw;
+  RunVals rv;
+  float hstart[G];
+  load_r(nck - 1, raw);
+  stage_r(nck - 1, raw, rv, hstart);
+  drain_vmem();
+  lds_barrier();
   for (int64_t c = nck - 1; c >= 0; --c) {
     const int64_t c0 = c * TC;
     const int n = static_cast<int>((L - c0 < TC) ? L - c0 : TC);
     const bool row_ok = tr < n;
-    RunVals rv;
-    stage(c0, n, true, rv);
-    const int r = tr < n ? tr : n - 1;
-    const int64_t off = (row0 + c0 + r) * dim + tch_c;
-    TileRun rz, rdo;
-    if (sh.has_z) load_run(rz, xz, off);
-    load_run(rdo, xdo, off);
-    lds_barrier();
+    const int64_t cn = c > 0 ? c - 1 : 0;   // next chunk to stage (the first reloads itself)
+    load_r(cn, raw);
 
     // recompute the chunk's states and decays from its checkpoint
-    float hstart[G], hs[TC][G], as[TC][G];
+    float h[G], hs[TC][G], as[TC][G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      hstart[g] = ckpt[(c * N + gidx + g) * 64 + lane];
-      h[g] = hstart[g];
-    }
+    for (int g = 0; g < G; ++g) h[g] = hstart[g];
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
-      const float dl = s_dl[t][lane];
-      const float du = s_du[t][lane];
+      const float dl = sm.r.dl[t][lane];
+      const float du = sm.r.du[t][lane];
       float y = 0.0f;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float a = exp2_hw(dl * A2[g]);
-        h[g] = fmaf(a, h[g], du * s_B[t][gidx + g]);
+        h[g] = fmaf(a, h[g], du * sm.r.B[t][gidx + g]);
         as[t][g] = a;
         hs[t][g] = h[g];
-        y = fmaf(s_C[t][gidx + g], h[g], y);
+        y = fmaf(sm.r.C[t][gidx + g], h[g], y);
       }
-      s_p1[w][t][lane] = y;
+      sm.r.p1[w][t][lane] = y;
     }
     lds_barrier();
 
@@ -252,21 +369,21 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
 #pragma unroll
       for (int k = 0; k < EPT; ++k) {
         const bool ok = row_ok && k <= run_last;
-        float y = s_p1[0][tr][tc + k];
+        float y = sm.r.p1[0][tr][tc + k];
 #pragma unroll
-        for (int q = 1; q < NG; ++q) y += s_p1[q][tr][tc + k];
+        for (int q = 1; q < NG; ++q) y += sm.r.p1[q][tr][tc + k];
         y += rD[k] * rv.u[k];
-        const float go = rdo.get(k);
+        const float go = rv.dout[k];
         float dyk = go;
         dzv[k] = 0.0f;
         if (sh.has_z) {
-          const float zv = rz.get(k);
+          const float zv = rv.z[k];
           const float sg = sigmoid_f32(zv);
           dyk = go * (zv * sg);
           dzv[k] = go * y * (sg * fmaf(zv, 1.0f - sg, 1.0f));
         }
         dy[k] = ok ? dyk : 0.0f;
-        s_dy[tr][tc + k] = dy[k];
+        sm.r.dy[tr][tc + k] = dy[k];
         dD_acc[k] = fmaf(dy[k], rv.u[k], dD_acc[k]);
       }
       if (sh.has_z && gdz && row_ok && run_valid)
@@ -277,25 +394,25 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
     // adjoint over the chunk, last step first
 #pragma unroll
     for (int t = TC - 1; t >= 0; --t) {
-      const float dl = s_dl[t][lane];
-      const float du = s_du[t][lane];
-      const float dyt = s_dy[t][lane];
+      const float dl = sm.r.dl[t][lane];
+      const float du = sm.r.du[t][lane];
+      const float dyt = sm.r.dy[t][lane];
       float s1 = 0.0f, s2 = 0.0f;
       float pB[G], pC[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float lam = fmaf(dyt, s_C[t][gidx + g], lamn[g]);
+        const float lam = fmaf(dyt, sm.r.C[t][gidx + g], lamn[g]);
         pC[g] = dyt * hs[t][g];
         pB[g] = lam * du;
-        s1 = fmaf(lam, s_B[t][gidx + g], s1);
+        s1 = fmaf(lam, sm.r.B[t][gidx + g], s1);
         const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][g] : hstart[g];
         const float lq = lam * (as[t][g] * hp);
         s2 = fmaf(lq, Af[g], s2);
         dA_acc[g] = fmaf(lq, dl, dA_acc[g]);
         lamn[g] = as[t][g] * lam;
       }
-      s_p1[w][t][lane] = s1;
-      s_p2[w][t][lane] = s2;
+      sm.r.p1[w][t][lane] = s1;
+      sm.r.p2[w][t][lane] = s2;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         pB[g] = quad_sum(pB[g]);
@@ -304,8 +421,8 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
       if ((lane & 3) == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          s_rB[t][lane >> 2][gidx + g] = pB[g];
-          s_rC[t][lane >> 2][gidx + g] = pC[g];
+          sm.r.rB[t][lane >> 2][gidx + g] = pB[g];
+          sm.r.rC[t][lane >> 2][gidx + g] = pC[g];
         }
       }
     }
@@ -317,12 +434,12 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
 #pragma unroll
       for (int k = 0; k < EPT; ++k) {
         const bool ok = row_ok && k <= run_last;
-        float S1 = s_p1[0][tr][tc + k];
-        float S2 = s_p2[0][tr][tc + k];
+        float S1 = sm.r.p1[0][tr][tc + k];
+        float S2 = sm.r.p2[0][tr][tc + k];
 #pragma unroll
         for (int q = 1; q < NG; ++q) {
-          S1 += s_p1[q][tr][tc + k];
-          S2 += s_p2[q][tr][tc + k];
+          S1 += sm.r.p1[q][tr][tc + k];
+          S2 += sm.r.p2[q][tr][tc + k];
         }
         duv[k] = fmaf(rv.dl[k], S1, rD[k] * dy[k]);
         const float ddl = fmaf(rv.u[k], S1, S2);
@@ -345,8 +462,8 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
         float sb = 0.0f, scv = 0.0f;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          sb += s_rB[row][q][nn];
-          scv += s_rC[row][q][nn];
+          sb += sm.r.rB[row][q][nn];
+          scv += sm.r.rC[row][q][nn];
         }
         if (row < n) {
           float* pr = part_bc + (c0 + row) * (2 * N);
@@ -355,6 +472,10 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
         }
       }
     }
+    // the next chunk's inputs (its rows and channels are read only after
+    // the barrier; the adjoint that read this chunk's finished before the
+    // barrier above)
+    stage_r(cn, raw, rv, hstart);
     lds_barrier();
   }
 
@@ -369,16 +490,16 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
   }
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
-    s_p1[0][tr][tc + k] = dD_acc[k];
-    s_p2[0][tr][tc + k] = dbias_acc[k];
+    sm.r.p1[0][tr][tc + k] = dD_acc[k];
+    sm.r.p2[0][tr][tc + k] = dbias_acc[k];
   }
   lds_barrier();
   if (tid < 64 && ch0 + tid < dim) {
     float sd = 0.0f, sbias = 0.0f;
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
-      sd += s_p1[0][t][tid];
-      sbias += s_p2[0][t][tid];
+      sd += sm.r.p1[0][t][tid];
+      sbias += sm.r.p2[0][t][tid];
     }
     p.part_d[static_cast<int64_t>(b) * dim + ch0 + tid] = sd;
     p.part_bias[static_cast<int64_t>(b) * dim + ch0 + tid] = sbias;
@@ -424,8 +545,9 @@ static dim3 grid_for(int64_t count) {
 template <typename T, int NG, int G>
 static hipError_t launch_bwd_typed(const BwdPtrs& p, const BwdShape& sh, hipStream_t st) {
   constexpr int TC = kBwdChunk;
+  constexpr int TCF = kBwdFwdChunk;
   const dim3 grid(static_cast<unsigned>(sh.batch * sh.n_cblk)), block(64 * NG);
-  hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, TC>), grid, block, 0, st, p, sh);
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, TC, TCF>), grid, block, 0, st, p, sh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int N = NG * G;

@@ -120,12 +120,15 @@ struct BwdShape {
   int64_t nchunks;   // ceil(seqlen / kBwdChunk)
   int32_t softplus;
   int32_t has_D, has_z, has_bias, has_h0, has_dlast;
-  int32_t vec_io;    // activation rows may be moved in aligned vector runs
+  int32_t vec_io;    // phase R runs (kBwdChunk / waves channels) may be vector moves
+  int32_t vec_io_f;  // phase F runs (kBwdFwdChunk / waves channels) may be vector moves
 };
 
-// Steps per chunk of the backward (one checkpoint per chunk; the chunk's
-// states and decays are recomputed into registers).
+// Steps per chunk of the backward's reverse phase (one checkpoint per chunk;
+// the chunk's states and decays are recomputed into registers), and steps
+// staged at a time by its checkpointing forward phase.
 constexpr int kBwdChunk = 8;
+constexpr int kBwdFwdChunk = 32;
 
 // Launches the backward kernel for (dtype, N) and the reductions over channel
 // blocks and batch.  Returns hipErrorInvalidValue for an unsupported N.
