@@ -203,7 +203,9 @@ int ssm_check_device_errors(void* stream);
  * segments of segment_len steps; lookback = 1 if segments exchange partial
  * aggregates (decoupled look-back), 0 if each waits for its predecessor's
  * final state; chunk = steps staged through LDS at a time; workgroups = the
- * launch's grid.  Returns SSM_OK or a validation error.
+ * launch's grid; whole_chains = how many (batch row, channel block) chains run
+ * the whole sequence in one workgroup (the others are split into `segments`).
+ * Returns SSM_OK or a validation error.
  */
 typedef struct {
   int32_t state_groups;
@@ -213,6 +215,7 @@ typedef struct {
   int32_t lookback;
   int32_t chunk;
   int64_t workgroups;
+  int32_t whole_chains;
 } ssm_fwd_plan;
 
 int ssm_fwd_plan_for(const ssm_dims* dims, ssm_fwd_plan* plan);

@@ -48,6 +48,7 @@ class SsmFwdPlan(ctypes.Structure):
         ("lookback", ctypes.c_int32),
         ("chunk", ctypes.c_int32),
         ("workgroups", ctypes.c_int64),
+        ("whole_chains", ctypes.c_int32),
     ]
 
 

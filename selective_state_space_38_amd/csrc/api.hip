@@ -12,6 +12,7 @@
 namespace {
 
 constexpr int kDefaultSpinLimit = 1 << 24;
+constexpr int64_t kComputeUnits = 256;  // MI355X (gfx950)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -79,8 +80,31 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
   if (force_seg > 0) seg_len = force_seg;
   seg_len = div_up(seg_len, ssm::kChunk) * ssm::kChunk;
   if (seg_len > d.seqlen) seg_len = div_up(d.seqlen, ssm::kChunk) * ssm::kChunk;
-  const int64_t n_seg = div_up(d.seqlen, seg_len);
+  int64_t n_seg = div_up(d.seqlen, seg_len);
   if (n_seg == 1) lookback = 0;
+  int64_t whole = n_seg == 1 ? chains : 0;
+
+  // Whole chains beyond a multiple of the CU count would double up on some
+  // CUs while the rest idle for the second half.  Those M chains are split
+  // into S ~ CUs/M look-back segments instead, so every CU runs one whole
+  // chain plus one short segment.
+  if (n_seg == 1 && force_mode < 0 && force_seg == 0) {
+    const int64_t K = (chains / kComputeUnits) * kComputeUnits;
+    const int64_t M = chains - K;
+    int64_t S = (K > 0 && M > 0) ? kComputeUnits / M : 1;
+    if (S < 3) S = 1;
+    const int force_split = env_int("SSM_FORCE_SPLIT", -1);
+    if (force_split >= 1 && K > 0 && M > 0) S = force_split;
+    if (S > 1) {
+      const int64_t sl = div_up(div_up(d.seqlen, S), ssm::kChunk) * ssm::kChunk;
+      if (div_up(d.seqlen, sl) > 1) {
+        seg_len = sl;
+        n_seg = div_up(d.seqlen, sl);
+        whole = K;
+        lookback = 1;
+      }
+    }
+  }
 
   p->state_groups = groups;
   p->states_per_group = g;
@@ -88,7 +112,8 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
   p->segment_len = static_cast<int32_t>(seg_len);
   p->lookback = lookback;
   p->chunk = chunk;
-  p->workgroups = chains * n_seg;
+  p->workgroups = whole + (chains - whole) * n_seg;
+  p->whole_chains = static_cast<int32_t>(whole);
 }
 
 int check_dims(const ssm_dims* dims) {
@@ -159,6 +184,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.dim = dims->dim;
   sh.chains = static_cast<int32_t>(chains);
   sh.n_cblk = static_cast<int32_t>(cblk);
+  sh.n_full = plan.whole_chains;
   sh.n_seg = plan.segments;
   sh.seg_len = plan.segment_len;
   sh.softplus = softplus ? 1 : 0;

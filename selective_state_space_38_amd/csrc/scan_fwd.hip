@@ -118,6 +118,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   __shared__ __align__(16) float s_C[2][TC][N];
   __shared__ float s_y[NG][TC][64];
   __shared__ int s_ticket;
+  __shared__ int s_pred_final;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,11 +126,24 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   // (and addresses built from them) in SGPRs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  if (tid == 0) s_ticket = atomicAdd(sc.ticket, 1);
-  __syncthreads();
-  const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
-  const int seg = ticket / sh.chains;
-  const int chain = ticket - seg * sh.chains;
+  // Workgroups 0 .. n_full-1 run whole chains (chain = workgroup index; they
+  // never wait).  The others are segments of the split chains and take their
+  // (segment, chain) from an atomic ticket, segment-major, so a segment only
+  // ever waits on lower tickets, which are already running.  Taking the role
+  // from the workgroup index keeps it tied to the hardware's placement
+  // (workgroups i and i + #CUs share a CU), so each CU gets one whole chain
+  // and one segment.
+  const bool whole = static_cast<int>(blockIdx.x) < sh.n_full;
+  int ticket = 0;
+  if (!whole) {
+    if (tid == 0) s_ticket = atomicAdd(sc.ticket, 1);
+    __syncthreads();
+    ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+  }
+  const int n_split = sh.chains - sh.n_full;
+  const int seg = whole ? 0 : ticket / n_split;
+  const int chain = whole ? static_cast<int>(blockIdx.x) : sh.n_full + (ticket - seg * n_split);
+  const int nseg_c = whole ? 1 : sh.n_seg;       // segments of this chain
   const int b = chain / sh.n_cblk;
   const int cblk = chain - b * sh.n_cblk;
 
@@ -178,8 +192,9 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
     rbias[k] = sh.has_bias ? bias[ck] : 0.0f;
   }
 
-  const int64_t t_begin = static_cast<int64_t>(seg) * sh.seg_len;
-  const int64_t t_end = (t_begin + sh.seg_len < L) ? t_begin + sh.seg_len : L;
+  const int64_t seg_len_c = whole ? L : sh.seg_len;
+  const int64_t t_begin = static_cast<int64_t>(seg) * seg_len_c;
+  const int64_t t_end = (t_begin + seg_len_c < L) ? t_begin + seg_len_c : L;
   const int64_t row0 = static_cast<int64_t>(b) * L;  // row of (b, t=0)
   const int rec = chain * sh.n_seg + seg;
 
@@ -486,6 +501,20 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   const int gidx = w * G;  // first state of this wave's group
   const int64_t rec_state = static_cast<int64_t>(rec) * N * 64;
   bool published = false;
+  // Look-back segment: skip the aggregate pass when the predecessor has
+  // already published the final state of every state group.  The decision is
+  // taken once for the workgroup (the aggregate pass stages tiles with
+  // workgroup barriers, so every wave must take the same path).
+  bool pred_final = false;
+  if (seg != 0 && sh.lookback) {
+    if (tid == 0) {
+      int all = 1;
+      for (int q = 0; q < NG; ++q) all &= load_relaxed(&sc.status[(rec - 1) * NG + q]) == kInclusive;
+      s_pred_final = all;
+    }
+    lds_barrier();
+    pred_final = __builtin_amdgcn_readfirstlane(s_pred_final) != 0;
+  }
   if (seg == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -497,7 +526,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g)
       h[g] = (st == kInclusive) ? sc.inc[ps + (gidx + g) * 64 + lane] : 0.0f;
-  } else if (load_relaxed(&sc.status[(rec - 1) * NG + w]) == kInclusive) {
+  } else if (pred_final) {
     // look-back mode, but the predecessor already published its final state:
     // no aggregate pass needed, behave like a chained segment
     acquire_fence();
@@ -585,7 +614,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) h[g] = acc_b[g];
-    if (seg + 1 < sh.n_seg) {
+    if (seg + 1 < nseg_c) {
       // this segment's own final state: its aggregate applied after the carry
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -598,12 +627,12 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
 
   output_pass(h);
 
-  if (!published && seg + 1 < sh.n_seg) {
+  if (!published && seg + 1 < nseg_c) {
 #pragma unroll
     for (int g = 0; g < G; ++g) sc.inc[rec_state + (gidx + g) * 64 + lane] = h[g];
     if (lane == 0) store_release(&sc.status[rec * NG + w], kInclusive);
   }
-  if (seg + 1 == sh.n_seg && sh.has_last && dvalid) {
+  if (seg + 1 == nseg_c && sh.has_last && dvalid) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
       last_state[(static_cast<int64_t>(b) * dim + d) * N + gidx + g] = h[g];

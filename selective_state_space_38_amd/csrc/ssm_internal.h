@@ -24,8 +24,9 @@ struct FwdShape {
   int64_t dim;
   int32_t chains;    // batch * channel blocks
   int32_t n_cblk;    // channel blocks of 64
-  int32_t n_seg;     // sequence segments per chain
-  int32_t seg_len;   // timesteps per segment (multiple of the chunk)
+  int32_t n_full;    // chains 0 .. n_full-1 run whole; the others are split
+  int32_t n_seg;     // sequence segments per split chain
+  int32_t seg_len;   // timesteps per segment of a split chain (multiple of the chunk)
   int32_t softplus;
   int32_t lookback;  // 1: decoupled look-back over aggregates, 0: chained
   int32_t has_bias, has_D, has_z, has_h0, has_last;

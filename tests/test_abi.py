@@ -118,7 +118,11 @@ def test_plan_query():
     assert plan.state_groups * plan.states_per_group == 16
     assert plan.segments * plan.segment_len >= 8192
     assert plan.segment_len % plan.chunk == 0
-    assert plan.workgroups == 4 * 80 * plan.segments
+    chains = 4 * 80
+    assert 0 <= plan.whole_chains <= chains
+    assert plan.workgroups == plan.whole_chains + (chains - plan.whole_chains) * plan.segments
+    # 320 chains on 256 CUs: 256 run whole, the other 64 are split
+    assert plan.whole_chains == 256 and plan.segments == 4 and plan.lookback == 1
     assert lib.ssm_fwd_plan_for(ctypes.byref(_dims(n=5)), ctypes.byref(plan)) == SSM_EINVAL
 
 

@@ -181,6 +181,27 @@ def test_carry_wait_bound_reports_timeout():
     check_device_errors()  # a normal call leaves the counter at zero
 
 
+@pytest.mark.parametrize("split", [None, 2, 8])
+def test_whole_and_split_chains(split):
+    """More chains than CUs: 256 chains run whole and the rest are split into
+    look-back segments (the planner's choice, or a forced split count)."""
+    from selective_state_space_38_amd import fwd_plan
+    x = _case("mamba130m", batch=1, seqlen=600, dim=64 * 300, dstate=16, a_init="random")
+    with env(SSM_FORCE_SPLIT=split):
+        plan = fwd_plan(1, 600, 64 * 300, 16)
+        got, st = gpu_forward(x, "f32")
+    assert plan["whole_chains"] == 256 and plan["segments"] > 1, plan
+    _log(f"mixed plan {plan}")
+    # columns of whole chains, of split chains and the block edges
+    cols = [(0, d) for d in (0, 63, 64, 16383, 16384, 16385, 17000, 19199)]
+    ref, ref_st = oracle_forward(x, cols=cols)
+    g_out = np.stack([got[b, :, d] for b, d in cols])
+    g_st = np.stack([st[b, d] for b, d in cols])
+    scale = float(np.max(np.abs(ref)))
+    check("out", g_out, ref, scale, TOL["f32"])
+    check("last_state", g_st, ref_st, scale, TOL["f32"])
+
+
 def test_lookback_wait_bound_reports_timeout():
     """The same for the windowed look-back walk: predecessors not yet
     published at the first poll end the walk, the kernel exits and the error
