@@ -30,3 +30,4 @@ from .scan import (  # noqa: F401
     scan_pairs_blelloch,
 )
 from .scan_bwd import scan_bwd  # noqa: F401
+from .conv1d import causal_conv1d, conv1d_update  # noqa: F401
