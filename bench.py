@@ -96,6 +96,9 @@ def parse():
     p.add_argument("--bwd", action="store_true",
                    help="instead of the step: time the backward (selective_scan_bwd) on the "
                         "forward workload; one JSON line with its own roofline and CPU baseline")
+    p.add_argument("--conv", action="store_true",
+                   help="instead of the step: time the causal conv1d + SiLU (width 4) on the "
+                        "forward workload's activations; one JSON line with an HBM roofline")
     p.add_argument("--l-sweep", action="store_true",
                    help="instead of the step: time the forward alone over L = 2^10 .. 2^20 "
                         "at B=1, D=256, N=16, float32 (one JSON line per L)")
@@ -270,6 +273,76 @@ def bwd_bench(args, torch, dev):
     print(json.dumps(line), flush=True)
 
 
+def conv_bench(args, torch, dev):
+    """Times causal_conv1d_fwd (width 4, SiLU, bias, final state) over the
+    workload's activation tensor; HBM-bound, so the roofline is bytes."""
+    from selective_state_space_38_amd import causal_conv1d_fwd
+
+    w = synth.WORKLOADS[args.workload]
+    act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    e = 2 if w.dtype == "bf16" else 4
+    k = 4
+    print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
+    x_np = synth.make(w)["u"]
+    r = np.random.default_rng(w.seed + 200)
+    wt_np = (r.standard_normal((w.dim, k)) * 0.5).astype(np.float32)
+    b_np = r.standard_normal(w.dim).astype(np.float32)
+    x = torch.from_numpy(x_np).to(device=dev, dtype=act)
+    wt = torch.from_numpy(wt_np).to(dev)
+    bias = torch.from_numpy(b_np).to(dev)
+    out = torch.empty_like(x)
+    st = torch.empty((w.batch, w.dim, k - 1), dtype=torch.float32, device=dev)
+
+    def conv():
+        causal_conv1d_fwd(x, wt, bias, out=out, state_out=st, return_final_state=True)
+
+    for _ in range(args.warmup):
+        conv()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ee in ev:
+        ee[0].record()
+        conv()
+        ee[1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = [ee[0].elapsed_time(ee[1]) for ee in ev]
+    avg = float(np.mean(ms))
+    tokch = w.batch * w.seqlen * w.dim
+    nbytes = 2 * e * tokch + 4 * (k * w.dim + w.dim) + 4 * w.batch * w.dim * (k - 1)
+    gbps = nbytes / (avg / 1e3) / 1e9
+    line = {
+        "metric": "causal conv1d + SiLU tokens·channels/s and achieved HBM GB/s, 1 GPU",
+        "value": tokch / (avg / 1e3), "unit": "tokens·channels/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) activations and filters)",
+        "config": {"workload": (f"{w.name} activations (B={w.batch}, L={w.seqlen}, "
+                                f"D={w.dim}, {w.dtype}), width {k}")},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "conv1d_fwd_kernel", "bytes_per_launch": nbytes,
+                     "avg_launch_ms": avg, "median_launch_ms": float(np.median(ms)),
+                     "min_launch_ms": float(np.min(ms))},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        Lp = min(w.seqlen, 512)
+        t0 = time.perf_counter()
+        oracle.causal_conv1d(x_np[:, :Lp], wt_np, b_np)
+        tb = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": w.batch * Lp * w.dim / tb, "unit": "tokens·channels/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"float64 NumPy oracle, single-threaded ufuncs: all {w.batch} batch rows "
+                       f"and {w.dim} channels, first {Lp} of {w.seqlen} steps ({tb:.2f} s)"),
+        }
+    print(json.dumps(line), flush=True)
+
+
 def l_sweep(args, torch, dev):
     """Forward time against sequence length at the million-token shape's width:
     the work is linear in L, so tokens*channels/s should level off, not fall."""
@@ -339,6 +412,9 @@ def main():
         return
     if args.bwd:
         bwd_bench(args, torch, dev)
+        return
+    if args.conv:
+        conv_bench(args, torch, dev)
         return
     w = synth.WORKLOADS[args.workload]
     dw = synth.WORKLOADS["decode"]

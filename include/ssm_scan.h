@@ -185,6 +185,38 @@ int selective_scan_bwd(const void* u, const void* delta, const float* A,
                        float* dD, void* dz, float* ddt_bias, float* dh0,
                        const ssm_dims* dims, void* stream);
 
+/*
+ * Causal depthwise conv1d + SiLU over a sequence: the short per-channel
+ * convolution a Mamba block applies before the selective SSM ("Mamba /
+ * MambaMini" Q&A on the Conv before the SSM; reading guide glossary "Mamba
+ * Block"):
+ *   out[b][t][d] = act( sum_{k<width} weight[d][k] * x[b][t-(width-1)+k][d] + bias[d] )
+ * with x at t < 0 taken from state_in (or zero).
+ *   x, out      : [B][L][D] of dims->dtype (dims->dstate is ignored)
+ *   weight      : [D][width] float32, width in 1..4;  bias : [D] float32 (nullable)
+ *   state_in    : [B][D][width-1] float32 (nullable = zeros): the width-1 inputs
+ *                 before t = 0, oldest first
+ *   state_out   : [B][D][width-1] float32 (nullable): the last width-1 inputs,
+ *                 ready for causal_conv1d_update or the next piece's state_in
+ *   silu        : nonzero -> act = SiLU, zero -> identity
+ * out must not alias x; state_out must not alias state_in or weight
+ * (SSM_EINVAL).  Returns an ssm_status.
+ */
+int causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
+                      const float* state_in, int width, int silu, void* out,
+                      float* state_out, const ssm_dims* dims, void* stream);
+
+/*
+ * One decode step of the same convolution, in place on the rolling state.
+ *   state       : [B][D][width-1] float32 (oldest first), read and shifted by
+ *                 one input (may be NULL only when width == 1)
+ *   x, out      : [B][D] of dims->dtype;  weight, bias, width, silu as above
+ *   dims->seqlen must be 1.  L successive calls reproduce causal_conv1d_fwd.
+ */
+int causal_conv1d_update(float* state, const void* x, const float* weight,
+                         const float* bias, int width, int silu, void* out,
+                         const ssm_dims* dims, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* ssm_status_string(int status);
 

@@ -5,6 +5,8 @@ from .api import (  # noqa: F401
     selective_scan_fwd,
     selective_scan_bwd,
     selective_state_update,
+    causal_conv1d_fwd,
+    causal_conv1d_update,
     check_device_errors,
     fwd_plan,
 )

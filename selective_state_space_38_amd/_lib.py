@@ -23,6 +23,8 @@ EXPORTED = (
     "selective_scan_bwd",
     "selective_state_update",
     "selective_state_update_ex",
+    "causal_conv1d_fwd",
+    "causal_conv1d_update",
     "ssm_status_string",
     "ssm_check_device_errors",
     "ssm_fwd_plan_for",
@@ -85,6 +87,12 @@ def load():
     lib.selective_state_update_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                               ctypes.c_int, ctypes.c_int, vp, dims_p, vp]
     lib.selective_state_update_ex.restype = ctypes.c_int
+    lib.causal_conv1d_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp,
+                                      dims_p, vp]
+    lib.causal_conv1d_fwd.restype = ctypes.c_int
+    lib.causal_conv1d_update.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, dims_p,
+                                         vp]
+    lib.causal_conv1d_update.restype = ctypes.c_int
     lib.ssm_status_string.argtypes = [ctypes.c_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_check_device_errors.argtypes = [vp]

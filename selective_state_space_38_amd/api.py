@@ -208,6 +208,71 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
     return out
 
 
+def _act_code(activation):
+    if activation not in ("silu", None):
+        raise ValueError(f"activation must be 'silu' or None, not {activation!r}")
+    return 1 if activation == "silu" else 0
+
+
+def causal_conv1d_fwd(x, weight, bias=None, state_in=None, activation="silu",
+                      return_final_state=False, out=None, state_out=None):
+    """Causal depthwise conv1d (+ SiLU) on the GPU.
+
+    x: [batch, L, dim] (float32 or bfloat16); weight: [dim, width] float32
+    (width 1..4); bias: [dim]; state_in: [batch, dim, width - 1] float32, the
+    inputs before t = 0 (zeros if None).  Returns out (same dtype as x) and,
+    with return_final_state, the last width - 1 inputs [batch, dim, width - 1].
+    """
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    bsz, L, dim = x.shape
+    width = weight.shape[1]
+    dev = x.device
+    _check(x, "x", x.dtype, (bsz, L, dim), dev)
+    _check(weight, "weight", torch.float32, (dim, width), dev)
+    _check(bias, "bias", torch.float32, (dim,), dev)
+    _check(state_in, "state_in", torch.float32, (bsz, dim, width - 1), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", x.dtype, (bsz, L, dim), dev)
+    if return_final_state and state_out is None:
+        state_out = torch.empty((bsz, dim, width - 1), dtype=torch.float32, device=dev)
+    _check(state_out, "state_out", torch.float32, (bsz, dim, width - 1), dev)
+    dims = _lib.SsmDims(bsz, L, dim, 1, _DTYPES[x.dtype])
+    with torch.cuda.device(dev):
+        rc = _lib.load().causal_conv1d_fwd(
+            _ptr(x), _ptr(weight), _ptr(bias), _ptr(state_in), width, _act_code(activation),
+            _ptr(out), _ptr(state_out) if state_out is not None and width > 1 else None,
+            ctypes.byref(dims), _stream(dev))
+    _raise(rc)
+    return (out, state_out) if return_final_state else out
+
+
+def causal_conv1d_update(state, x, weight, bias=None, activation="silu", out=None):
+    """One decode step of the causal conv1d on the GPU, shifting ``state``
+    ([batch, dim, width - 1] float32) by one input in place.  x: [batch, dim].
+    Returns out [batch, dim] in x's dtype."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    bsz, dim = x.shape
+    width = weight.shape[1]
+    dev = x.device
+    _check(state, "state", torch.float32, (bsz, dim, width - 1), dev)
+    _check(x, "x", x.dtype, (bsz, dim), dev)
+    _check(weight, "weight", torch.float32, (dim, width), dev)
+    _check(bias, "bias", torch.float32, (dim,), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", x.dtype, (bsz, dim), dev)
+    dims = _lib.SsmDims(bsz, 1, dim, 1, _DTYPES[x.dtype])
+    with torch.cuda.device(dev):
+        rc = _lib.load().causal_conv1d_update(
+            _ptr(state) if width > 1 else None, _ptr(x), _ptr(weight), _ptr(bias), width,
+            _act_code(activation), _ptr(out), ctypes.byref(dims), _stream(dev))
+    _raise(rc)
+    return out
+
+
 def check_device_errors(device=None):
     """Synchronises the current stream and raises if a carry wait timed out."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device

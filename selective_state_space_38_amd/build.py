@@ -19,6 +19,7 @@ SOURCES = [
     ("scan_fwd.hip", "scan_fwd_bf16", ["-DSSM_FWD_DTYPE=1"]),
     ("scan_bwd.hip", "scan_bwd", []),
     ("state_update.hip", "state_update", []),
+    ("conv1d.hip", "conv1d", []),
 ]
 
 HIPCC_FLAGS = [

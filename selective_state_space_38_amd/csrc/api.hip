@@ -349,6 +349,62 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   return rc;
 }
 
+int check_conv(const ssm_dims* dims, int width) {
+  if (!dims) return SSM_EINVAL;
+  if (dims->dtype != SSM_F32 && dims->dtype != SSM_BF16) return SSM_EDTYPE;
+  if (dims->batch <= 0 || dims->seqlen <= 0 || dims->dim <= 0) return SSM_EINVAL;
+  if (width < 1 || width > 4) return SSM_EINVAL;
+  if (dims->batch * dims->seqlen * dims->dim > (1LL << 46)) return SSM_EINVAL;
+  return SSM_OK;
+}
+
+int conv_fwd_impl(const void* x, const float* weight, const float* bias, const float* state_in,
+                  int width, int silu, void* out, float* state_out, const ssm_dims* dims,
+                  void* stream) {
+  int rc = check_conv(dims, width);
+  if (rc != SSM_OK) return rc;
+  if (!x || !weight || !out) return SSM_EINVAL;
+  const void* ptrs[] = {x, weight, bias, state_in, out, state_out};
+  for (const void* q : ptrs)
+    if (q && !aligned(q, 4)) return SSM_EALIGN;
+  if (out == x || (state_out && (state_out == state_in || state_out == weight)))
+    return SSM_EINVAL;
+  ssm::ConvPtrs p{x, weight, bias, state_in, out, state_out, nullptr};
+  ssm::ConvShape sh{};
+  sh.batch = dims->batch;
+  sh.seqlen = dims->seqlen;
+  sh.dim = dims->dim;
+  sh.silu = silu ? 1 : 0;
+  const int64_t ept = dims->dtype == SSM_BF16 ? 8 : 4;  // one 16-byte vector of channels
+  sh.vec_io = (dims->dim % ept == 0 && aligned(x, 16) && aligned(out, 16)) ? 1 : 0;
+  if (ssm::launch_conv1d_fwd(dims->dtype, width, p, sh, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return SSM_ELAUNCH;
+  return SSM_OK;
+}
+
+int conv_update_impl(float* state, const void* x, const float* weight, const float* bias,
+                     int width, int silu, void* out, const ssm_dims* dims, void* stream) {
+  int rc = check_conv(dims, width);
+  if (rc != SSM_OK) return rc;
+  if (dims->seqlen != 1) return SSM_EINVAL;
+  if (!x || !weight || !out || (width > 1 && !state)) return SSM_EINVAL;
+  const void* ptrs[] = {state, x, weight, bias, out};
+  for (const void* q : ptrs)
+    if (q && !aligned(q, 4)) return SSM_EALIGN;
+  if (out == x || (state && (out == state || state == weight))) return SSM_EINVAL;
+  ssm::ConvPtrs p{x, weight, bias, nullptr, out, nullptr, state};
+  ssm::ConvShape sh{};
+  sh.batch = dims->batch;
+  sh.seqlen = 1;
+  sh.dim = dims->dim;
+  sh.silu = silu ? 1 : 0;
+  if (ssm::launch_conv1d_update(dims->dtype, width, p, sh, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return SSM_ELAUNCH;
+  return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -401,6 +457,17 @@ int selective_scan_bwd(const void* u, const void* delta, const float* A, const v
                        void* stream) {
   return bwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, dout, dlast, du, ddelta, dA,
                   dB, dC, dD, dz, ddt_bias, dh0, dims, stream);
+}
+
+int causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
+                      const float* state_in, int width, int silu, void* out, float* state_out,
+                      const ssm_dims* dims, void* stream) {
+  return conv_fwd_impl(x, weight, bias, state_in, width, silu, out, state_out, dims, stream);
+}
+
+int causal_conv1d_update(float* state, const void* x, const float* weight, const float* bias,
+                         int width, int silu, void* out, const ssm_dims* dims, void* stream) {
+  return conv_update_impl(state, x, weight, bias, width, silu, out, dims, stream);
 }
 
 const char* ssm_status_string(int status) {

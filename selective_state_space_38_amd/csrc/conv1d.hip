@@ -1,0 +1,193 @@
+// Causal depthwise conv1d + SiLU for gfx950: the short per-channel
+// convolution a Mamba block applies before the selective SSM ("Mamba /
+// MambaMini" Q&A on the Conv before the SSM: fuse local context, then a
+// nonlinearity; reading guide glossary "Mamba Block"), and its constant-time
+// decode step on a rolling state of the last K-1 inputs.
+//
+//   out[b, t, d] = act( sum_{k<K} w[d, k] x[b, t-(K-1)+k, d] + bias[d] )
+//
+// The op streams x once and writes out once, so it is HBM-bound and laid out
+// for it: a thread owns a run of EPT consecutive channels (one 16-byte vector
+// per row) of a tile of TT time steps; a wave reads 64 runs of one row, 1 KB
+// contiguous.  The K-1 rows before the tile are read once more (the halo,
+// (K-1)/TT extra), or come from the caller's initial state at t < 0.  Rows
+// are loaded U at a time ahead of their use so each thread keeps U vector
+// loads in flight.
+
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+
+template <typename T, int K, int EPT, int TT, int U>
+__global__ __launch_bounds__(256) void conv1d_fwd_kernel(ConvPtrs p, ConvShape sh) {
+  using R = Run<T, EPT>;
+  constexpr int H = K > 1 ? K - 1 : 1;   // window rows (at least 1 for the array)
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t runs = sh.runs;
+  const int64_t tiles = sh.tiles;
+  if (g >= sh.batch * tiles * runs) return;
+  const int64_t run = g % runs;
+  const int64_t rest = g / runs;
+  const int64_t tile = rest % tiles;
+  const int64_t b = rest / tiles;
+  const int64_t L = sh.seqlen;
+  const int64_t dim = sh.dim;
+  const int64_t c0 = run * EPT;
+  const int last = static_cast<int>((dim - 1 - c0) < (EPT - 1) ? (dim - 1 - c0) : (EPT - 1));
+  const bool vec = R::kCanVec && sh.vec_io != 0;
+  const T* x = static_cast<const T*>(p.x) + b * L * dim + c0;
+  T* out = static_cast<T*>(p.out) + b * L * dim + c0;
+
+  float w[EPT][K], bias[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int64_t c = c0 + (e < last ? e : last);
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[e][k] = p.weight[c * K + k];
+    bias[e] = p.bias ? p.bias[c] : 0.0f;
+  }
+
+  auto load_row = [&](int64_t t, float (&v)[EPT]) {
+    R r;
+    if (vec) {
+      r.load_vec(x + t * dim);
+    } else {
+      r.load_elems(x + t * dim, last);
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) v[e] = r.get(e);
+  };
+
+  // window: the K-1 inputs before the current row, oldest first
+  const int64_t t0 = tile * TT;
+  const int64_t t1 = (t0 + TT < L) ? t0 + TT : L;
+  float win[H][EPT];
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    const int64_t t = t0 - (K - 1) + j;
+    if (K > 1 && t >= 0) {
+      load_row(t, win[j]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int64_t c = c0 + (e < last ? e : last);
+        win[j][e] = (K > 1 && p.state_in) ? p.state_in[(b * dim + c) * (K - 1) + (K - 1 + t)]
+                                          : 0.0f;
+      }
+    }
+  }
+
+  for (int64_t tb = t0; tb < t1; tb += U) {
+    const int nr = static_cast<int>((t1 - tb < U) ? t1 - tb : U);
+    float xv[U][EPT];
+#pragma unroll
+    for (int i = 0; i < U; ++i) load_row(tb + (i < nr ? i : nr - 1), xv[i]);
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      if (i < nr) {
+        float o[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          // oldest input first, the same order as the decode step, so L
+          // decode steps reproduce the forward bit for bit
+          float acc = bias[e];
+#pragma unroll
+          for (int k = 0; k < K - 1; ++k) acc = fmaf(w[e][k], win[k][e], acc);
+          acc = fmaf(w[e][K - 1], xv[i][e], acc);
+          o[e] = sh.silu ? acc * sigmoid_f32(acc) : acc;
+        }
+        store_run<T, EPT>(out + (tb + i) * dim, o, vec, last);
+        if constexpr (K > 1) {
+#pragma unroll
+          for (int j = 0; j < K - 2; ++j)
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) win[j][e] = win[j + 1][e];
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) win[K - 2][e] = xv[i][e];
+        }
+      }
+    }
+  }
+
+  // the tile holding the last row leaves the last K-1 inputs as the state
+  if (K > 1 && p.state_out && t1 == L) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (e <= last) {
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) p.state_out[(b * dim + c0 + e) * (K - 1) + j] = win[j][e];
+      }
+    }
+  }
+}
+
+// One decode step per (batch, channel), in place on the rolling state.
+template <typename T, int K>
+__global__ __launch_bounds__(256) void conv1d_update_kernel(ConvPtrs p, ConvShape sh) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= sh.batch * sh.dim) return;
+  const int64_t d = i % sh.dim;
+  float win[K];
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) win[j] = p.state_inout[i * (K - 1) + j];
+  win[K - 1] = to_f32(static_cast<const T*>(p.x)[i]);
+  float acc = p.bias ? p.bias[d] : 0.0f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) acc = fmaf(p.weight[d * K + k], win[k], acc);
+  store_act(static_cast<T*>(p.out), i, sh.silu ? acc * sigmoid_f32(acc) : acc);
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) p.state_inout[i * (K - 1) + j] = win[j + 1];
+}
+
+template <typename T, int K>
+static hipError_t launch_fwd_k(const ConvPtrs& p, ConvShape sh, hipStream_t st) {
+  constexpr int EPT = 16 / sizeof(T);
+  constexpr int TT = kConvTile;
+  sh.runs = (sh.dim + EPT - 1) / EPT;
+  sh.tiles = (sh.seqlen + TT - 1) / TT;
+  const int64_t threads = sh.batch * sh.tiles * sh.runs;
+  hipLaunchKernelGGL((conv1d_fwd_kernel<T, K, EPT, TT, 8>),
+                     dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st, p, sh);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dispatch_fwd(int width, const ConvPtrs& p, const ConvShape& sh,
+                               hipStream_t st) {
+  switch (width) {
+    case 1: return launch_fwd_k<T, 1>(p, sh, st);
+    case 2: return launch_fwd_k<T, 2>(p, sh, st);
+    case 3: return launch_fwd_k<T, 3>(p, sh, st);
+    case 4: return launch_fwd_k<T, 4>(p, sh, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_conv1d_fwd(int dtype, int width, const ConvPtrs& p, const ConvShape& sh,
+                             hipStream_t stream) {
+  if (dtype == 0) return dispatch_fwd<float>(width, p, sh, stream);
+  return dispatch_fwd<bf16_t>(width, p, sh, stream);
+}
+
+template <typename T>
+static hipError_t dispatch_update(int width, const ConvPtrs& p, const ConvShape& sh,
+                                  hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((sh.batch * sh.dim + 255) / 256));
+  switch (width) {
+    case 1: hipLaunchKernelGGL((conv1d_update_kernel<T, 1>), grid, dim3(256), 0, st, p, sh); break;
+    case 2: hipLaunchKernelGGL((conv1d_update_kernel<T, 2>), grid, dim3(256), 0, st, p, sh); break;
+    case 3: hipLaunchKernelGGL((conv1d_update_kernel<T, 3>), grid, dim3(256), 0, st, p, sh); break;
+    case 4: hipLaunchKernelGGL((conv1d_update_kernel<T, 4>), grid, dim3(256), 0, st, p, sh); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_conv1d_update(int dtype, int width, const ConvPtrs& p, const ConvShape& sh,
+                                hipStream_t stream) {
+  if (dtype == 0) return dispatch_update<float>(width, p, sh, stream);
+  return dispatch_update<bf16_t>(width, p, sh, stream);
+}
+
+}  // namespace ssm

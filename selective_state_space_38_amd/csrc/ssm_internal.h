@@ -137,4 +137,36 @@ hipError_t launch_scan_bwd(int dtype, int dstate, const BwdPtrs& p, const BwdSha
                            hipStream_t stream);
 
 
+// Causal depthwise conv1d (+ SiLU): forward over a sequence and the decode
+// step.  x and out are of the call's dtype; weight [dim][K], bias [dim] and
+// the states [batch][dim][K-1] (oldest input first) are float32.
+struct ConvPtrs {
+  const void* x;
+  const float* weight;
+  const float* bias;        // nullable
+  const float* state_in;    // forward: inputs before t = 0 (nullable = zeros)
+  void* out;
+  float* state_out;         // forward: last K-1 inputs (nullable)
+  float* state_inout;       // decode: rolling state, updated in place
+};
+
+struct ConvShape {
+  int64_t batch;
+  int64_t seqlen;
+  int64_t dim;
+  int64_t runs;             // channel runs of one vector (set by the launcher)
+  int64_t tiles;            // time tiles of kConvTile steps (set by the launcher)
+  int32_t silu;
+  int32_t vec_io;           // rows of x / out may be moved in aligned 16-byte runs
+};
+
+// Time steps per thread of the conv forward (the halo of K-1 rows is read
+// once more per tile).
+constexpr int kConvTile = 128;
+
+hipError_t launch_conv1d_fwd(int dtype, int width, const ConvPtrs& p, const ConvShape& sh,
+                             hipStream_t stream);
+hipError_t launch_conv1d_update(int dtype, int width, const ConvPtrs& p, const ConvShape& sh,
+                                hipStream_t stream);
+
 }  // namespace ssm

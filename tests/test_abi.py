@@ -162,3 +162,27 @@ def test_ex_entry_points_validate_like_the_plain_ones():
     rc = lib.selective_state_update_ex(P[0], P[1], P[2], P[3], P[4], P[5], None, None, None,
                                        1, 1, P[6], ctypes.byref(_dims(L=2)), None)
     assert rc == SSM_EINVAL  # seqlen must be 1
+
+
+def _conv(dims, *, x=P[0], w=P[1], out=P[2], s_in=None, s_out=None, width=4):
+    lib = _lib.load()
+    return lib.causal_conv1d_fwd(x, w, None, s_in, width, 1, out, s_out, ctypes.byref(dims), None)
+
+
+def test_conv_validation():
+    assert _conv(_dims(), width=0) == SSM_EINVAL
+    assert _conv(_dims(), width=5) == SSM_EINVAL
+    assert _conv(_dims(), x=None) == SSM_EINVAL
+    assert _conv(_dims(), out=P[0]) == SSM_EINVAL                    # out aliases x
+    assert _conv(_dims(), s_in=P[3], s_out=P[3]) == SSM_EINVAL       # state in == out
+    assert _conv(_dims(dtype=9)) == SSM_EDTYPE
+    assert _conv(_dims(), x=ctypes.c_void_p(0x100002)) == SSM_EALIGN
+    lib = _lib.load()
+    d1 = _dims(L=2)
+    assert lib.causal_conv1d_update(P[0], P[1], P[2], None, 4, 1, P[3], ctypes.byref(d1),
+                                    None) == SSM_EINVAL               # seqlen must be 1
+    d1 = _dims(L=1)
+    assert lib.causal_conv1d_update(None, P[1], P[2], None, 4, 1, P[3], ctypes.byref(d1),
+                                    None) == SSM_EINVAL               # state required
+    assert lib.causal_conv1d_update(P[0], P[1], P[2], None, 4, 1, P[0], ctypes.byref(d1),
+                                    None) == SSM_EINVAL               # out aliases state
