@@ -31,3 +31,4 @@ from .scan import (  # noqa: F401
 )
 from .scan_bwd import scan_bwd  # noqa: F401
 from .conv1d import causal_conv1d, conv1d_update  # noqa: F401
+from .block import mamba_block_fwd  # noqa: F401
