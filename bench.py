@@ -99,6 +99,9 @@ def parse():
     p.add_argument("--conv", action="store_true",
                    help="instead of the step: time the causal conv1d + SiLU (width 4) on the "
                         "forward workload's activations; one JSON line with an HBM roofline")
+    p.add_argument("--block", action="store_true",
+                   help="instead of the step: time one Mamba block (projections, conv1d, scan) "
+                        "of the workload's model with random weights; one JSON line")
     p.add_argument("--l-sweep", action="store_true",
                    help="instead of the step: time the forward alone over L = 2^10 .. 2^20 "
                         "at B=1, D=256, N=16, float32 (one JSON line per L)")
@@ -343,6 +346,92 @@ def conv_bench(args, torch, dev):
     print(json.dumps(line), flush=True)
 
 
+def _time_ms(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        fn()
+        e[1].record()
+    torch.cuda.synchronize()
+    return [e[0].elapsed_time(e[1]) for e in ev]
+
+
+def block_bench(args, torch, dev):
+    """One Mamba block of the workload's model (B, L of the workload; d_model
+    = d_inner / 2) with seeded random weights.  The conv1d and the scan are
+    also timed alone on the same shapes, so the projections' share (rocBLAS
+    GEMMs on MFMA) is the block time minus theirs."""
+    from selective_state_space_38_amd import (causal_conv1d_fwd, mamba_block_fwd,
+                                              selective_scan_fwd)
+
+    w = synth.WORKLOADS[args.workload]
+    cfg = synth.BLOCKS[args.workload]
+    act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    print(f"bench: generating {w.name} block weights", file=sys.stderr, flush=True)
+    x_np, wt_np = synth.make_block(**cfg, batch=w.batch, seqlen=w.seqlen, dtype=w.dtype)
+    f32 = ("conv_w", "conv_b", "dt_bias", "A", "D")
+    wt = {k: torch.from_numpy(v).to(device=dev, dtype=torch.float32 if k in f32 else act)
+          for k, v in wt_np.items()}
+    x = torch.from_numpy(x_np).to(device=dev, dtype=act)
+    out = torch.empty_like(x)
+    M = w.batch * w.seqlen
+    dm, di, n, r = cfg["d_model"], cfg["d_inner"], cfg["d_state"], cfg["dt_rank"]
+    ms_block = _time_ms(torch, lambda: mamba_block_fwd(x, wt, out=out), args.steps, args.warmup)
+    # the block's own conv1d and scan, alone on the same shapes
+    xi = torch.randn(w.batch, w.seqlen, di, device=dev).to(act)
+    u = torch.empty_like(xi)
+    ms_conv = _time_ms(torch, lambda: causal_conv1d_fwd(xi, wt["conv_w"], wt["conv_b"], out=u),
+                       args.steps, args.warmup)
+    dt = torch.randn(w.batch, w.seqlen, di, device=dev).to(act)
+    Bm = torch.randn(w.batch, w.seqlen, n, device=dev).to(act)
+    Cm = torch.randn(w.batch, w.seqlen, n, device=dev).to(act)
+    y = torch.empty_like(xi)
+    ms_scan = _time_ms(torch, lambda: selective_scan_fwd(u, dt, wt["A"], Bm, Cm, D=wt["D"], z=xi,
+                                                         delta_bias=wt["dt_bias"], out=y),
+                       args.steps, args.warmup)
+    tb, tc, ts = (float(np.mean(v)) for v in (ms_block, ms_conv, ms_scan))
+    gemm_flops = 2 * M * (dm * 2 * di + di * (r + 2 * n) + r * di + di * dm)
+    t_gemm = max(tb - tc - ts, 1e-6)
+    gemm_tflops = gemm_flops / (t_gemm / 1e3) / 1e12
+    peak = 2500.0 if w.dtype == "bf16" else 157.3
+    line = {
+        "metric": "Mamba block forward tokens/s, 1 GPU",
+        "value": M / (tb / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": tb,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype if w.dtype == "f32" else "bf16 storage, f32 accumulation",
+        "data": "synthetic (seeded random weights and N(0,1) input)",
+        "config": {"workload": (f"{w.name} block (B={w.batch}, L={w.seqlen}, d_model={dm}, "
+                                f"d_inner={di}, d_state={n}, dt_rank={r}, conv width "
+                                f"{cfg['conv_width']}, {w.dtype})")},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / peak, "traffic": None,
+                     "kernel": "projection GEMMs (block time minus conv1d and scan alone)",
+                     "flops_per_launch": gemm_flops},
+        "breakdown_ms": {"block": tb, "scan_alone": ts, "conv1d_alone": tc,
+                         "projections_by_difference": t_gemm,
+                         "block_median": float(np.median(ms_block)),
+                         "block_min": float(np.min(ms_block))},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        Lp = 64
+        t0 = time.perf_counter()
+        oracle.mamba_block_fwd(x_np[:, :Lp], wt_np)
+        tcpu = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": w.batch * Lp / tcpu, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": (f"float64 NumPy oracle block on the first {Lp} tokens of every row "
+                       f"({tcpu:.1f} s; the matrix products may use every host core)"),
+        }
+    print(json.dumps(line), flush=True)
+
+
 def l_sweep(args, torch, dev):
     """Forward time against sequence length at the million-token shape's width:
     the work is linear in L, so tokens*channels/s should level off, not fall."""
@@ -415,6 +504,9 @@ def main():
         return
     if args.conv:
         conv_bench(args, torch, dev)
+        return
+    if args.block:
+        block_bench(args, torch, dev)
         return
     w = synth.WORKLOADS[args.workload]
     dw = synth.WORKLOADS["decode"]

@@ -217,6 +217,53 @@ int causal_conv1d_update(float* state, const void* x, const float* weight,
                          const float* bias, int width, int silu, void* out,
                          const ssm_dims* dims, void* stream);
 
+/*
+ * Weights of one Mamba block (reading guide glossary "Mamba Block": input
+ * projection, 1-D convolution, selective SSM, multiplicative gate; "Mamba /
+ * MambaMini" Q&A: d_inner = expand * d_model, the Conv before the SSM, B and
+ * C from a linear layer, Delta from a low-rank pair of linear layers).
+ * Matrices are row-major [rows][cols]; "dtype" is the block's dims->dtype.
+ */
+typedef struct {
+  const void* in_x;      /* [d_model][d_inner] dtype: x = x_in in_x            */
+  const void* in_z;      /* [d_model][d_inner] dtype: z = x_in in_z (gate)     */
+  const float* conv_w;   /* [d_inner][conv_width] float32                      */
+  const float* conv_b;   /* [d_inner] float32 (nullable)                       */
+  const void* x_dt;      /* [d_inner][dt_rank] dtype: dt_low = u x_dt          */
+  const void* x_B;       /* [d_inner][d_state] dtype: B = u x_B                */
+  const void* x_C;       /* [d_inner][d_state] dtype: C = u x_C                */
+  const void* dt;        /* [dt_rank][d_inner] dtype: dt = dt_low dt           */
+  const float* dt_bias;  /* [d_inner] float32 (nullable)                       */
+  const float* A;        /* [d_inner][d_state] float32                         */
+  const float* D;        /* [d_inner] float32 (nullable)                       */
+  const void* out;       /* [d_inner][d_model] dtype: out = y out              */
+} mamba_block_weights;
+
+typedef struct {
+  int64_t batch, seqlen, d_model, d_inner, d_state, dt_rank;
+  int32_t conv_width;    /* 1..4 */
+  int32_t dtype;         /* ssm_dtype of x_in, out, the projection weights and
+                            every intermediate activation */
+} mamba_block_dims;
+
+/*
+ * Forward of one Mamba block:
+ *   x, z  = x_in in_x, x_in in_z                      (rocBLAS GEMMs)
+ *   u     = SiLU(causal_conv1d(x) + conv_b)            (causal_conv1d_fwd)
+ *   dt_low, B, C = u x_dt, u x_B, u x_C;  dt = dt_low dt   (GEMMs)
+ *   y     = selective scan of u with Delta = softplus(dt + dt_bias), gated
+ *           by SiLU(z)                                 (selective_scan_fwd)
+ *   out   = y out                                      (GEMM)
+ *   x_in, out : [batch][seqlen][d_model] of dtype; out must not alias x_in.
+ * GEMMs accumulate in float32; intermediates are stored in dtype.  Scratch
+ * for the intermediates (about (4 d_inner + dt_rank + 2 d_state) * batch *
+ * seqlen elements of dtype) is allocated stream-ordered and freed on the
+ * stream.  Normalisation and the residual connection are the caller's.
+ * Returns an ssm_status (SSM_ELAUNCH if rocBLAS fails).
+ */
+int mamba_block_fwd(const void* x_in, const mamba_block_weights* weights, void* out,
+                    const mamba_block_dims* dims, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* ssm_status_string(int status);
 

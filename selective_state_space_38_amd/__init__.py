@@ -7,6 +7,7 @@ from .api import (  # noqa: F401
     selective_state_update,
     causal_conv1d_fwd,
     causal_conv1d_update,
+    mamba_block_fwd,
     check_device_errors,
     fwd_plan,
 )

@@ -25,6 +25,7 @@ EXPORTED = (
     "selective_state_update_ex",
     "causal_conv1d_fwd",
     "causal_conv1d_update",
+    "mamba_block_fwd",
     "ssm_status_string",
     "ssm_check_device_errors",
     "ssm_fwd_plan_for",
@@ -51,6 +52,25 @@ class SsmFwdPlan(ctypes.Structure):
         ("chunk", ctypes.c_int32),
         ("workgroups", ctypes.c_int64),
         ("whole_chains", ctypes.c_int32),
+    ]
+
+
+class MambaBlockWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("in_x", "in_z", "conv_w", "conv_b", "x_dt", "x_B", "x_C", "dt", "dt_bias",
+                 "A", "D", "out")]
+
+
+class MambaBlockDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("d_model", ctypes.c_int64),
+        ("d_inner", ctypes.c_int64),
+        ("d_state", ctypes.c_int64),
+        ("dt_rank", ctypes.c_int64),
+        ("conv_width", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
     ]
 
 
@@ -93,6 +113,9 @@ def load():
     lib.causal_conv1d_update.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, dims_p,
                                          vp]
     lib.causal_conv1d_update.restype = ctypes.c_int
+    lib.mamba_block_fwd.argtypes = [vp, ctypes.POINTER(MambaBlockWeights), vp,
+                                    ctypes.POINTER(MambaBlockDims), vp]
+    lib.mamba_block_fwd.restype = ctypes.c_int
     lib.ssm_status_string.argtypes = [ctypes.c_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_check_device_errors.argtypes = [vp]

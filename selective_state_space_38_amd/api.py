@@ -273,6 +273,51 @@ def causal_conv1d_update(state, x, weight, bias=None, activation="silu", out=Non
     return out
 
 
+BLOCK_WEIGHTS = ("in_x", "in_z", "conv_w", "conv_b", "x_dt", "x_B", "x_C", "dt", "dt_bias",
+                 "A", "D", "out")
+
+
+def mamba_block_fwd(x_in, weights, out=None):
+    """Forward of one Mamba block on the GPU (projections on rocBLAS, conv1d
+    + SiLU and the gated selective scan in this library's kernels).
+
+    x_in: [batch, L, d_model] (float32 or bfloat16).  ``weights``: dict with
+    in_x, in_z [d_model, d_inner], x_dt [d_inner, r], x_B, x_C
+    [d_inner, N], dt [r, d_inner], out [d_inner, d_model] in x_in's dtype,
+    and conv_w [d_inner, K], A [d_inner, N], optional conv_b, dt_bias, D
+    [d_inner] in float32.  Returns out [batch, L, d_model].
+    """
+    if x_in.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x_in.dtype}")
+    bsz, L, dm = x_in.shape
+    dev = x_in.device
+    act = x_in.dtype
+    di = weights["in_x"].shape[1]
+    n = weights["A"].shape[1]
+    r = weights["x_dt"].shape[1]
+    k = weights["conv_w"].shape[1]
+    shapes = dict(in_x=((dm, di), act), in_z=((dm, di), act), conv_w=((di, k), torch.float32),
+                  conv_b=((di,), torch.float32), x_dt=((di, r), act), x_B=((di, n), act),
+                  x_C=((di, n), act), dt=((r, di), act), dt_bias=((di,), torch.float32),
+                  A=((di, n), torch.float32), D=((di,), torch.float32), out=((di, dm), act))
+    _check(x_in, "x_in", act, (bsz, L, dm), dev)
+    for name, (shp, dt_) in shapes.items():
+        if weights.get(name) is None and name not in ("conv_b", "dt_bias", "D"):
+            raise ValueError(f"weight {name} is required")
+        _check(weights.get(name), name, dt_, shp, dev)
+    if out is None:
+        out = torch.empty_like(x_in)
+    _check(out, "out", act, (bsz, L, dm), dev)
+    wts = _lib.MambaBlockWeights(*[None if weights.get(nm) is None else weights[nm].data_ptr()
+                                   for nm in BLOCK_WEIGHTS])
+    dims = _lib.MambaBlockDims(bsz, L, dm, di, n, r, k, _DTYPES[act])
+    with torch.cuda.device(dev):
+        rc = _lib.load().mamba_block_fwd(_ptr(x_in), ctypes.byref(wts), _ptr(out),
+                                         ctypes.byref(dims), _stream(dev))
+    _raise(rc)
+    return out
+
+
 def check_device_errors(device=None):
     """Synchronises the current stream and raises if a carry wait timed out."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device

@@ -20,6 +20,7 @@ SOURCES = [
     ("scan_bwd.hip", "scan_bwd", []),
     ("state_update.hip", "state_update", []),
     ("conv1d.hip", "conv1d", []),
+    ("gemm.hip", "gemm", []),
 ]
 
 HIPCC_FLAGS = [
@@ -33,6 +34,10 @@ HIPCC_FLAGS = [
     "-Wall",
     "-Wno-unused-result",
 ]
+
+
+# rocBLAS runs the Mamba block's projection GEMMs
+LINK_LIBS = ["-L/opt/rocm/lib", "-lrocblas"]
 
 
 def hipcc():
@@ -72,8 +77,8 @@ def build(verbose=False):
     for proc in procs:
         _check(proc, verbose)
     tmp = LIB + ".tmp"
-    _check(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
-                verbose), verbose)
+    _check(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs +
+                ["-o", tmp] + LINK_LIBS, verbose), verbose)
     os.replace(tmp, LIB)
     return LIB
 

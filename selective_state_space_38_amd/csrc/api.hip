@@ -405,6 +405,80 @@ int conv_update_impl(float* state, const void* x, const float* weight, const flo
   return SSM_OK;
 }
 
+int block_impl(const void* x_in, const mamba_block_weights* w, void* out,
+               const mamba_block_dims* bd, void* stream) {
+  if (!bd || !w || !x_in || !out) return SSM_EINVAL;
+  if (bd->dtype != SSM_F32 && bd->dtype != SSM_BF16) return SSM_EDTYPE;
+  if (bd->batch <= 0 || bd->seqlen <= 0 || bd->d_model <= 0 || bd->d_inner <= 0 ||
+      bd->dt_rank <= 0 || !valid_dstate(bd->d_state) || bd->conv_width < 1 ||
+      bd->conv_width > 4)
+    return SSM_EINVAL;
+  if (!w->in_x || !w->in_z || !w->conv_w || !w->x_dt || !w->x_B || !w->x_C || !w->dt ||
+      !w->A || !w->out)
+    return SSM_EINVAL;
+  const void* ptrs[] = {x_in, out, w->in_x, w->in_z, w->conv_w, w->conv_b, w->x_dt, w->x_B,
+                        w->x_C, w->dt, w->dt_bias, w->A, w->D, w->out};
+  for (const void* q : ptrs)
+    if (q && !aligned(q, 4)) return SSM_EALIGN;
+  if (out == x_in) return SSM_EINVAL;
+  const int64_t M = bd->batch * bd->seqlen;
+  const int64_t di = bd->d_inner, dm = bd->d_model, n = bd->d_state, r = bd->dt_rank;
+  // rocBLAS takes 32-bit sizes
+  const int64_t lim = (1LL << 31) - 1;
+  if (M > lim || di > lim || dm > lim || M * di > (1LL << 46)) return SSM_EINVAL;
+
+  const int64_t esz = bd->dtype == SSM_BF16 ? 2 : 4;
+  auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
+  const int64_t b_act = up256(M * di * esz);
+  const int64_t b_low = up256(M * r * esz);
+  const int64_t b_bc = up256(M * n * esz);
+  const int64_t total = 5 * b_act + b_low + 2 * b_bc;  // x, z, u, dt, y; dt_low; B, C
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (env_int("SSM_TEST_FAIL_ALLOC", 0) == 1) return SSM_ENOMEM;
+  char* ws = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(total), st) !=
+          hipSuccess ||
+      !ws)
+    return SSM_ENOMEM;
+  char* x = ws;
+  char* z = x + b_act;
+  char* u = z + b_act;
+  char* dt = u + b_act;
+  char* y = dt + b_act;
+  char* low = y + b_act;
+  char* Bm = low + b_low;
+  char* Cm = Bm + b_bc;
+  const int dtype = bd->dtype;
+
+  int rc = SSM_OK;
+  auto gemm = [&](int64_t rows, int64_t cols, int64_t inner, const void* a, const void* wt,
+                  void* c) {
+    if (rc == SSM_OK &&
+        ssm::gemm_rowmajor(dtype, rows, cols, inner, a, inner, wt, cols, c, cols, st) !=
+            hipSuccess)
+      rc = SSM_ELAUNCH;
+  };
+  gemm(M, di, dm, x_in, w->in_x, x);
+  gemm(M, di, dm, x_in, w->in_z, z);
+  if (rc == SSM_OK) {
+    ssm_dims cd{bd->batch, bd->seqlen, di, 1, dtype};
+    rc = conv_fwd_impl(x, w->conv_w, w->conv_b, nullptr, bd->conv_width, 1, u, nullptr, &cd,
+                       stream);
+  }
+  gemm(M, r, di, u, w->x_dt, low);
+  gemm(M, n, di, u, w->x_B, Bm);
+  gemm(M, n, di, u, w->x_C, Cm);
+  gemm(M, di, r, low, w->dt, dt);
+  if (rc == SSM_OK) {
+    ssm_dims sd{bd->batch, bd->seqlen, di, n, dtype};
+    rc = fwd_impl(u, dt, w->A, Bm, Cm, w->D, z, w->dt_bias, 1, nullptr, SSM_BBAR_DELTA, y,
+                  nullptr, &sd, stream);
+  }
+  gemm(M, dm, di, y, w->out, out);
+  if (hipFreeAsync(ws, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,6 +542,11 @@ int causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
 int causal_conv1d_update(float* state, const void* x, const float* weight, const float* bias,
                          int width, int silu, void* out, const ssm_dims* dims, void* stream) {
   return conv_update_impl(state, x, weight, bias, width, silu, out, dims, stream);
+}
+
+int mamba_block_fwd(const void* x_in, const mamba_block_weights* weights, void* out,
+                    const mamba_block_dims* dims, void* stream) {
+  return block_impl(x_in, weights, out, dims, stream);
 }
 
 const char* ssm_status_string(int status) {

@@ -140,3 +140,46 @@ def algorithmic_bytes(w, *, batch=None, seqlen=None, dim=None, dstate=None):
     if w.decode:
         return 8 * b * d * n + 4 * e * b * d + 2 * e * b * n + params
     return 4 * e * b * L * d + 2 * e * b * L * n + params + 4 * b * d * n
+
+
+# Block shapes of the two Mamba models the pages name (d_inner = 2 d_model,
+# d_state 16); dt_rank = ceil(d_model / 16) and conv width 4 are readings
+# (the pages give neither value).
+BLOCKS = {
+    "mamba130m": dict(d_model=768, d_inner=1536, d_state=16, dt_rank=48, conv_width=4),
+    "mamba2p8b": dict(d_model=2560, d_inner=5120, d_state=16, dt_rank=160, conv_width=4),
+}
+
+
+def make_block(d_model, d_inner, d_state, dt_rank, conv_width, *, batch, seqlen,
+               dtype="f32", seed=38100):
+    """Seeded random weights and input of one Mamba block.  Projection
+    weights are N(0, 1/fan_in); conv weights N(0, 1/K); conv bias N(0, 0.1^2);
+    dt_bias = log(expm1(dt0)) with dt0 log-uniform on [1e-3, 1e-1]; A is
+    S4D-real -(n+1); D = 1; the input is N(0, 1).  Matrices and the input are
+    rounded to bfloat16 (ties to even) when dtype is "bf16"; conv weights,
+    biases, A and D stay float32.  Returns (x_in, weights)."""
+    g = [np.random.Generator(np.random.PCG64(c)) for c in np.random.SeedSequence(seed).spawn(12)]
+
+    def mat(rng, rows, cols):
+        return (rng.standard_normal((rows, cols)) / np.sqrt(rows)).astype(np.float32)
+
+    w = dict(
+        in_x=mat(g[0], d_model, d_inner), in_z=mat(g[1], d_model, d_inner),
+        conv_w=(g[2].standard_normal((d_inner, conv_width)) / np.sqrt(conv_width)).astype(
+            np.float32),
+        conv_b=(g[3].standard_normal(d_inner) * 0.1).astype(np.float32),
+        x_dt=mat(g[4], d_inner, dt_rank), x_B=mat(g[5], d_inner, d_state),
+        x_C=mat(g[6], d_inner, d_state), dt=mat(g[7], dt_rank, d_inner),
+        dt_bias=np.log(np.expm1(np.exp(g[8].uniform(np.log(1e-3), np.log(1e-1),
+                                                     d_inner)))).astype(np.float32),
+        A=-np.broadcast_to(np.arange(1, d_state + 1, dtype=np.float32),
+                           (d_inner, d_state)).copy(),
+        D=np.ones(d_inner, dtype=np.float32),
+        out=mat(g[9], d_inner, d_model))
+    x_in = g[10].standard_normal((batch, seqlen, d_model)).astype(np.float32)
+    if dtype == "bf16":
+        for k in ("in_x", "in_z", "x_dt", "x_B", "x_C", "dt", "out"):
+            w[k] = round_bf16(w[k])
+        x_in = round_bf16(x_in)
+    return x_in, w
