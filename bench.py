@@ -96,6 +96,9 @@ def parse():
     p.add_argument("--bwd", action="store_true",
                    help="instead of the step: time the backward (selective_scan_bwd) on the "
                         "forward workload; one JSON line with its own roofline and CPU baseline")
+    p.add_argument("--train", action="store_true",
+                   help="with --bwd: the training pair (forward keeping checkpoints, then the "
+                        "backward reading them)")
     p.add_argument("--conv", action="store_true",
                    help="instead of the step: time the causal conv1d + SiLU (width 4) on the "
                         "forward workload's activations; one JSON line with an HBM roofline")
@@ -188,7 +191,8 @@ def dec_dim(dec):
 def bwd_bench(args, torch, dev):
     """Times selective_scan_bwd on the workload's forward inputs with a
     seeded N(0,1) output gradient."""
-    from selective_state_space_38_amd import check_device_errors, selective_scan_bwd
+    from selective_state_space_38_amd import (check_device_errors, ckpt_buffer,
+                                              selective_scan_bwd, selective_scan_fwd)
 
     w = synth.WORKLOADS[args.workload]
     act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -205,8 +209,19 @@ def bwd_bench(args, torch, dev):
     Bm, Cm = up(x["B"], act), up(x["C"], act)
     A, Dv, bias = up(x["A"]), up(x["D"]), up(x["dt_bias"])
 
+    ck = ckpt_buffer(u, w.dstate) if args.train else None
+    fout = torch.empty_like(u)
+
+    def fwd_train():
+        selective_scan_fwd(u, dt, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, out=fout, ckpt=ck)
+
+    if args.train:
+        fwd_train()
+        torch.cuda.synchronize()
+        fwd_ms = _time_ms(torch, fwd_train, args.steps, args.warmup)
+
     def bwd():
-        return selective_scan_bwd(u, dt, A, Bm, Cm, dout, D=Dv, z=z, delta_bias=bias)
+        return selective_scan_bwd(u, dt, A, Bm, Cm, dout, D=Dv, z=z, delta_bias=bias, ckpt=ck)
 
     for _ in range(args.warmup):
         bwd()
@@ -235,7 +250,9 @@ def bwd_bench(args, torch, dev):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded N(0,1) activations and output gradient)",
         "config": {"workload": (f"{w.name} backward (B={w.batch}, L={w.seqlen}, D={w.dim}, "
-                                f"N={w.dstate}, {w.dtype} activations)")},
+                                f"N={w.dstate}, {w.dtype} activations)"
+                                + (", from the training-mode forward's checkpoints"
+                                   if args.train else ", recomputing its own checkpoints"))},
         "roofline": {
             "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS, "unit": "TFLOP/s",
             "frac": achieved / VALU_PEAK_TOPS, "traffic": None,
@@ -247,6 +264,7 @@ def bwd_bench(args, torch, dev):
         },
         "hbm": {"algorithmic_bytes": nbytes, "GBps": nbytes / (avg / 1e3) / 1e9,
                 "frac_of_8TBps": nbytes / (avg / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "training_forward_ms": float(np.mean(fwd_ms)) if args.train else None,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

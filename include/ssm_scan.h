@@ -264,6 +264,37 @@ typedef struct {
 int mamba_block_fwd(const void* x_in, const mamba_block_weights* weights, void* out,
                     const mamba_block_dims* dims, void* stream);
 
+/*
+ * Training pair: a forward that also keeps the states the backward needs,
+ * and a backward that uses them instead of recomputing its own forward pass.
+ *   ckpt : float32 device buffer of ssm_ckpt_bytes(dims) bytes holding the
+ *          state before every 8th step of every (batch row, block of 64
+ *          channels) -- one state per 8 steps, the backward's recompute
+ *          granularity; its layout is internal to the library.
+ * selective_scan_fwd_train is selective_scan_fwd_h0 (Delta*B input) that
+ * also writes ckpt (which must not alias another argument); its out and
+ * last_state are identical to selective_scan_fwd_h0's.
+ * selective_scan_bwd_ckpt is selective_scan_bwd with ckpt read from a
+ * selective_scan_fwd_train call on the same inputs; ckpt NULL -> SSM_EINVAL.
+ */
+int selective_scan_fwd_train(const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D,
+                             const void* z, const float* dt_bias, int softplus,
+                             const float* h0, void* out, float* last_state,
+                             float* ckpt, const ssm_dims* dims, void* stream);
+
+int selective_scan_bwd_ckpt(const void* u, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D,
+                            const void* z, const float* dt_bias, int softplus,
+                            const float* h0, const void* dout,
+                            const float* dlast, const float* ckpt, void* du,
+                            void* ddelta, float* dA, void* dB, void* dC,
+                            float* dD, void* dz, float* ddt_bias, float* dh0,
+                            const ssm_dims* dims, void* stream);
+
+/* Bytes of the ckpt buffer for dims (a negative ssm_status if dims are invalid). */
+int64_t ssm_ckpt_bytes(const ssm_dims* dims);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* ssm_status_string(int status);
 

@@ -4,6 +4,7 @@ with hand-written HIP kernels, and a thin PyTorch binding."""
 from .api import (  # noqa: F401
     selective_scan_fwd,
     selective_scan_bwd,
+    ckpt_buffer,
     selective_state_update,
     causal_conv1d_fwd,
     causal_conv1d_update,

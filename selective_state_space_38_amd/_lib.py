@@ -21,6 +21,9 @@ EXPORTED = (
     "selective_scan_fwd_h0",
     "selective_scan_fwd_ex",
     "selective_scan_bwd",
+    "selective_scan_fwd_train",
+    "selective_scan_bwd_ckpt",
+    "ssm_ckpt_bytes",
     "selective_state_update",
     "selective_state_update_ex",
     "causal_conv1d_fwd",
@@ -101,6 +104,15 @@ def load():
     lib.selective_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp]
     lib.selective_scan_bwd.restype = ctypes.c_int
+    lib.selective_scan_fwd_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                             vp, vp, vp, dims_p, vp]
+    lib.selective_scan_fwd_train.restype = ctypes.c_int
+    lib.selective_scan_bwd_ckpt.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                            vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            dims_p, vp]
+    lib.selective_scan_bwd_ckpt.restype = ctypes.c_int
+    lib.ssm_ckpt_bytes.argtypes = [dims_p]
+    lib.ssm_ckpt_bytes.restype = ctypes.c_int64
     lib.selective_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                            vp, dims_p, vp]
     lib.selective_state_update.restype = ctypes.c_int

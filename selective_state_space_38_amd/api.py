@@ -60,9 +60,19 @@ def _bbar_code(bbar):
     return codes[bbar]
 
 
+def ckpt_buffer(u, dstate):
+    """A float32 device buffer for the training pair's checkpoints (the state
+    before every 8th step of every block of 64 channels) of activations u."""
+    bsz, L, dim = u.shape
+    dims = _lib.SsmDims(bsz, L, dim, dstate, _DTYPES[u.dtype])
+    nbytes = _lib.load().ssm_ckpt_bytes(ctypes.byref(dims))
+    _raise(nbytes if nbytes < 0 else 0)
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=u.device)
+
+
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                        delta_softplus=True, return_last_state=False, h0=None,
-                       out=None, last_state=None, bbar="delta"):
+                       out=None, last_state=None, bbar="delta", ckpt=None):
     """Selective-scan forward on the GPU.
 
     u, delta, z: [batch, L, dim]; B, C: [batch, L, dstate] (float32 or
@@ -70,9 +80,12 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     h0: [batch, dim, dstate] float32.  Returns out (same dtype as u) and, with
     return_last_state, the float32 final state [batch, dim, dstate].
     bbar: "delta" (Bbar = Delta*B) or "zoh" (exact zero-order hold,
-    (exp(Delta A) - 1)/A * B).
+    (exp(Delta A) - 1)/A * B).  ckpt: a buffer from ckpt_buffer() to keep the
+    backward's checkpoints (training mode; Delta*B only).
     """
     code = _bbar_code(bbar)
+    if ckpt is not None and code != _lib.SSM_BBAR_DELTA:
+        raise ValueError("checkpoints are kept for the Delta*B input only")
     if u.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {u.dtype}")
     bsz, L, dim = u.shape
@@ -96,8 +109,18 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     _check(last_state, "last_state", torch.float32, (bsz, dim, dstate), dev)
     dims = _lib.SsmDims(bsz, L, dim, dstate, _DTYPES[act])
     lib = _lib.load()
+    if ckpt is not None:
+        if ckpt.dtype != torch.float32 or ckpt.device != dev or not ckpt.is_contiguous():
+            raise ValueError("ckpt must be a contiguous float32 tensor on the same device")
+        if ckpt.numel() * 4 < lib.ssm_ckpt_bytes(ctypes.byref(dims)):
+            raise ValueError("ckpt is too small (use ckpt_buffer)")
     with torch.cuda.device(dev):
-        if code == _lib.SSM_BBAR_DELTA:
+        if ckpt is not None:
+            rc = lib.selective_scan_fwd_train(
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(out),
+                _ptr(last_state), _ptr(ckpt), ctypes.byref(dims), _stream(dev))
+        elif code == _lib.SSM_BBAR_DELTA:
             rc = lib.selective_scan_fwd_h0(
                 _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                 _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(out),
@@ -112,7 +135,7 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
 
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
-                       delta_softplus=True, h0=None, dlast=None):
+                       delta_softplus=True, h0=None, dlast=None, ckpt=None):
     """Backward of selective_scan_fwd (Delta*B input) on the GPU.
 
     Inputs as in the forward, plus dout [batch, L, dim] (activation dtype),
@@ -120,7 +143,9 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
     (optional), the gradient of the final state.  Returns a dict of gradients:
     du, ddelta (of the raw dt), dz (if z is given) in the activation dtype;
     dB, dC [batch, L, dstate] in the activation dtype; dA [dim, dstate] and,
-    for given D / delta_bias / h0, dD, ddt_bias, dh0 in float32.
+    for given D / delta_bias / h0, dD, ddt_bias, dh0 in float32.  ckpt: the
+    buffer a training-mode selective_scan_fwd filled on the same inputs (the
+    backward then skips its own forward pass).
     """
     if u.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {u.dtype}")
@@ -152,13 +177,21 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         g["dh0"] = torch.empty((bsz, dim, dstate), dtype=torch.float32, device=dev)
     dims = _lib.SsmDims(bsz, L, dim, dstate, _DTYPES[act])
     lib = _lib.load()
+    if ckpt is not None:
+        if ckpt.dtype != torch.float32 or ckpt.device != dev or not ckpt.is_contiguous():
+            raise ValueError("ckpt must be a contiguous float32 tensor on the same device")
+        if ckpt.numel() * 4 < lib.ssm_ckpt_bytes(ctypes.byref(dims)):
+            raise ValueError("ckpt is too small (use ckpt_buffer)")
     with torch.cuda.device(dev):
-        rc = lib.selective_scan_bwd(
-            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-            1 if delta_softplus else 0, _ptr(h0), _ptr(dout), _ptr(dlast),
-            _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
-            _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddt_bias")), _ptr(g.get("dh0")),
-            ctypes.byref(dims), _stream(dev))
+        head = [_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(dout), _ptr(dlast)]
+        tail = [_ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddt_bias")),
+                _ptr(g.get("dh0")), ctypes.byref(dims), _stream(dev)]
+        if ckpt is not None:
+            rc = lib.selective_scan_bwd_ckpt(*head, _ptr(ckpt), *tail)
+        else:
+            rc = lib.selective_scan_bwd(*head, *tail)
     _raise(rc)
     return g
 

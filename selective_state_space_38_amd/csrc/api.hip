@@ -131,7 +131,8 @@ int check_dims(const ssm_dims* dims) {
 
 int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
              const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
-             int bbar, void* out, float* last_state, const ssm_dims* dims, void* stream) {
+             int bbar, void* out, float* last_state, float* ckpt, const ssm_dims* dims,
+             void* stream) {
   int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
   if (bbar != SSM_BBAR_DELTA && bbar != SSM_BBAR_ZOH) return SSM_EINVAL;
@@ -178,6 +179,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sc.agg_b = reinterpret_cast<float*>(scratch + off_inc + inc_bytes);
   sc.agg_s = reinterpret_cast<float*>(scratch + off_inc + inc_bytes + aggb_bytes);
   sc.spin_limit = env_int("SSM_TEST_SPIN_LIMIT", kDefaultSpinLimit);
+  sc.ckpt = ckpt;
 
   ssm::FwdShape sh;
   sh.seqlen = dims->seqlen;
@@ -195,6 +197,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.has_h0 = h0 != nullptr;
   sh.has_last = last_state != nullptr;
   sh.zoh = bbar == SSM_BBAR_ZOH ? 1 : 0;
+  sh.n_ckpt = div_up(dims->seqlen, ssm::kBwdChunk);
   {
     // per-thread runs of the chunk tile: kChunk / groups consecutive channels
     const int64_t ept = plan.chunk / plan.state_groups;
@@ -264,15 +267,15 @@ int bwd_groups(int64_t n) {
 
 int bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
              const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
-             const void* dout, const float* dlast, void* du, void* ddelta, float* dA, void* dB,
-             void* dC, float* dD, void* dz, float* ddt_bias, float* dh0, const ssm_dims* dims,
-             void* stream) {
+             const void* dout, const float* dlast, const float* ckpt_in, void* du, void* ddelta,
+             float* dA, void* dB, void* dC, float* dD, void* dz, float* ddt_bias, float* dh0,
+             const ssm_dims* dims, void* stream) {
   int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
     return SSM_EINVAL;
   if (dz && !z) return SSM_EINVAL;  // no gate, no gate gradient
-  const void* ins[] = {u, delta, A, B, C, D, z, dt_bias, h0, dout, dlast};
+  const void* ins[] = {u, delta, A, B, C, D, z, dt_bias, h0, dout, dlast, ckpt_in};
   const void* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddt_bias, dh0};
   for (const void* q : ins)
     if (q && !aligned(q, 4)) return SSM_EALIGN;
@@ -291,7 +294,7 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const int64_t cblk = div_up(dims->dim, 64);
   const int64_t nck = div_up(dims->seqlen, ssm::kBwdChunk);
   auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
-  const int64_t b_ckpt = up256(dims->batch * cblk * nck * N * 64 * 4);
+  const int64_t b_ckpt = ckpt_in ? 0 : up256(dims->batch * cblk * nck * N * 64 * 4);
   const int64_t b_bc = up256(cblk * dims->batch * dims->seqlen * 2 * N * 4);
   const int64_t b_a = up256(dims->batch * dims->dim * N * 4);
   const int64_t b_d = up256(dims->batch * dims->dim * 4);
@@ -306,9 +309,10 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
       !scratch)
     return SSM_ENOMEM;
 
-  ssm::BwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, dout, dlast, du, ddelta, dA, dB, dC,
-                 dD, dz, ddt_bias, dh0, nullptr, nullptr, nullptr, nullptr, nullptr};
-  p.ckpt = reinterpret_cast<float*>(scratch);
+  ssm::BwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, dout, dlast, ckpt_in, du, ddelta, dA,
+                 dB, dC, dD, dz, ddt_bias, dh0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  // with the forward's checkpoints the backward skips its own forward pass
+  p.ckpt = ckpt_in ? const_cast<float*>(ckpt_in) : reinterpret_cast<float*>(scratch);
   p.part_bc = reinterpret_cast<float*>(scratch + b_ckpt);
   p.part_a = reinterpret_cast<float*>(scratch + b_ckpt + b_bc);
   p.part_d = reinterpret_cast<float*>(scratch + b_ckpt + b_bc + b_a);
@@ -472,7 +476,7 @@ int block_impl(const void* x_in, const mamba_block_weights* w, void* out,
   if (rc == SSM_OK) {
     ssm_dims sd{bd->batch, bd->seqlen, di, n, dtype};
     rc = fwd_impl(u, dt, w->A, Bm, Cm, w->D, z, w->dt_bias, 1, nullptr, SSM_BBAR_DELTA, y,
-                  nullptr, &sd, stream);
+                  nullptr, nullptr, &sd, stream);
   }
   gemm(M, dm, di, y, w->out, out);
   if (hipFreeAsync(ws, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
@@ -488,7 +492,7 @@ int selective_scan_fwd(const void* u, const void* delta, const float* A, const v
                        int softplus, void* out, float* last_state, const ssm_dims* dims,
                        void* stream) {
   return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, nullptr, SSM_BBAR_DELTA, out,
-                  last_state, dims, stream);
+                  last_state, nullptr, dims, stream);
 }
 
 int selective_scan_fwd_h0(const void* u, const void* delta, const float* A, const void* B,
@@ -496,15 +500,36 @@ int selective_scan_fwd_h0(const void* u, const void* delta, const float* A, cons
                           int softplus, const float* h0, void* out, float* last_state,
                           const ssm_dims* dims, void* stream) {
   return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, SSM_BBAR_DELTA, out,
-                  last_state, dims, stream);
+                  last_state, nullptr, dims, stream);
 }
 
 int selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
                           const void* C, const float* D, const void* z, const float* dt_bias,
                           int softplus, const float* h0, int bbar, void* out,
                           float* last_state, const ssm_dims* dims, void* stream) {
-  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, bbar, out, last_state, dims,
-                  stream);
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, bbar, out, last_state,
+                  nullptr, dims, stream);
+}
+
+int selective_scan_fwd_train(const void* u, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z,
+                             const float* dt_bias, int softplus, const float* h0, void* out,
+                             float* last_state, float* ckpt, const ssm_dims* dims,
+                             void* stream) {
+  if (!ckpt) return SSM_EINVAL;
+  if (!aligned(ckpt, 4)) return SSM_EALIGN;
+  const void* others[] = {u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
+  for (const void* q : others)
+    if (q && q == ckpt) return SSM_EINVAL;
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, SSM_BBAR_DELTA, out,
+                  last_state, ckpt, dims, stream);
+}
+
+int64_t ssm_ckpt_bytes(const ssm_dims* dims) {
+  const int rc = check_dims(dims);
+  if (rc != SSM_OK) return rc;
+  return dims->batch * div_up(dims->dim, 64) * div_up(dims->seqlen, ssm::kBwdChunk) *
+         dims->dstate * 64 * 4;
 }
 
 int selective_state_update(float* state, const void* x, const void* dt, const float* A,
@@ -529,8 +554,19 @@ int selective_scan_bwd(const void* u, const void* delta, const float* A, const v
                        void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD,
                        void* dz, float* ddt_bias, float* dh0, const ssm_dims* dims,
                        void* stream) {
-  return bwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, dout, dlast, du, ddelta, dA,
-                  dB, dC, dD, dz, ddt_bias, dh0, dims, stream);
+  return bwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, dout, dlast, nullptr, du,
+                  ddelta, dA, dB, dC, dD, dz, ddt_bias, dh0, dims, stream);
+}
+
+int selective_scan_bwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z, const float* dt_bias,
+                            int softplus, const float* h0, const void* dout, const float* dlast,
+                            const float* ckpt, void* du, void* ddelta, float* dA, void* dB,
+                            void* dC, float* dD, void* dz, float* ddt_bias, float* dh0,
+                            const ssm_dims* dims, void* stream) {
+  if (!ckpt) return SSM_EINVAL;
+  return bwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, dout, dlast, ckpt, du, ddelta,
+                  dA, dB, dC, dD, dz, ddt_bias, dh0, dims, stream);
 }
 
 int causal_conv1d_fwd(const void* x, const float* weight, const float* bias,

@@ -149,7 +149,8 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
   const int elem_last_f = run_last_f > 0 ? run_last_f : 0;
 
   // ---- phase F: checkpoints, with loads one chunk of TCF steps ahead -------
-  {
+  // (skipped when the forward's training mode has written them)
+  if (!p.ckpt_in) {
     float rbias_f[EPTF];
 #pragma unroll
     for (int k = 0; k < EPTF; ++k)

@@ -125,6 +125,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   // wave-uniform values go through readfirstlane so the compiler keeps them
   // (and addresses built from them) in SGPRs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gidx = w * G;  // first state of this wave's group
 
   // Workgroups 0 .. n_full-1 run whole chains (chain = workgroup index; they
   // never wait).  The others are segments of the split chains and take their
@@ -365,6 +366,16 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   };
 
   // ---- output pass: from carry-in h, produce out and the final state -----
+  // training mode: the state before every kBwdChunk-th step of the output
+  // pass goes to the backward's checkpoint array
+  const bool ckpt_on = sc.ckpt != nullptr;
+  float* const ckpt_c = ckpt_on ? sc.ckpt + static_cast<int64_t>(chain) * sh.n_ckpt * N * 64 : nullptr;
+  auto save_ckpt = [&](int64_t t, const float (&hh)[G]) {
+    const int64_t c = t / kBwdChunk;
+#pragma unroll
+    for (int g = 0; g < G; ++g) ckpt_c[(c * N + gidx + g) * 64 + lane] = hh[g];
+  };
+
   auto output_pass = [&](float (&h)[G]) {
     Prefetch pf;
     float sk[EPT], zf[EPT], sk_next[EPT], zf_next[EPT];
@@ -385,6 +396,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       // phase S: the recurrence over the chunk, one step per time index; a
       // ragged last chunk runs the plain loop below
       auto step = [&](int lt) {
+        if (ckpt_on && (lt % kBwdChunk) == 0) save_ckpt(c0 + lt, h);
         const float dl = s_delta[buf][lt][lane];
         const float du = s_du[buf][lt][lane];
         float bv[G], cv[G];
@@ -424,6 +436,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
 #pragma unroll
         for (int lt = 0; lt < TC; ++lt) {
           if (lt + PD < TC) rd(lt + PD, (lt + PD) % (PD + 1));
+          if (lt % kBwdChunk == 0 && ckpt_on) save_ckpt(c0 + lt, h);
           __builtin_amdgcn_sched_barrier(0);
           const int slot = lt % (PD + 1);
           float y = 0.0f;
@@ -498,7 +511,6 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
 
   // ---- carry-in ------------------------------------------------------------
   float h[G];
-  const int gidx = w * G;  // first state of this wave's group
   const int64_t rec_state = static_cast<int64_t>(rec) * N * 64;
   bool published = false;
   // Look-back segment: skip the aggregate pass when the predecessor has

@@ -7,6 +7,12 @@
 
 namespace ssm {
 
+// Steps per chunk of the backward's reverse phase: one checkpoint (the state
+// before the chunk) per kBwdChunk steps; the chunk's states and decays are
+// recomputed into registers.  The forward's training mode writes the same
+// checkpoints.
+constexpr int kBwdChunk = 8;
+
 // Carry records exchanged between sequence segments of one channel block.
 // A record is indexed by rec = chain * n_seg + seg, and split per state group
 // (one wave per group), so every wave publishes and consumes its own part.
@@ -17,6 +23,8 @@ struct FwdScratch {
   float* agg_b;      // [recs][N][64] segment's own final state from zero (look-back only)
   float* agg_s;      // [recs][groups][64] segment's sum of Delta (look-back only)
   int spin_limit;    // bound on each carry wait (iterations of s_sleep)
+  float* ckpt;       // nullable: [chains][n_ckpt][N][64] state before every
+                     // kBwdChunk-th step, for the backward (training mode)
 };
 
 struct FwdShape {
@@ -32,6 +40,7 @@ struct FwdShape {
   int32_t has_bias, has_D, has_z, has_h0, has_last;
   int32_t vec_io;    // activation rows may be moved in aligned vector runs
   int32_t zoh;       // 1: exact zero-order-hold input term, 0: Delta * B
+  int64_t n_ckpt;    // ceil(seqlen / kBwdChunk): checkpoints per chain
 };
 
 struct FwdPtrs {
@@ -96,6 +105,7 @@ struct BwdPtrs {
   const float* h0;
   const void* dout;
   const float* dlast;
+  const float* ckpt_in;  // nullable: checkpoints written by the forward's training mode
   void* du;
   void* ddelta;
   float* dA;
@@ -125,10 +135,7 @@ struct BwdShape {
   int32_t vec_io_f;  // phase F runs (kBwdFwdChunk / waves channels) may be vector moves
 };
 
-// Steps per chunk of the backward's reverse phase (one checkpoint per chunk;
-// the chunk's states and decays are recomputed into registers), and steps
-// staged at a time by its checkpointing forward phase.
-constexpr int kBwdChunk = 8;
+// Steps staged at a time by the backward's checkpointing forward phase.
 constexpr int kBwdFwdChunk = 32;
 
 // Launches the backward kernel for (dtype, N) and the reductions over channel

@@ -18,7 +18,8 @@ SSM_OK, SSM_EINVAL, SSM_EDTYPE, SSM_EALIGN, SSM_ENOMEM = 0, -1, -2, -3, -4
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 def test_header_declares_the_abi():
@@ -186,3 +187,21 @@ def test_conv_validation():
                                     None) == SSM_EINVAL               # state required
     assert lib.causal_conv1d_update(P[0], P[1], P[2], None, 4, 1, P[0], ctypes.byref(d1),
                                     None) == SSM_EINVAL               # out aliases state
+
+
+def test_training_pair_validation():
+    lib = _lib.load()
+    d = _dims(b=2, L=20, d=100, n=16)
+    # 2 rows x 2 channel blocks x ceil(20/8) checkpoints x 16 states x 64 lanes x 4 bytes
+    assert lib.ssm_ckpt_bytes(ctypes.byref(d)) == 2 * 2 * 3 * 16 * 64 * 4
+    assert lib.ssm_ckpt_bytes(ctypes.byref(_dims(n=5))) == SSM_EINVAL
+    rc = lib.selective_scan_fwd_train(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None,
+                                      P[5], None, None, ctypes.byref(d), None)
+    assert rc == SSM_EINVAL            # ckpt is required
+    rc = lib.selective_scan_fwd_train(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None,
+                                      P[5], None, P[0], ctypes.byref(d), None)
+    assert rc == SSM_EINVAL            # ckpt aliases u
+    rc = lib.selective_scan_bwd_ckpt(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None,
+                                     P[5], None, None, P[6], P[7], P[8], P[9], P[10], None,
+                                     None, None, None, ctypes.byref(d), None)
+    assert rc == SSM_EINVAL            # ckpt is required

@@ -35,7 +35,7 @@ def _grads_in(x, tag, seed, *, dlast=True, h0=True):
     return g
 
 
-def gpu_backward(x, tag, g, *, D=True, z=True, bias=True, softplus=True):
+def gpu_backward(x, tag, g, *, D=True, z=True, bias=True, softplus=True, ckpt=None):
     from selective_state_space_38_amd import selective_scan_bwd
     dt = act_dtype(tag)
     res = selective_scan_bwd(
@@ -44,9 +44,32 @@ def gpu_backward(x, tag, g, *, D=True, z=True, bias=True, softplus=True):
         D=to_dev(x["D"], torch.float32) if D else None, z=to_dev(x["z"], dt) if z else None,
         delta_bias=to_dev(x["dt_bias"], torch.float32) if bias else None,
         delta_softplus=softplus, h0=to_dev(g["h0"], torch.float32),
-        dlast=to_dev(g["dlast"], torch.float32))
+        dlast=to_dev(g["dlast"], torch.float32), ckpt=ckpt)
     torch.cuda.synchronize()
     return {k: v.double().cpu().numpy() for k, v in res.items()}
+
+
+def gpu_forward_train(x, tag, g):
+    """The training-mode forward: returns (out, ckpt buffer) and checks its
+    output against the plain forward's: bit for bit when no segment uses the
+    look-back (whose summation path depends on timing), else to tolerance."""
+    from selective_state_space_38_amd import ckpt_buffer, fwd_plan, selective_scan_fwd
+    dt = act_dtype(tag)
+    args = (to_dev(x["u"], dt), to_dev(x["delta"], dt), to_dev(x["A"], torch.float32),
+            to_dev(x["B"], dt), to_dev(x["C"], dt))
+    kw = dict(D=to_dev(x["D"], torch.float32), z=to_dev(x["z"], dt),
+              delta_bias=to_dev(x["dt_bias"], torch.float32), h0=to_dev(g["h0"], torch.float32))
+    ck = ckpt_buffer(args[0], x["A"].shape[1])
+    out_t = selective_scan_fwd(*args, **kw, ckpt=ck)
+    out_p = selective_scan_fwd(*args, **kw)
+    torch.cuda.synchronize()
+    b, L, d = x["u"].shape
+    if fwd_plan(b, L, d, x["A"].shape[1], dt)["lookback"] == 0:
+        assert torch.equal(out_t, out_p), "training-mode forward changed the output"
+    else:
+        a, c = out_t.double().cpu().numpy(), out_p.double().cpu().numpy()
+        check("training-mode out", a, c, float(np.max(np.abs(c))), TOL[tag])
+    return out_t, ck
 
 
 def oracle_backward(x, g, *, D=True, z=True, bias=True, softplus=True, chans=None):
@@ -167,3 +190,46 @@ def test_backward_2p8b_full_size_sampled():
     got2 = gpu_backward(x, "bf16", g2)
     check_grads({"dB": got2["dB"], "dC": got2["dC"]}, ref, "bf16", keys=["dB", "dC"])
     assert np.all(got2["du"][:, :, ~mask] == 0.0)
+
+
+@pytest.mark.parametrize("wl,b,L,d", [
+    ("tiny", 1, 64, 16),
+    ("mamba130m", 2, 301, 130),
+    ("mamba130m", 1, 200, 64 * 300),     # 256 whole chains + split remainder
+])
+def test_training_pair(wl, b, L, d):
+    """selective_scan_fwd with ckpt, then selective_scan_bwd with the same
+    ckpt: the backward reads the forward's checkpoints instead of running its
+    own forward pass; every gradient against the oracle."""
+    tag = synth.WORKLOADS[wl].dtype
+    n = 4 if wl == "tiny" else 16
+    x = synth.make(wl, batch=b, seqlen=L, dim=d, dstate=n, a_init="random")
+    g = _grads_in(x, tag, 12)
+    _, ck = gpu_forward_train(x, tag, g)
+    got = gpu_backward(x, tag, g, ckpt=ck)
+    if d <= 256:
+        ref = oracle_backward(x, g)
+        check_grads(got, ref, tag)
+    else:
+        chans = np.array([0, 5, 16383, 16384, 17000, d - 1])
+        ref = oracle_backward(x, g, chans=chans)
+        cols = {"du": got["du"][:, :, chans], "ddelta": got["ddelta"][:, :, chans],
+                "dz": got["dz"][:, :, chans], "dA": got["dA"][chans], "dD": got["dD"][chans],
+                "ddt_bias": got["ddt_bias"][chans], "dh0": got["dh0"][:, chans]}
+        check_grads(cols, ref, tag, keys=list(cols))
+
+
+def test_training_pair_2p8b_full_size():
+    """The 2.8B layer: training-mode forward, then the backward from its
+    checkpoints, checked on sampled channels as in the full-size test."""
+    w = synth.WORKLOADS["mamba2p8b"]
+    x = synth.make("mamba2p8b")
+    g = _grads_in(x, "bf16", 13)
+    _, ck = gpu_forward_train(x, "bf16", g)
+    got = gpu_backward(x, "bf16", g, ckpt=ck)
+    chans = np.array([0, 63, 64, 4095, 4096, w.dim - 1])
+    ref = oracle_backward(x, g, chans=chans)
+    cols = {"du": got["du"][:, :, chans], "ddelta": got["ddelta"][:, :, chans],
+            "dz": got["dz"][:, :, chans], "dA": got["dA"][chans], "dD": got["dD"][chans],
+            "ddt_bias": got["ddt_bias"][chans], "dh0": got["dh0"][:, chans]}
+    check_grads(cols, ref, "bf16", keys=list(cols))
