@@ -294,11 +294,44 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const int64_t cblk = div_up(dims->dim, 64);
   const int64_t nck = div_up(dims->seqlen, ssm::kBwdChunk);
   auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
+  // Plan.  With the forward's checkpoints the state at any chunk start is
+  // known, so the chains beyond a multiple of the CU count can be split into
+  // segments that exchange only the adjoint carry (reverse look-back), as the
+  // forward does; without them every chain runs whole.
+  const int64_t chains = dims->batch * cblk;
+  int64_t n_full = chains, n_seg = 1, seg_len = dims->seqlen;
+  if (ckpt_in) {
+    const int64_t K = (chains / kComputeUnits) * kComputeUnits;
+    const int64_t M = chains - K;
+    int64_t S = (K > 0 && M > 0) ? kComputeUnits / M : 1;
+    if (S < 3) S = 1;
+    int64_t kf = K;
+    const int force_split = env_int("SSM_FORCE_BWD_SPLIT", 0);
+    const int force_whole = env_int("SSM_FORCE_BWD_WHOLE", -1);
+    if (force_split >= 1) {
+      S = force_split;
+      kf = force_whole >= 0 && force_whole <= chains ? force_whole : K;
+    }
+    if (S > 1 && kf < chains) {
+      const int64_t sl = div_up(div_up(dims->seqlen, S), ssm::kBwdFwdChunk) * ssm::kBwdFwdChunk;
+      if (div_up(dims->seqlen, sl) > 1) {
+        n_full = kf;
+        seg_len = sl;
+        n_seg = div_up(dims->seqlen, sl);
+      }
+    }
+  }
+  const int64_t recs = (chains - n_full) * n_seg;
+  const int64_t groups = bwd_groups(N);
   const int64_t b_ckpt = ckpt_in ? 0 : up256(dims->batch * cblk * nck * N * 64 * 4);
   const int64_t b_bc = up256(cblk * dims->batch * dims->seqlen * 2 * N * 4);
-  const int64_t b_a = up256(dims->batch * dims->dim * N * 4);
-  const int64_t b_d = up256(dims->batch * dims->dim * 4);
-  const int64_t total = b_ckpt + b_bc + b_a + 2 * b_d;
+  const int64_t b_a = up256(dims->batch * n_seg * dims->dim * N * 4);
+  const int64_t b_d = up256(dims->batch * n_seg * dims->dim * 4);
+  const int64_t n_int = 1 + recs * groups;                    // ticket + status words
+  const int64_t b_int = up256(n_int * 4);
+  const int64_t b_rec = up256(recs * N * 64 * 4);
+  const int64_t b_recs = up256(recs * groups * 64 * 4);
+  const int64_t total = b_ckpt + b_bc + b_a + 2 * b_d + b_int + 2 * b_rec + b_recs;
   if (total > (1LL << 40)) return SSM_EINVAL;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -317,12 +350,25 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   p.part_a = reinterpret_cast<float*>(scratch + b_ckpt + b_bc);
   p.part_d = reinterpret_cast<float*>(scratch + b_ckpt + b_bc + b_a);
   p.part_bias = reinterpret_cast<float*>(scratch + b_ckpt + b_bc + b_a + b_d);
+  {
+    char* q = scratch + b_ckpt + b_bc + b_a + 2 * b_d;
+    p.ticket = reinterpret_cast<int*>(q);
+    p.status = p.ticket + 1;
+    p.inc = reinterpret_cast<float*>(q + b_int);
+    p.agg_b = reinterpret_cast<float*>(q + b_int + b_rec);
+    p.agg_s = reinterpret_cast<float*>(q + b_int + 2 * b_rec);
+  }
 
   ssm::BwdShape sh;
   sh.batch = dims->batch;
   sh.seqlen = dims->seqlen;
   sh.dim = dims->dim;
   sh.n_cblk = static_cast<int32_t>(cblk);
+  sh.chains = static_cast<int32_t>(chains);
+  sh.n_full = static_cast<int32_t>(n_full);
+  sh.n_seg = static_cast<int32_t>(n_seg);
+  sh.seg_len = seg_len;
+  sh.spin_limit = env_int("SSM_TEST_SPIN_LIMIT", kDefaultSpinLimit);
   sh.nchunks = nck;
   sh.softplus = softplus ? 1 : 0;
   sh.has_D = D != nullptr;
@@ -599,12 +645,13 @@ const char* ssm_status_string(int status) {
 }
 
 int ssm_check_device_errors(void* stream) {
-  unsigned c32 = 0, c16 = 0;
+  unsigned c32 = 0, c16 = 0, cb = 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (ssm::fwd_f32::read_and_clear_errors(st, &c32) != hipSuccess ||
-      ssm::fwd_bf16::read_and_clear_errors(st, &c16) != hipSuccess)
+      ssm::fwd_bf16::read_and_clear_errors(st, &c16) != hipSuccess ||
+      ssm::read_and_clear_bwd_errors(st, &cb) != hipSuccess)
     return SSM_ELAUNCH;
-  return (c32 || c16) ? SSM_ETIMEOUT : SSM_OK;
+  return (c32 || c16 || cb) ? SSM_ETIMEOUT : SSM_OK;
 }
 
 int ssm_fwd_plan_for(const ssm_dims* dims, ssm_fwd_plan* plan) {

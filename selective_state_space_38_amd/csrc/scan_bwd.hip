@@ -47,6 +47,10 @@
 
 namespace ssm {
 
+__device__ unsigned g_bwd_carry_timeouts;
+
+enum : int { kBwdEmpty = 0, kBwdAggregate = 1, kBwdInclusive = 2 };
+
 template <typename T, int NG, int G, int TC, int TCF>
 __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
   constexpr int N = NG * G;
@@ -89,6 +93,8 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
     SmemF f;
   };
   __shared__ __align__(16) Smem sm;
+  __shared__ int s_ticket;
+  __shared__ int s_pred_final;
 
   const T* const xu = static_cast<const T*>(p.u);
   const T* const xdt = static_cast<const T*>(p.delta);
@@ -103,9 +109,24 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = static_cast<int>(blockIdx.x);
-  const int b = wg / sh.n_cblk;
-  const int cblk = wg - b * sh.n_cblk;
+  // Workgroups 0 .. n_full-1 run whole chains; the others are segments of
+  // the split chains, ordered by an atomic ticket from the LAST segment in
+  // time backwards (the adjoint runs backwards), so a segment only waits on
+  // lower tickets, which are already running.
+  const bool whole = static_cast<int>(blockIdx.x) < sh.n_full;
+  int ticket = 0;
+  if (!whole) {
+    if (tid == 0) s_ticket = atomicAdd(p.ticket, 1);
+    __syncthreads();
+    ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+  }
+  const int n_split = sh.chains - sh.n_full;
+  const int rseg = whole ? 0 : ticket / n_split;
+  const int chain = whole ? static_cast<int>(blockIdx.x) : sh.n_full + (ticket - rseg * n_split);
+  const int nseg_c = whole ? 1 : sh.n_seg;
+  const int seg = nseg_c - 1 - rseg;              // segment index in time order
+  const int b = chain / sh.n_cblk;
+  const int cblk = chain - b * sh.n_cblk;
   const int64_t L = sh.seqlen;
   const int64_t dim = sh.dim;
   const int64_t bsz = sh.batch;
@@ -123,7 +144,15 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
   }
   const int64_t row0 = static_cast<int64_t>(b) * L;
   const int64_t nck = sh.nchunks;
-  float* ckpt = p.ckpt + (static_cast<int64_t>(wg) * nck) * N * 64;
+  float* ckpt = p.ckpt + (static_cast<int64_t>(chain) * nck) * N * 64;
+  // this workgroup's time range and chunks
+  const int64_t seg_len_c = whole ? L : sh.seg_len;
+  const int64_t t_begin = static_cast<int64_t>(seg) * seg_len_c;
+  const int64_t t_end = (t_begin + seg_len_c < L) ? t_begin + seg_len_c : L;
+  const int64_t c_lo = t_begin / TC;
+  const int64_t c_hi = (t_end - 1) / TC;
+  const int rec = whole ? 0 : (chain - sh.n_full) * sh.n_seg + seg;
+  const int slot = whole ? 0 : seg;               // partial-sum slot of dA, dD, ddt_bias
 
   // Tile roles: a thread owns one row of a chunk tile and a run of EPT (phase
   // R) or EPTF (phase F) consecutive channels.  last = index of the run's
@@ -315,10 +344,152 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
 
   float lamn[G], dA_acc[G];   // lamn = Abar_{t+1} lambda_{t+1}
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    lamn[g] = (sh.has_dlast && dvalid) ? p.dlast[(static_cast<int64_t>(b) * dim + d) * N + gidx + g]
-                                       : 0.0f;
-    dA_acc[g] = 0.0f;
+  for (int g = 0; g < G; ++g) dA_acc[g] = 0.0f;
+  bool published = false;
+  if (seg == nseg_c - 1) {
+    // the last segment in time starts from the final state's gradient
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      lamn[g] = (sh.has_dlast && dvalid)
+                    ? p.dlast[(static_cast<int64_t>(b) * dim + d) * N + gidx + g]
+                    : 0.0f;
+  } else {
+    // A split segment needs the adjoint carried out of the segments after
+    // it.  If the next segment has published its inclusive carry for every
+    // state group, take it; otherwise compute this segment's aggregate (the
+    // adjoint run backwards over the segment from zero, and its sum of
+    // Delta), publish it, and walk the later segments' records.  The map
+    // carry-in -> carry-out of a segment is lamn_out = exp(A sum Delta)
+    // lamn_in + lamn_out(0): the pair operator of "Mamba / MambaMini" Step 2.
+    if (tid == 0) {
+      int all = 1;
+      for (int q = 0; q < NG; ++q)
+        all &= __hip_atomic_load(&p.status[(rec + 1) * NG + q], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) == kBwdInclusive;
+      s_pred_final = all;
+    }
+    lds_barrier();
+    const bool next_final = __builtin_amdgcn_readfirstlane(s_pred_final) != 0;
+    const int64_t rs_base = static_cast<int64_t>(rec) * N * 64;
+    if (next_final) {
+      acquire_fence();
+      const int64_t ns = static_cast<int64_t>(rec + 1) * N * 64;
+#pragma unroll
+      for (int g = 0; g < G; ++g) lamn[g] = p.inc[ns + (gidx + g) * 64 + lane];
+    } else {
+      float lamA[G], sum_delta = 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) lamA[g] = 0.0f;
+      for (int64_t c = c_hi; c >= c_lo; --c) {
+        const int64_t c0 = c * TC;
+        const int n = static_cast<int>((L - c0 < TC) ? L - c0 : TC);
+        RawR raw;
+        RunVals rv;
+        float unused[G];
+        load_r(c, raw);
+        stage_r(c, raw, rv, unused);
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+          const bool ok = tr < n && k <= run_last;
+          float dyk = rv.dout[k];
+          if (sh.has_z) dyk = rv.dout[k] * (rv.z[k] * sigmoid_f32(rv.z[k]));
+          sm.r.dy[tr][tc + k] = ok ? dyk : 0.0f;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int t = TC - 1; t >= 0; --t) {
+          const float dl = sm.r.dl[t][lane];
+          const float dyt = sm.r.dy[t][lane];
+          sum_delta += dl;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float lam = fmaf(dyt, sm.r.C[t][gidx + g], lamA[g]);
+            lamA[g] = exp2_hw(dl * A2[g]) * lam;
+          }
+        }
+        lds_barrier();
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) p.agg_b[rs_base + (gidx + g) * 64 + lane] = lamA[g];
+      p.agg_s[(static_cast<int64_t>(rec) * NG + w) * 64 + lane] = sum_delta;
+      if (lane == 0)
+        __hip_atomic_store(&p.status[rec * NG + w], kBwdAggregate, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      // walk the later segments in windows of kWin: lane i polls record j + i
+      float acc_s = 0.0f, acc_b[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc_b[g] = 0.0f;
+      const int rec_last = (chain - sh.n_full) * sh.n_seg + sh.n_seg - 1;
+      constexpr int kWin = 8;
+      int j = rec + 1;
+      int spins = 0;
+      while (j <= rec_last) {
+        const int W = (rec_last - j + 1 < kWin) ? rec_last - j + 1 : kWin;
+        const int st = lane < W ? __hip_atomic_load(&p.status[(j + lane) * NG + w],
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : kBwdEmpty;
+        const uint64_t ready = __ballot(st >= kBwdAggregate);
+        const uint64_t incl = __ballot(st == kBwdInclusive);
+        const int run = static_cast<int>(__builtin_ctzll(~ready));
+        const uint64_t inc_in_run = incl & ((1ull << run) - 1ull);
+        const int take = inc_in_run ? static_cast<int>(__builtin_ctzll(inc_in_run)) + 1 : run;
+        if (take == 0) {
+          if (++spins > sh.spin_limit) {
+            if (lane == 0) atomicAdd(&g_bwd_carry_timeouts, 1u);
+            break;
+          }
+          if (spins < 16) {
+            __builtin_amdgcn_s_sleep(2);
+          } else {
+            __builtin_amdgcn_s_sleep(32);
+          }
+          continue;
+        }
+        acquire_fence();
+        float rb[kWin][G], rsum[kWin], ri[G];
+#pragma unroll
+        for (int k = 0; k < kWin; ++k) {
+          const int jj = j + (k < take ? k : 0);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            rb[k][g] = p.agg_b[(static_cast<int64_t>(jj) * N + gidx + g) * 64 + lane];
+          rsum[k] = p.agg_s[(static_cast<int64_t>(jj) * NG + w) * 64 + lane];
+        }
+        {
+          const int ji = j + take - 1;
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            ri[g] = inc_in_run ? p.inc[(static_cast<int64_t>(ji) * N + gidx + g) * 64 + lane]
+                               : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kWin; ++k) {
+          if (k < take) {
+            const bool last_inc = inc_in_run && k == take - 1;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+              acc_b[g] = fmaf(exp2_hw(A2[g] * acc_s), last_inc ? ri[g] : rb[k][g], acc_b[g]);
+            acc_s += rsum[k];
+          }
+        }
+        if (inc_in_run) break;
+        j += take;
+        spins = 0;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) lamn[g] = acc_b[g];
+      if (seg > 0) {
+        // this segment's own carry-out: its aggregate applied after the carry-in
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          p.inc[rs_base + (gidx + g) * 64 + lane] =
+              fmaf(exp2_hw(A2[g] * sum_delta), lamn[g], lamA[g]);
+        if (lane == 0)
+          __hip_atomic_store(&p.status[rec * NG + w], kBwdInclusive, __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      published = true;
+    }
   }
   float dD_acc[EPT], dbias_acc[EPT];
 #pragma unroll
@@ -331,15 +502,15 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
   RawR raw;
   RunVals rv;
   float hstart[G];
-  load_r(nck - 1, raw);
-  stage_r(nck - 1, raw, rv, hstart);
+  load_r(c_hi, raw);
+  stage_r(c_hi, raw, rv, hstart);
   drain_vmem();
   lds_barrier();
-  for (int64_t c = nck - 1; c >= 0; --c) {
+  for (int64_t c = c_hi; c >= c_lo; --c) {
     const int64_t c0 = c * TC;
     const int n = static_cast<int>((L - c0 < TC) ? L - c0 : TC);
     const bool row_ok = tr < n;
-    const int64_t cn = c > 0 ? c - 1 : 0;   // next chunk to stage (the first reloads itself)
+    const int64_t cn = c > c_lo ? c - 1 : c_lo;   // next chunk to stage (the first reloads itself)
     load_r(cn, raw);
 
     // recompute the chunk's states and decays from its checkpoint
@@ -480,13 +651,24 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
     lds_barrier();
   }
 
-  // ---- per-batch partials of dA, dD, ddt_bias; dh0 --------------------------
+  // a segment that took its carry-in ready-made publishes its carry-out now
+  if (!whole && !published && seg > 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      p.inc[static_cast<int64_t>(rec) * N * 64 + (gidx + g) * 64 + lane] = lamn[g];
+    if (lane == 0)
+      __hip_atomic_store(&p.status[rec * NG + w], kBwdInclusive, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- per-(batch, segment) partials of dA, dD, ddt_bias; dh0 -------------
+  const int64_t pslot = static_cast<int64_t>(b) * sh.n_seg + slot;
   if (dvalid) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int64_t i = (static_cast<int64_t>(b) * dim + d) * N + gidx + g;
-      p.part_a[i] = dA_acc[g];
-      if (p.dh0) p.dh0[i] = lamn[g];
+      p.part_a[(pslot * dim + d) * N + gidx + g] = dA_acc[g];
+      if (p.dh0 && seg == 0)
+        p.dh0[(static_cast<int64_t>(b) * dim + d) * N + gidx + g] = lamn[g];
     }
   }
 #pragma unroll
@@ -502,8 +684,8 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
       sd += sm.r.p1[0][t][tid];
       sbias += sm.r.p2[0][t][tid];
     }
-    p.part_d[static_cast<int64_t>(b) * dim + ch0 + tid] = sd;
-    p.part_bias[static_cast<int64_t>(b) * dim + ch0 + tid] = sbias;
+    p.part_d[pslot * dim + ch0 + tid] = sd;
+    p.part_bias[pslot * dim + ch0 + tid] = sbias;
   }
 }
 
@@ -543,20 +725,42 @@ static dim3 grid_for(int64_t count) {
   return dim3(static_cast<unsigned>((count + 255) / 256));
 }
 
+__global__ void bwd_fill_zero_kernel(int* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 template <typename T, int NG, int G>
 static hipError_t launch_bwd_typed(const BwdPtrs& p, const BwdShape& sh, hipStream_t st) {
   constexpr int TC = kBwdChunk;
   constexpr int TCF = kBwdFwdChunk;
-  const dim3 grid(static_cast<unsigned>(sh.batch * sh.n_cblk)), block(64 * NG);
+  hipError_t e;
+  if (sh.n_seg > 1) {
+    // split chains: zero the ticket, the status words and the partial-sum
+    // slots that whole chains leave unwritten
+    const int64_t n_int = 1 + static_cast<int64_t>(sh.chains - sh.n_full) * sh.n_seg * NG;
+    hipLaunchKernelGGL(bwd_fill_zero_kernel, grid_for(n_int), dim3(256), 0, st, p.ticket, n_int);
+    const int64_t na = sh.batch * sh.n_seg * sh.dim * (NG * G);
+    const int64_t nd = sh.batch * sh.n_seg * sh.dim;
+    hipLaunchKernelGGL(bwd_fill_zero_kernel, grid_for(na), dim3(256), 0, st,
+                       reinterpret_cast<int*>(p.part_a), na);
+    hipLaunchKernelGGL(bwd_fill_zero_kernel, grid_for(nd), dim3(256), 0, st,
+                       reinterpret_cast<int*>(p.part_d), nd);
+    hipLaunchKernelGGL(bwd_fill_zero_kernel, grid_for(nd), dim3(256), 0, st,
+                       reinterpret_cast<int*>(p.part_bias), nd);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t workgroups = sh.n_full + static_cast<int64_t>(sh.chains - sh.n_full) * sh.n_seg;
+  const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * NG);
   hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, TC, TCF>), grid, block, 0, st, p, sh);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int N = NG * G;
   const int64_t rows = sh.batch * sh.seqlen;
   hipLaunchKernelGGL(reduce_bc_kernel<T>, grid_for(rows * N), dim3(256), 0, st, p.part_bc,
                      static_cast<T*>(p.dB), static_cast<T*>(p.dC), rows, N, sh.n_cblk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int parts = static_cast<int>(sh.batch);
+  const int parts = static_cast<int>(sh.batch * sh.n_seg);
   hipLaunchKernelGGL(reduce_sum_kernel, grid_for(sh.dim * N), dim3(256), 0, st, p.part_a, p.dA,
                      sh.dim * N, parts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -586,6 +790,17 @@ static hipError_t dispatch_bwd(int dstate, const BwdPtrs& p, const BwdShape& sh,
     case 64: return launch_bwd_typed<T, 8, 8>(p, sh, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t read_and_clear_bwd_errors(hipStream_t stream, unsigned* count) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_bwd_carry_timeouts), sizeof(unsigned), 0,
+                          hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  const unsigned zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_bwd_carry_timeouts), &zero, sizeof(unsigned), 0,
+                           hipMemcpyHostToDevice);
 }
 
 hipError_t launch_scan_bwd(int dtype, int dstate, const BwdPtrs& p, const BwdShape& sh,

@@ -118,9 +118,15 @@ struct BwdPtrs {
   // scratch
   float* ckpt;       // [batch * channel blocks][chunks][N][64] chunk-start states
   float* part_bc;    // [channel blocks][batch][L][2N] per-block dB | dC rows
-  float* part_a;     // [batch][dim][N] per-batch dA
-  float* part_d;     // [batch][dim] per-batch dD
-  float* part_bias;  // [batch][dim] per-batch ddt_bias
+  float* part_a;     // [batch][n_seg][dim][N] per-(batch, segment) dA
+  float* part_d;     // [batch][n_seg][dim] per-(batch, segment) dD
+  float* part_bias;  // [batch][n_seg][dim] per-(batch, segment) ddt_bias
+  // adjoint carries between the segments of split chains (reverse look-back)
+  int* ticket;       // [1] work-order counter (zeroed before launch)
+  int* status;       // [recs][groups] 0 empty, 1 aggregate, 2 inclusive
+  float* inc;        // [recs][N][64] adjoint carried out of the segment's start
+  float* agg_b;      // [recs][N][64] the same from a zero carry-in
+  float* agg_s;      // [recs][groups][64] segment's sum of Delta
 };
 
 struct BwdShape {
@@ -128,6 +134,11 @@ struct BwdShape {
   int64_t seqlen;
   int64_t dim;
   int32_t n_cblk;    // channel blocks of 64
+  int32_t chains;    // batch * channel blocks
+  int32_t n_full;    // chains 0 .. n_full-1 run whole (workgroup = chain)
+  int32_t n_seg;     // segments per split chain (1: no split)
+  int64_t seg_len;   // steps per segment of a split chain (multiple of kBwdFwdChunk)
+  int32_t spin_limit;  // bound on each carry wait
   int64_t nchunks;   // ceil(seqlen / kBwdChunk)
   int32_t softplus;
   int32_t has_D, has_z, has_bias, has_h0, has_dlast;
@@ -142,6 +153,10 @@ constexpr int kBwdFwdChunk = 32;
 // blocks and batch.  Returns hipErrorInvalidValue for an unsupported N.
 hipError_t launch_scan_bwd(int dtype, int dstate, const BwdPtrs& p, const BwdShape& sh,
                            hipStream_t stream);
+
+// Reads and clears the backward's count of adjoint-carry waits that timed
+// out (synchronises the stream first).
+hipError_t read_and_clear_bwd_errors(hipStream_t stream, unsigned* count);
 
 
 // Causal depthwise conv1d (+ SiLU): forward over a sequence and the decode

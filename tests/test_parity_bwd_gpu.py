@@ -233,3 +233,46 @@ def test_training_pair_2p8b_full_size():
             "dz": got["dz"][:, :, chans], "dA": got["dA"][chans], "dD": got["dD"][chans],
             "ddt_bias": got["ddt_bias"][chans], "dh0": got["dh0"][:, chans]}
     check_grads(cols, ref, "bf16", keys=list(cols))
+
+
+@pytest.mark.parametrize("split,whole,L", [(4, 1, 700), (8, 0, 515), (3, 2, 300)])
+def test_training_pair_split_chains(split, whole, L):
+    """Backward from checkpoints with chains split into segments that
+    exchange the adjoint carry by a reverse look-back (forced here on a small
+    shape: `whole` chains run whole, the rest in `split` segments); every
+    gradient, including the channel sums, against the oracle."""
+    x = synth.make("mamba130m", batch=2, seqlen=L, dim=130, dstate=16, a_init="random")
+    g = _grads_in(x, "f32", 14)
+    _, ck = gpu_forward_train(x, "f32", g)
+    with env(SSM_FORCE_BWD_SPLIT=split, SSM_FORCE_BWD_WHOLE=whole):
+        got = gpu_backward(x, "f32", g, ckpt=ck)
+    ref = oracle_backward(x, g)
+    check_grads(got, ref, "f32")
+
+
+def test_split_backward_without_dlast_and_h0():
+    x = synth.make("mamba2p8b", batch=1, seqlen=400, dim=200, dstate=16, a_init="random")
+    g = _grads_in(x, "bf16", 15, dlast=False, h0=False)
+    _, ck = gpu_forward_train(x, "bf16", g)
+    with env(SSM_FORCE_BWD_SPLIT=5, SSM_FORCE_BWD_WHOLE=1):
+        got = gpu_backward(x, "bf16", g, ckpt=ck)
+    ref = oracle_backward(x, g)
+    check_grads(got, ref, "bf16")
+
+
+def test_split_backward_wait_bound_reports_timeout():
+    """A zero spin bound ends the adjoint-carry walk at the first unpublished
+    record; the kernel still exits and the error counter reports it."""
+    from selective_state_space_38_amd import check_device_errors
+    x = synth.make("mamba130m", batch=1, seqlen=2048, dim=64, dstate=16, a_init="random")
+    g = _grads_in(x, "f32", 16)
+    _, ck = gpu_forward_train(x, "f32", g)
+    check_device_errors()
+    with env(SSM_FORCE_BWD_SPLIT=16, SSM_FORCE_BWD_WHOLE=0, SSM_TEST_SPIN_LIMIT=0):
+        gpu_backward(x, "f32", g, ckpt=ck)
+    with pytest.raises(RuntimeError, match="SSM_ETIMEOUT"):
+        check_device_errors()
+    with env(SSM_FORCE_BWD_SPLIT=16, SSM_FORCE_BWD_WHOLE=0):
+        got = gpu_backward(x, "f32", g, ckpt=ck)
+    check_device_errors()
+    check_grads(got, oracle_backward(x, g), "f32")
