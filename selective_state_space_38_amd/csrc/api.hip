@@ -301,9 +301,14 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const int64_t chains = dims->batch * cblk;
   int64_t n_full = chains, n_seg = 1, seg_len = dims->seqlen;
   if (ckpt_in) {
+    // With fewer chains than CUs (K = 0) every chain is split, into enough
+    // segments for ~4 workgroups per CU (measured best at the million-token
+    // shape: 64, 128, 256 segments per chain took 16.4, 10.4, 9.6 ms); else
+    // the remainder chains get ~one segment per CU (4 of 2, 3, 4, 8, 16
+    // measured best at the 2.8B layer).  Segments are at least 512 steps.
     const int64_t K = (chains / kComputeUnits) * kComputeUnits;
     const int64_t M = chains - K;
-    int64_t S = (K > 0 && M > 0) ? kComputeUnits / M : 1;
+    int64_t S = M == 0 ? 1 : (K == 0 ? 4 * kComputeUnits / M : kComputeUnits / M);
     if (S < 3) S = 1;
     int64_t kf = K;
     const int force_split = env_int("SSM_FORCE_BWD_SPLIT", 0);
@@ -313,7 +318,8 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
       kf = force_whole >= 0 && force_whole <= chains ? force_whole : K;
     }
     if (S > 1 && kf < chains) {
-      const int64_t sl = div_up(div_up(dims->seqlen, S), ssm::kBwdFwdChunk) * ssm::kBwdFwdChunk;
+      int64_t sl = div_up(div_up(dims->seqlen, S), ssm::kBwdFwdChunk) * ssm::kBwdFwdChunk;
+      if (force_split < 1 && sl < 512) sl = 512;
       if (div_up(dims->seqlen, sl) > 1) {
         n_full = kf;
         seg_len = sl;
