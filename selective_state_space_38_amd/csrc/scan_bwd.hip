@@ -578,10 +578,10 @@ __global__ __launch_bounds__(64 * NG) void scan_bwd_kernel(BwdPtrs p, BwdShape s
         pB[g] = lam * du;
         s1 = fmaf(lam, sm.r.B[t][gidx + g], s1);
         const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][g] : hstart[g];
-        const float lq = lam * (as[t][g] * hp);
+        lamn[g] = as[t][g] * lam;               // Abar_t lambda_t, carried to step t-1
+        const float lq = lamn[g] * hp;          // lambda_t Abar_t h_{t-1}
         s2 = fmaf(lq, Af[g], s2);
         dA_acc[g] = fmaf(lq, dl, dA_acc[g]);
-        lamn[g] = as[t][g] * lam;
       }
       sm.r.p1[w][t][lane] = s1;
       sm.r.p2[w][t][lane] = s2;
