@@ -301,14 +301,17 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const int64_t chains = dims->batch * cblk;
   int64_t n_full = chains, n_seg = 1, seg_len = dims->seqlen;
   if (ckpt_in) {
-    // With fewer chains than CUs (K = 0) every chain is split, into enough
-    // segments for ~4 workgroups per CU (measured best at the million-token
-    // shape: 64, 128, 256 segments per chain took 16.4, 10.4, 9.6 ms); else
+    // With at most half as many chains as CUs (K = 0) every chain is split,
+    // into enough segments for ~4 workgroups per CU (measured best at the
+    // million-token shape: 64, 128, 256 segments per chain took 16.4, 10.4,
+    // 9.6 ms; with 192 chains, 130M, splitting measured slower); otherwise
     // the remainder chains get ~one segment per CU (4 of 2, 3, 4, 8, 16
     // measured best at the 2.8B layer).  Segments are at least 512 steps.
     const int64_t K = (chains / kComputeUnits) * kComputeUnits;
     const int64_t M = chains - K;
-    int64_t S = M == 0 ? 1 : (K == 0 ? 4 * kComputeUnits / M : kComputeUnits / M);
+    int64_t S = M == 0 ? 1
+              : (K == 0 ? (M <= kComputeUnits / 2 ? 4 * kComputeUnits / M : 1)
+                        : kComputeUnits / M);
     if (S < 3) S = 1;
     int64_t kf = K;
     const int force_split = env_int("SSM_FORCE_BWD_SPLIT", 0);
