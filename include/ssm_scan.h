@@ -45,11 +45,13 @@
  *     aligned, `out` must not alias an input.  A failed launch returns
  *     SSM_ELAUNCH; faults inside a kernel surface at the caller's next
  *     synchronisation, as for any HIP kernel.
- *   - The forward allocates stream-ordered scratch (hipMallocAsync) for the
- *     carries between sequence segments and frees it on the same stream;
- *     failure returns SSM_ENOMEM.  There is no other global state except a
- *     per-device error counter read by ssm_check_device_errors, so calls on
- *     different streams or host threads may run concurrently.
+ *   - Entry points that need scratch (carries between sequence segments,
+ *     checkpoints, partial sums, the block's intermediates) allocate it
+ *     stream-ordered (hipMallocAsync) and free it on the same stream;
+ *     failure returns SSM_ENOMEM.  The only other state is a per-device count
+ *     of timed-out carry waits (read by ssm_check_device_errors) and, for
+ *     mamba_block_fwd, one rocBLAS handle per host thread and device, so
+ *     calls on different streams or host threads may run concurrently.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
