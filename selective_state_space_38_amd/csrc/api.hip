@@ -38,9 +38,10 @@ int states_per_group(int64_t n) {
     // instantiated (groups, per-group) pairs
     if ((n <= 2 && groups == 1) || (n == 4 && groups == 1) || (n == 8 && (groups <= 2)) ||
         (n == 16 && (groups == 1 || groups == 2 || groups == 4 || groups == 8)) ||
-        (n == 32 && groups == 8) || (n == 64 && groups == 16))
+        (n == 32 && groups == 8) || (n == 64 && groups == 8))
       return g;
   }
+  if (n == 64) return 8;
   return n < 4 ? static_cast<int>(n) : 4;
 }
 
@@ -199,8 +200,8 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.zoh = bbar == SSM_BBAR_ZOH ? 1 : 0;
   sh.n_ckpt = div_up(dims->seqlen, ssm::kBwdChunk);
   {
-    // per-thread runs of the chunk tile: kChunk / groups consecutive channels
-    const int64_t ept = plan.chunk / plan.state_groups;
+    // per-thread runs of the chunk tile: chunk / helper waves consecutive channels
+    const int64_t ept = plan.chunk / ssm::helper_waves(plan.state_groups);
     const int64_t esz = dims->dtype == SSM_BF16 ? 2 : 4;
     const uintptr_t need = static_cast<uintptr_t>(ept * esz >= 16 ? 16 : ept * esz);
     bool ok = ept * esz >= 4 && dims->dim % ept == 0;

@@ -91,8 +91,8 @@ __device__ __forceinline__ int wait_status(const int* p, int need, int limit) {
   return v;
 }
 
-template <typename T, int NG, int G, int TC, bool ZOH>
-__global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
+template <typename T, int NG, int G, int NP, int TC, bool ZOH>
+__global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     const T* __restrict__ u, const T* __restrict__ dtp,
     const float* __restrict__ A, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const float* __restrict__ Dv,
@@ -100,23 +100,21 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
     const float* __restrict__ h0, T* __restrict__ out,
     float* __restrict__ last_state, FwdScratch sc, FwdShape sh) {
   constexpr int N = NG * G;
-  constexpr int NT = 64 * NG;          // threads
-  constexpr int EPT = TC / NG;         // tile elements per thread (one row run)
-  constexpr int TPR = 64 / EPT;        // threads per tile row
-  static_assert(TC % NG == 0 && 64 % EPT == 0, "chunk must split evenly over the groups");
+  constexpr int PT = 64 * NP;          // helper threads
+  constexpr int EPT = TC / NP;         // tile elements per helper thread (one row run)
+  constexpr int TPR = 64 / EPT;        // helper threads per tile row
+  static_assert(TC % NP == 0 && 64 % EPT == 0, "chunk must split evenly over the helpers");
   constexpr int ESZ = static_cast<int>(sizeof(T));
   constexpr bool kBCWords = (N * ESZ) % 4 == 0;          // B/C chunk rows are dword granular
   constexpr int BC_UNITS = kBCWords ? TC * N * ESZ / 4 : TC * N;
-  constexpr int BCPT = (BC_UNITS + NT - 1) / NT;          // B/C dwords (or elements) per thread
+  constexpr int BCPT = (BC_UNITS + PT - 1) / PT;          // B/C dwords (or elements) per thread
   using TileRun = Run<T, EPT>;
-
-
 
   __shared__ float s_delta[2][TC][64];
   __shared__ float s_du[2][TC][64];
   __shared__ __align__(16) float s_B[2][TC][N];
   __shared__ __align__(16) float s_C[2][TC][N];
-  __shared__ float s_y[NG][TC][64];
+  __shared__ __align__(16) float s_y[2][NG][TC][64];
   __shared__ int s_ticket;
   __shared__ int s_pred_final;
 
@@ -125,7 +123,8 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   // wave-uniform values go through readfirstlane so the compiler keeps them
   // (and addresses built from them) in SGPRs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int gidx = w * G;  // first state of this wave's group
+  const bool scan_wave = w < NG;           // scan waves 0..NG-1, helpers NG..NG+NP-1
+  const int gidx = scan_wave ? w * G : 0;  // first state of a scan wave's group
 
   // Workgroups 0 .. n_full-1 run whole chains (chain = workgroup index; they
   // never wait).  The others are segments of the split chains and take their
@@ -155,12 +154,221 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   const bool dvalid = d < dim;
   const int64_t dc = dvalid ? d : dim - 1;      // tail lanes read a valid channel, never store
 
+  const int64_t seg_len_c = whole ? L : sh.seg_len;
+  const int64_t t_begin = static_cast<int64_t>(seg) * seg_len_c;
+  const int64_t t_end = (t_begin + seg_len_c < L) ? t_begin + seg_len_c : L;
+  const int n_chunks = static_cast<int>((t_end - t_begin + TC - 1) / TC);
+  const int64_t row0 = static_cast<int64_t>(b) * L;  // row of (b, t=0)
+  const int rec = chain * sh.n_seg + seg;
+  auto chunk_rows = [&](int c) -> int {
+    const int64_t r = t_end - (t_begin + static_cast<int64_t>(c) * TC);
+    return r <= 0 ? 0 : (r < TC ? static_cast<int>(r) : TC);
+  };
+
+  // =========================================================================
+  // Helper waves: stage the chunk tiles (phase P) and finish the outputs
+  // (phase E).  In the iteration where the scan waves run chunk c, the
+  // helpers finish chunk c-1, prepare chunk c+1 and issue the loads of chunk
+  // c+3 (two register sets, so every load has two chunk times to land).
+  // =========================================================================
+  struct Prefetch {
+    TileRun dt, uu, zz;
+    uint32_t bc[2][BCPT];
+  };
+  auto helper_loop = [&](bool out_mode) {
+    const int ptid = tid - 64 * NG;
+    const int tr = ptid / TPR;
+    const int tc = (ptid - tr * TPR) * EPT;
+    const int64_t tch = ch0 + tc;                       // first channel of the run
+    const bool run_valid = tch < dim;                   // any channel of the run inside
+    const int run_last = run_valid ? static_cast<int>((dim - 1 - tch) < (EPT - 1) ? (dim - 1 - tch)
+                                                                                  : (EPT - 1))
+                                   : 0;
+    // vector IO needs the whole run in range and aligned; the host guarantees
+    // alignment when sh.vec_io is set (dim % EPT == 0, aligned pointers)
+    const bool run_vec = TileRun::kCanVec && sh.vec_io != 0 && run_valid;
+    const int64_t tch_c = run_valid ? tch : (dim - 1);  // clamp for loads of dead runs
+    const bool use_sp = sh.softplus != 0;
+    const bool with_z = out_mode && sh.has_z;
+    float rD[EPT], rbias[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int64_t ck = tch_c + (k < run_last ? k : run_last);
+      rD[k] = sh.has_D ? Dv[ck] : 0.0f;
+      rbias[k] = sh.has_bias ? bias[ck] : 0.0f;
+    }
+
+    // loads of chunk c (clamped to the last chunk, so every iteration loads
+    // and consumes the same registers unconditionally)
+    auto load_p = [&](int c, Prefetch& pf) {
+      const int cc = c < n_chunks ? c : n_chunks - 1;
+      const int n = chunk_rows(cc);
+      const int64_t c0 = t_begin + static_cast<int64_t>(cc) * TC;
+      const int r = tr < n ? tr : n - 1;               // ragged chunk: clamp the row
+      const int64_t off = (row0 + c0 + r) * dim + tch_c;
+      if (run_vec) {
+        pf.dt.load_vec(dtp + off);
+        pf.uu.load_vec(u + off);
+        if (with_z) pf.zz.load_vec(zp + off);
+      } else {
+        pf.dt.load_elems(dtp + off, run_last);
+        pf.uu.load_elems(u + off, run_last);
+        if (with_z) pf.zz.load_elems(zp + off, run_last);
+      }
+      const int64_t base = (row0 + c0) * N;  // first B/C element of the chunk
+      if constexpr (kBCWords) {
+        const int nw = n * N * ESZ / 4;
+        const uint32_t* qb = reinterpret_cast<const uint32_t*>(Bm + base);
+        const uint32_t* qc = reinterpret_cast<const uint32_t*>(Cm + base);
+#pragma unroll
+        for (int k = 0; k < BCPT; ++k) {
+          const int e = ptid + k * PT;
+          const int ec = e < nw ? e : nw - 1;
+          pf.bc[0][k] = qb[ec];
+          if (out_mode) pf.bc[1][k] = qc[ec];
+        }
+      } else {
+        const int ne = n * N;
+#pragma unroll
+        for (int k = 0; k < BCPT; ++k) {
+          const int e = ptid + k * PT;
+          const int ec = e < ne ? e : ne - 1;
+          pf.bc[0][k] = static_cast<uint32_t>(Bm[base + ec]);
+          if (out_mode) pf.bc[1][k] = static_cast<uint32_t>(Cm[base + ec]);
+        }
+      }
+    };
+    auto bc_float = [&](uint32_t word, int half) -> float {
+      if constexpr (ESZ == 4) {
+        return __uint_as_float(word);
+      } else {
+        return __uint_as_float(half ? (word & 0xffff0000u) : (word << 16));
+      }
+    };
+    // Phase P of chunk c into LDS buffer c % 2: Delta, Delta*u (u with ZOH)
+    // and float B/C; D*u and z stay in this thread's registers until phase E.
+    // Every prefetched register is consumed unconditionally (only the LDS
+    // writes are predicated), so no load can still be counted as in flight
+    // when the registers are reloaded.
+    auto compute_p = [&](int c, const Prefetch& pf, float (&sk)[EPT], float (&zf)[EPT]) {
+      pf.dt.consume_all();
+      pf.uu.consume_all();
+      if (with_z) pf.zz.consume_all();
+#pragma unroll
+      for (int k = 0; k < BCPT; ++k) {
+        consume(pf.bc[0][k]);
+        if (out_mode) consume(pf.bc[1][k]);
+      }
+      const int n = chunk_rows(c);
+      const int buf = c & 1;
+      float dl[EPT], du[EPT];
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) {
+        const float uv = pf.uu.get(k);
+        const float s = pf.dt.get(k) + rbias[k];
+        dl[k] = use_sp ? softplus_f32(s) : s;
+        du[k] = ZOH ? uv : dl[k] * uv;
+        sk[k] = rD[k] * uv;
+        zf[k] = with_z ? pf.zz.get(k) : 0.0f;
+      }
+      if (tr < n) {
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+          s_delta[buf][tr][tc + k] = dl[k];
+          s_du[buf][tr][tc + k] = du[k];
+        }
+      }
+      float* sb = &s_B[buf][0][0];
+      float* scc = &s_C[buf][0][0];
+      if constexpr (kBCWords) {
+        const int nw = n * N * ESZ / 4;
+#pragma unroll
+        for (int k = 0; k < BCPT; ++k) {
+          const int e = ptid + k * PT;
+          const float b0 = bc_float(pf.bc[0][k], 0), b1 = bc_float(pf.bc[0][k], 1);
+          const float c0v = out_mode ? bc_float(pf.bc[1][k], 0) : 0.0f;
+          const float c1v = out_mode ? bc_float(pf.bc[1][k], 1) : 0.0f;
+          if (e < nw) {
+            if constexpr (ESZ == 4) {
+              sb[e] = b0;
+              if (out_mode) scc[e] = c0v;
+            } else {
+              sb[2 * e] = b0;
+              sb[2 * e + 1] = b1;
+              if (out_mode) {
+                scc[2 * e] = c0v;
+                scc[2 * e + 1] = c1v;
+              }
+            }
+          }
+        }
+      } else {
+        const int ne = n * N;
+#pragma unroll
+        for (int k = 0; k < BCPT; ++k) {
+          const int e = ptid + k * PT;
+          const float bv = to_f32(static_cast<T>(pf.bc[0][k]));
+          const float cv = out_mode ? to_f32(static_cast<T>(pf.bc[1][k])) : 0.0f;
+          if (e < ne) {
+            sb[e] = bv;
+            if (out_mode) scc[e] = cv;
+          }
+        }
+      }
+    };
+    // Phase E of chunk c: sum the NG partial readouts, add D*u, gate with
+    // SiLU(z), round and store this thread's run.
+    auto finish_e = [&](int c, const float (&sk)[EPT], const float (&zf)[EPT]) {
+      const int n = chunk_rows(c);
+      const int buf = c & 1;
+      if (tr < n && run_valid) {
+        float yv[EPT];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+          float y = s_y[buf][0][tr][tc + k];
+#pragma unroll
+          for (int q = 1; q < NG; ++q) y += s_y[buf][q][tr][tc + k];
+          y += sk[k];
+          if (sh.has_z) y = silu_gate(y, zf[k]);
+          yv[k] = y;
+        }
+        const int64_t c0 = t_begin + static_cast<int64_t>(c) * TC;
+        store_run<T, EPT>(out + (row0 + c0 + tr) * dim + tch, yv, run_vec, run_last);
+      }
+    };
+
+    Prefetch pf0, pf1;
+    float sk0[EPT], zf0[EPT], sk1[EPT], zf1[EPT];
+    load_p(0, pf0);
+    load_p(1, pf1);
+    compute_p(0, pf0, sk0, zf0);
+    load_p(2, pf0);
+    lds_barrier();
+    // iteration c (scan waves on chunk c): E(c-1), P(c+1), loads of c+3;
+    // chunk k uses register set k % 2
+    auto iter = [&](int c, Prefetch& pf, float (&sk)[EPT], float (&zf)[EPT]) {
+      if (out_mode && c >= 1) finish_e(c - 1, sk, zf);
+      compute_p(c + 1, pf, sk, zf);
+      load_p(c + 3, pf);
+      lds_barrier();
+    };
+    const int iters = out_mode ? n_chunks + 1 : n_chunks;
+    for (int c = 0; c < iters; c += 2) {
+      iter(c, pf1, sk1, zf1);
+      if (c + 1 < iters) iter(c + 1, pf0, sk0, zf0);
+    }
+  };
+
+  // =========================================================================
+  // Scan waves: the recurrence.  Lane = channel, registers = the wave's G
+  // states; B_t / C_t slices are LDS broadcasts.
+  // =========================================================================
   float A2[G], iA[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float av = A[dc * N + w * G + g];
+    const float av = scan_wave ? A[dc * N + gidx + g] : 0.0f;
     A2[g] = av * kLog2e;
-    iA[g] = ZOH ? 1.0f / av : 0.0f;
+    iA[g] = (ZOH && scan_wave) ? 1.0f / av : 0.0f;
   }
   // input term of state g: Delta*u*B (du holds Delta*u), or with ZOH
   // (exp(Delta A) - 1)/A * u*B (du holds u); x2 = Delta*A*log2 e, a = exp2(x2)
@@ -171,179 +379,23 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       return du * bv;
     }
   };
-  const bool use_sp = sh.softplus != 0;
 
-  // tile role of this thread in the P and E phases: row tr, channels tc..tc+EPT
-  const int tr = tid / TPR;
-  const int tc = (tid - tr * TPR) * EPT;
-  const int64_t tch = ch0 + tc;                       // first channel of the run
-  const bool run_valid = tch < dim;                   // any channel of the run inside
-  const int run_last = run_valid ? static_cast<int>((dim - 1 - tch) < (EPT - 1) ? (dim - 1 - tch)
-                                                                                : (EPT - 1))
-                                 : 0;
-  // vector IO needs the whole run in range and aligned; the host guarantees
-  // alignment when sh.vec_io is set (dim % EPT == 0, aligned pointers)
-  const bool run_vec = TileRun::kCanVec && sh.vec_io != 0 && run_valid;
-  const int64_t tch_c = run_valid ? tch : (dim - 1);  // clamp for loads of dead runs
-  float rD[EPT], rbias[EPT];
-#pragma unroll
-  for (int k = 0; k < EPT; ++k) {
-    const int64_t ck = tch_c + (k < run_last ? k : run_last);
-    rD[k] = sh.has_D ? Dv[ck] : 0.0f;
-    rbias[k] = sh.has_bias ? bias[ck] : 0.0f;
-  }
-
-  const int64_t seg_len_c = whole ? L : sh.seg_len;
-  const int64_t t_begin = static_cast<int64_t>(seg) * seg_len_c;
-  const int64_t t_end = (t_begin + seg_len_c < L) ? t_begin + seg_len_c : L;
-  const int64_t row0 = static_cast<int64_t>(b) * L;  // row of (b, t=0)
-  const int rec = chain * sh.n_seg + seg;
-
-  // ---- phase P: loads one chunk ahead, LDS operands after the scan --------
-  struct Prefetch {
-    TileRun dt, uu, zz;
-    uint32_t bc[2][BCPT];
-  };
-  auto load_p = [&](int64_t c0, int n, bool out_mode, Prefetch& pf) {
-    const int r = tr < n ? tr : n - 1;                 // ragged chunk: clamp the row
-    const int64_t off = (row0 + c0 + r) * dim + tch_c;
-    if (run_vec) {
-      pf.dt.load_vec(dtp + off);
-      pf.uu.load_vec(u + off);
-      if (out_mode && sh.has_z) pf.zz.load_vec(zp + off);
-    } else {
-      pf.dt.load_elems(dtp + off, run_last);
-      pf.uu.load_elems(u + off, run_last);
-      if (out_mode && sh.has_z) pf.zz.load_elems(zp + off, run_last);
-    }
-    const int64_t base = (row0 + c0) * N;  // first B/C element of the chunk
-    if constexpr (kBCWords) {
-      const int nw = n * N * ESZ / 4;
-      const uint32_t* qb = reinterpret_cast<const uint32_t*>(Bm + base);
-      const uint32_t* qc = reinterpret_cast<const uint32_t*>(Cm + base);
-#pragma unroll
-      for (int k = 0; k < BCPT; ++k) {
-        const int e = tid + k * NT;
-        const int ec = e < nw ? e : nw - 1;
-        pf.bc[0][k] = qb[ec];
-        if (out_mode) pf.bc[1][k] = qc[ec];
-      }
-    } else {
-      const int ne = n * N;
-#pragma unroll
-      for (int k = 0; k < BCPT; ++k) {
-        const int e = tid + k * NT;
-        const int ec = e < ne ? e : ne - 1;
-        pf.bc[0][k] = static_cast<uint32_t>(Bm[base + ec]);
-        if (out_mode) pf.bc[1][k] = static_cast<uint32_t>(Cm[base + ec]);
-      }
-    }
-  };
-  auto bc_float = [&](uint32_t word, int half) -> float {
-    if constexpr (ESZ == 4) {
-      return __uint_as_float(word);
-    } else {
-      return __uint_as_float(half ? (word & 0xffff0000u) : (word << 16));
-    }
-  };
-  // Every prefetched register is consumed unconditionally (only the LDS
-  // writes are predicated), so no load of this chunk can still be counted as
-  // in flight when the next chunk's loads reuse the registers.
-  // D*u and z of the chunk's tile run stay in the P/E thread's registers
-  // (sk, zf): the thread that prepares a run is the one that gates it.
-  auto compute_p = [&](int buf, int n, bool out_mode, const Prefetch& pf, float (&sk)[EPT],
-                       float (&zf)[EPT]) {
-    pf.dt.consume_all();
-    pf.uu.consume_all();
-    if (out_mode && sh.has_z) pf.zz.consume_all();
-#pragma unroll
-    for (int k = 0; k < BCPT; ++k) {
-      consume(pf.bc[0][k]);
-      if (out_mode) consume(pf.bc[1][k]);
-    }
-    float dl[EPT], du[EPT];
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      const float uv = pf.uu.get(k);
-      const float s = pf.dt.get(k) + rbias[k];
-      dl[k] = use_sp ? softplus_f32(s) : s;
-      du[k] = ZOH ? uv : dl[k] * uv;
-      sk[k] = rD[k] * uv;
-      zf[k] = (out_mode && sh.has_z) ? pf.zz.get(k) : 0.0f;
-    }
-    if (tr < n) {
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) {
-        s_delta[buf][tr][tc + k] = dl[k];
-        s_du[buf][tr][tc + k] = du[k];
-      }
-    }
-    float* sb = &s_B[buf][0][0];
-    float* scc = &s_C[buf][0][0];
-    if constexpr (kBCWords) {
-      const int nw = n * N * ESZ / 4;
-#pragma unroll
-      for (int k = 0; k < BCPT; ++k) {
-        const int e = tid + k * NT;
-        const float b0 = bc_float(pf.bc[0][k], 0), b1 = bc_float(pf.bc[0][k], 1);
-        const float c0v = out_mode ? bc_float(pf.bc[1][k], 0) : 0.0f;
-        const float c1v = out_mode ? bc_float(pf.bc[1][k], 1) : 0.0f;
-        if (e < nw) {
-          if constexpr (ESZ == 4) {
-            sb[e] = b0;
-            if (out_mode) scc[e] = c0v;
-          } else {
-            sb[2 * e] = b0;
-            sb[2 * e + 1] = b1;
-            if (out_mode) {
-              scc[2 * e] = c0v;
-              scc[2 * e + 1] = c1v;
-            }
-          }
-        }
-      }
-    } else {
-      const int ne = n * N;
-#pragma unroll
-      for (int k = 0; k < BCPT; ++k) {
-        const int e = tid + k * NT;
-        const float bv = to_f32(static_cast<T>(pf.bc[0][k]));
-        const float cv = out_mode ? to_f32(static_cast<T>(pf.bc[1][k])) : 0.0f;
-        if (e < ne) {
-          sb[e] = bv;
-          if (out_mode) scc[e] = cv;
-        }
-      }
-    }
-  };
-
-  // ---- aggregate pass: own final state from zero and sum of Delta --------
-  auto aggregate_pass = [&](float (&hA)[G], float& sum_delta) {
+  // aggregate pass of a look-back segment: own final state from zero and
+  // the sum of Delta (the helpers stage dt, u and B only)
+  auto scan_aggregate = [&](float (&hA)[G], float& sum_delta) {
 #pragma unroll
     for (int g = 0; g < G; ++g) hA[g] = 0.0f;
     sum_delta = 0.0f;
-    Prefetch pf;
-    float sk[EPT], zf[EPT];
-    int64_t c0 = t_begin;
-    int n0 = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
-    load_p(c0, n0, false, pf);
-    compute_p(0, n0, false, pf, sk, zf);
-    drain_vmem();
-    lds_barrier();
-    int buf = 0;
-    while (c0 < t_end) {
-      const int n = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
-      const int64_t c1 = c0 + n;
-      const int n1 = static_cast<int>((t_end - c1 < TC) ? t_end - c1 : TC);
-      // the last chunk reloads itself instead of skipping the prefetch, so
-      // loads and their consumption are unconditional in the loop body
-      load_p(n1 > 0 ? c1 : c0, n1 > 0 ? n1 : n, false, pf);
+    lds_barrier();  // helpers' prologue staged chunk 0
+    for (int c = 0; c < n_chunks; ++c) {
+      const int n = chunk_rows(c);
+      const int buf = c & 1;
       auto step = [&](int lt) {
         const float dl = s_delta[buf][lt][lane];
         const float du = s_du[buf][lt][lane];
         float bv[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) bv[g] = s_B[buf][lt][w * G + g];
+        for (int g = 0; g < G; ++g) bv[g] = s_B[buf][lt][gidx + g];
         sum_delta += dl;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -358,16 +410,13 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
       } else {
         for (int lt = 0; lt < n; ++lt) step(lt);
       }
-      compute_p(buf ^ 1, n1 > 0 ? n1 : 0, false, pf, sk, zf);
       lds_barrier();
-      buf ^= 1;
-      c0 = c1;
     }
   };
 
-  // ---- output pass: from carry-in h, produce out and the final state -----
-  // training mode: the state before every kBwdChunk-th step of the output
-  // pass goes to the backward's checkpoint array
+  // output pass: from carry-in h, produce the readout partials and the final
+  // state; in training mode the state before every kBwdChunk-th step goes to
+  // the backward's checkpoint array
   const bool ckpt_on = sc.ckpt != nullptr;
   float* const ckpt_c = ckpt_on ? sc.ckpt + static_cast<int64_t>(chain) * sh.n_ckpt * N * 64 : nullptr;
   auto save_ckpt = [&](int64_t t, const float (&hh)[G]) {
@@ -375,51 +424,16 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g) ckpt_c[(c * N + gidx + g) * 64 + lane] = hh[g];
   };
-
-  auto output_pass = [&](float (&h)[G]) {
-    Prefetch pf;
-    float sk[EPT], zf[EPT], sk_next[EPT], zf_next[EPT];
-    int64_t c0 = t_begin;
-    int n0 = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
-    load_p(c0, n0, true, pf);
-    compute_p(0, n0, true, pf, sk, zf);
-    drain_vmem();
-    lds_barrier();
-    int buf = 0;
-    while (c0 < t_end) {
-      const int n = static_cast<int>((t_end - c0 < TC) ? t_end - c0 : TC);
-      const int64_t c1 = c0 + n;
-      const int n1 = static_cast<int>((t_end - c1 < TC) ? t_end - c1 : TC);
-      // every global load of the iteration is issued here, one chunk ahead,
-      // and consumed by compute_p after the scan of the current chunk
-      load_p(n1 > 0 ? c1 : c0, n1 > 0 ? n1 : n, true, pf);
-      // phase S: the recurrence over the chunk, one step per time index; a
-      // ragged last chunk runs the plain loop below
-      auto step = [&](int lt) {
-        if (ckpt_on && (lt % kBwdChunk) == 0) save_ckpt(c0 + lt, h);
-        const float dl = s_delta[buf][lt][lane];
-        const float du = s_du[buf][lt][lane];
-        float bv[G], cv[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          bv[g] = s_B[buf][lt][w * G + g];
-          cv[g] = s_C[buf][lt][w * G + g];
-        }
-        float y = 0.0f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float x2 = dl * A2[g];
-          const float a = exp2_hw(x2);
-          h[g] = fmaf(a, h[g], input_term(g, dl, x2, a, du, bv[g]));
-          y = fmaf(cv[g], h[g], y);
-        }
-        s_y[w][lt][lane] = y;
-      };
+  auto scan_output = [&](float (&h)[G]) {
+    lds_barrier();  // helpers' prologue staged chunk 0
+    for (int c = 0; c < n_chunks; ++c) {
+      const int n = chunk_rows(c);
+      const int buf = c & 1;
+      const int64_t c0 = t_begin + static_cast<int64_t>(c) * TC;
       if (n == TC) {
         // software-pipelined: the LDS operands of step lt + PD are read while
         // step lt computes, and scheduling barriers keep the compiler from
-        // sinking the reads back next to their uses (about 2% over leaving
-        // the placement to the scheduler)
+        // sinking the reads back next to their uses
         constexpr int PD = 2;
         float pdl[PD + 1], pdu[PD + 1], pb[PD + 1][G], pc[PD + 1][G];
         auto rd = [&](int lt, int slot) {
@@ -427,8 +441,8 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
           pdu[slot] = s_du[buf][lt][lane];
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            pb[slot][g] = s_B[buf][lt][w * G + g];
-            pc[slot][g] = s_C[buf][lt][w * G + g];
+            pb[slot][g] = s_B[buf][lt][gidx + g];
+            pc[slot][g] = s_C[buf][lt][gidx + g];
           }
         };
 #pragma unroll
@@ -447,66 +461,28 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
             h[g] = fmaf(a, h[g], input_term(g, pdl[slot], x2, a, pdu[slot], pb[slot][g]));
             y = fmaf(pc[slot][g], h[g], y);
           }
-          s_y[w][lt][lane] = y;
+          s_y[buf][w][lt][lane] = y;
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        for (int lt = 0; lt < n; ++lt) step(lt);
-      }
-      lds_barrier();
-      compute_p(buf ^ 1, n1 > 0 ? n1 : 0, true, pf, sk_next, zf_next);
-      // phase E: this thread's run of the tile
-      if (tr < n && run_valid) {
-        float yv[EPT];
+        for (int lt = 0; lt < n; ++lt) {
+          if (ckpt_on && (lt % kBwdChunk) == 0) save_ckpt(c0 + lt, h);
+          const float dl = s_delta[buf][lt][lane];
+          const float du = s_du[buf][lt][lane];
+          float y = 0.0f;
 #pragma unroll
-        for (int k = 0; k < EPT; ++k) {
-          float y = s_y[0][tr][tc + k];
-#pragma unroll
-          for (int q = 1; q < NG; ++q) y += s_y[q][tr][tc + k];
-          y += sk[k];
-          if (sh.has_z) y = silu_gate(y, zf[k]);
-          yv[k] = y;
-        }
-        T* op = out + (row0 + c0 + tr) * dim + tch;
-        if (run_vec) {
-          TileRun o;
-#pragma unroll
-          for (int k = 0; k < TileRun::NW; ++k) o.w[k] = 0;
-#pragma unroll
-          for (int k = 0; k < EPT; ++k) {
-            T v;
-            store_act(&v, 0, yv[k]);
-            if constexpr (ESZ == 4) {
-              o.w[k] = __builtin_bit_cast(uint32_t, v);
-            } else {
-              o.w[k / 2] |= static_cast<uint32_t>(v) << (16 * (k % 2));
-            }
+          for (int g = 0; g < G; ++g) {
+            const float x2 = dl * A2[g];
+            const float a = exp2_hw(x2);
+            h[g] = fmaf(a, h[g], input_term(g, dl, x2, a, du, s_B[buf][lt][gidx + g]));
+            y = fmaf(s_C[buf][lt][gidx + g], h[g], y);
           }
-          uint32_t* q = reinterpret_cast<uint32_t*>(op);
-          if constexpr (TileRun::NW >= 4) {
-#pragma unroll
-            for (int i = 0; i < TileRun::NW; i += 4)
-              *reinterpret_cast<uint4*>(q + i) = make_uint4(o.w[i], o.w[i + 1], o.w[i + 2], o.w[i + 3]);
-          } else if constexpr (TileRun::NW == 2) {
-            *reinterpret_cast<uint2*>(q) = make_uint2(o.w[0], o.w[1]);
-          } else {
-            q[0] = o.w[0];
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < EPT; ++k)
-            if (k <= run_last) store_act(op, k, yv[k]);
+          s_y[buf][w][lt][lane] = y;
         }
       }
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) {
-        sk[k] = sk_next[k];
-        zf[k] = zf_next[k];
-      }
       lds_barrier();
-      buf ^= 1;
-      c0 = c1;
     }
+    lds_barrier();  // the helpers finish the last chunk
   };
 
   // ---- carry-in ------------------------------------------------------------
@@ -527,6 +503,14 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
     lds_barrier();
     pred_final = __builtin_amdgcn_readfirstlane(s_pred_final) != 0;
   }
+  const bool run_aggregate = seg != 0 && sh.lookback && !pred_final;
+
+  if (!scan_wave) {
+    if (run_aggregate) helper_loop(false);
+    helper_loop(true);
+    return;
+  }
+
   if (seg == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -548,7 +532,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
   } else {
     float hA[G];
     float sum_delta;
-    aggregate_pass(hA, sum_delta);
+    scan_aggregate(hA, sum_delta);
 #pragma unroll
     for (int g = 0; g < G; ++g) sc.agg_b[rec_state + (gidx + g) * 64 + lane] = hA[g];
     sc.agg_s[(static_cast<int64_t>(rec) * NG + w) * 64 + lane] = sum_delta;
@@ -637,7 +621,7 @@ __global__ __launch_bounds__(64 * NG) void scan_fwd_kernel(
     published = true;
   }
 
-  output_pass(h);
+  scan_output(h);
 
   if (!published && seg + 1 < nseg_c) {
 #pragma unroll
@@ -668,9 +652,10 @@ template <typename T, int NG, int G>
 static hipError_t launch_typed(const FwdPtrs& p, const FwdScratch& s, const FwdShape& sh,
                                int64_t workgroups, hipStream_t stream) {
   constexpr int TC = chunk_for_groups(NG);
-  const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * NG);
+  constexpr int NP = helper_waves(NG);
+  const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * (NG + NP));
 #define SSM_LAUNCH_FWD(Z)                                                                    \
-  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, TC, Z>), grid, block, 0, stream,              \
+  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, NP, TC, Z>), grid, block, 0, stream,          \
                      static_cast<const T*>(p.u), static_cast<const T*>(p.delta), p.A,         \
                      static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,             \
                      static_cast<const T*>(p.z), p.dt_bias, p.h0, static_cast<T*>(p.out),     \
@@ -709,7 +694,7 @@ static hipError_t dispatch_groups(int groups, int per_group, const FwdPtrs& p,
       if (groups == 8) return launch_typed<T, 8, 4>(p, s, sh, wg, st);
       break;
     case 64:
-      if (groups == 16) return launch_typed<T, 16, 4>(p, s, sh, wg, st);
+      if (groups == 8) return launch_typed<T, 8, 8>(p, s, sh, wg, st);
       break;
     default:
       break;

@@ -57,11 +57,16 @@ struct FwdPtrs {
   float* last_state;
 };
 
-// Chunk length (timesteps staged through LDS per step of the segment loop):
-// 32 for up to four state groups, 16 for eight or more (LDS holds the partial
-// readouts of every group).  Segments are a multiple of the largest chunk.
+// Forward workgroup shape: `groups` scan waves (one per state group) plus
+// four helper waves (one per SIMD) that stage the chunk tiles and finish the
+// outputs.  Chunk length (timesteps staged
+// through LDS per iteration): 32 for one or two state groups, 16 from four
+// on, where two workgroups of 8 waves must fit a CU's LDS (the tiles and the
+// partial readouts of every group are double buffered).  Segments are a
+// multiple of the largest chunk.
 constexpr int kChunk = 32;
-constexpr int chunk_for_groups(int groups) { return groups >= 8 ? 16 : 32; }
+constexpr int chunk_for_groups(int groups) { return groups >= 4 ? 16 : 32; }
+constexpr int helper_waves(int /*groups*/) { return 4; }
 
 // The forward is built once per activation type; each build lives in its own
 // namespace (fwd_f32, fwd_bf16) with the same interface:
