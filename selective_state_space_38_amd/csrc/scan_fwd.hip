@@ -91,7 +91,7 @@ __device__ __forceinline__ int wait_status(const int* p, int need, int limit) {
   return v;
 }
 
-template <typename T, int NG, int G, int NP, int TC, bool ZOH>
+template <typename T, int NG, int G, int NP, int TC, bool ZOH, bool VEC>
 __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     const T* __restrict__ u, const T* __restrict__ dtp,
     const float* __restrict__ A, const T* __restrict__ Bm,
@@ -160,6 +160,13 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
   const int n_chunks = static_cast<int>((t_end - t_begin + TC - 1) / TC);
   const int64_t row0 = static_cast<int64_t>(b) * L;  // row of (b, t=0)
   const int rec = chain * sh.n_seg + seg;
+  // Barrier-separated iterations of a pass after its prologue: one per chunk,
+  // plus one for the last chunk's outputs, rounded up to even (see the
+  // helpers' loop); both roles run exactly this many.
+  auto pass_iterations = [&](bool out_mode) -> int {
+    const int it = out_mode ? n_chunks + 1 : n_chunks;
+    return (it + 1) & ~1;
+  };
   auto chunk_rows = [&](int c) -> int {
     const int64_t r = t_end - (t_begin + static_cast<int64_t>(c) * TC);
     return r <= 0 ? 0 : (r < TC ? static_cast<int>(r) : TC);
@@ -184,12 +191,18 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     const int run_last = run_valid ? static_cast<int>((dim - 1 - tch) < (EPT - 1) ? (dim - 1 - tch)
                                                                                   : (EPT - 1))
                                    : 0;
-    // vector IO needs the whole run in range and aligned; the host guarantees
-    // alignment when sh.vec_io is set (dim % EPT == 0, aligned pointers)
-    const bool run_vec = TileRun::kCanVec && sh.vec_io != 0 && run_valid;
-    const int64_t tch_c = run_valid ? tch : (dim - 1);  // clamp for loads of dead runs
+    // VEC: the host guarantees whole aligned runs (dim % EPT == 0, aligned
+    // pointers).  Every lane then issues the same vector loads (dead runs past
+    // the last channel read the last run and store nothing), so the compiler
+    // can count the loads in flight exactly and wait only for the register
+    // set being consumed.
+    constexpr bool run_vec = VEC && TileRun::kCanVec;
+    const int64_t tch_c = run_valid ? tch : (run_vec ? dim - EPT : dim - 1);
     const bool use_sp = sh.softplus != 0;
     const bool with_z = out_mode && sh.has_z;
+    // without a gate the output pass still loads a z tile (u's, unused) so
+    // the loads in flight do not depend on it
+    const T* const zsrc = sh.has_z ? zp : u;
     float rD[EPT], rbias[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
@@ -206,14 +219,14 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
       const int64_t c0 = t_begin + static_cast<int64_t>(cc) * TC;
       const int r = tr < n ? tr : n - 1;               // ragged chunk: clamp the row
       const int64_t off = (row0 + c0 + r) * dim + tch_c;
-      if (run_vec) {
+      if constexpr (run_vec) {
         pf.dt.load_vec(dtp + off);
         pf.uu.load_vec(u + off);
-        if (with_z) pf.zz.load_vec(zp + off);
+        if (out_mode) pf.zz.load_vec(zsrc + off);
       } else {
         pf.dt.load_elems(dtp + off, run_last);
         pf.uu.load_elems(u + off, run_last);
-        if (with_z) pf.zz.load_elems(zp + off, run_last);
+        if (out_mode) pf.zz.load_elems(zsrc + off, run_last);
       }
       const int64_t base = (row0 + c0) * N;  // first B/C element of the chunk
       if constexpr (kBCWords) {
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     auto compute_p = [&](int c, const Prefetch& pf, float (&sk)[EPT], float (&zf)[EPT]) {
       pf.dt.consume_all();
       pf.uu.consume_all();
-      if (with_z) pf.zz.consume_all();
+      if (out_mode) pf.zz.consume_all();
 #pragma unroll
       for (int k = 0; k < BCPT; ++k) {
         consume(pf.bc[0][k]);
@@ -345,17 +358,20 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     load_p(2, pf0);
     lds_barrier();
     // iteration c (scan waves on chunk c): E(c-1), P(c+1), loads of c+3;
-    // chunk k uses register set k % 2
+    // chunk k uses register set k % 2.  The count is rounded up to even so
+    // both halves of the unrolled loop always run: with a conditional second
+    // half the compiler must assume the set consumed next was loaded just
+    // before, and waits for every outstanding load and store.
     auto iter = [&](int c, Prefetch& pf, float (&sk)[EPT], float (&zf)[EPT]) {
-      if (out_mode && c >= 1) finish_e(c - 1, sk, zf);
+      if (out_mode && c >= 1 && c <= n_chunks) finish_e(c - 1, sk, zf);
       compute_p(c + 1, pf, sk, zf);
       load_p(c + 3, pf);
       lds_barrier();
     };
-    const int iters = out_mode ? n_chunks + 1 : n_chunks;
+    const int iters = pass_iterations(out_mode);
     for (int c = 0; c < iters; c += 2) {
       iter(c, pf1, sk1, zf1);
-      if (c + 1 < iters) iter(c + 1, pf0, sk0, zf0);
+      iter(c + 1, pf0, sk0, zf0);
     }
   };
 
@@ -412,6 +428,7 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
       }
       lds_barrier();
     }
+    for (int c = n_chunks; c < pass_iterations(false); ++c) lds_barrier();
   };
 
   // output pass: from carry-in h, produce the readout partials and the final
@@ -482,7 +499,8 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
       }
       lds_barrier();
     }
-    lds_barrier();  // the helpers finish the last chunk
+    // the helpers finish the last chunk (and the rounding iteration)
+    for (int c = n_chunks; c < pass_iterations(true); ++c) lds_barrier();
   };
 
   // ---- carry-in ------------------------------------------------------------
@@ -654,16 +672,24 @@ static hipError_t launch_typed(const FwdPtrs& p, const FwdScratch& s, const FwdS
   constexpr int TC = chunk_for_groups(NG);
   constexpr int NP = helper_waves(NG);
   const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * (NG + NP));
-#define SSM_LAUNCH_FWD(Z)                                                                    \
-  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, NP, TC, Z>), grid, block, 0, stream,          \
+#define SSM_LAUNCH_FWD(Z, V)                                                                 \
+  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, NP, TC, Z, V>), grid, block, 0, stream,       \
                      static_cast<const T*>(p.u), static_cast<const T*>(p.delta), p.A,         \
                      static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,             \
                      static_cast<const T*>(p.z), p.dt_bias, p.h0, static_cast<T*>(p.out),     \
                      p.last_state, s, sh)
   if (sh.zoh) {
-    SSM_LAUNCH_FWD(true);
+    if (sh.vec_io) {
+      SSM_LAUNCH_FWD(true, true);
+    } else {
+      SSM_LAUNCH_FWD(true, false);
+    }
   } else {
-    SSM_LAUNCH_FWD(false);
+    if (sh.vec_io) {
+      SSM_LAUNCH_FWD(false, true);
+    } else {
+      SSM_LAUNCH_FWD(false, false);
+    }
   }
 #undef SSM_LAUNCH_FWD
   return hipGetLastError();

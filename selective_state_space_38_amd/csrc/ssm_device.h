@@ -29,17 +29,16 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(s) = max(s, 0) + log1p(e^-|s|).  log1p(e) is evaluated as
-// ln(w) * e / (w - 1) with w = 1 + e: w - 1 is exact, so the factor
-// e / (w - 1) undoes the rounding of 1 + e and keeps full relative accuracy
-// for tiny e (and gives e itself when w rounds to 1).
+// softplus(s) = max(s, 0) + log1p(e) with e = e^-|s| in (0, 1].  With
+// w = 1 + e rounded, r = e - (w - 1) is the rounding error exactly (w - 1 is
+// exact for w in [1, 2]), and log1p(e) = ln(w) + ln(1 + r/w) = ln(w) + r
+// up to r e / w <= 2^-24 e: full relative accuracy for tiny e (where w = 1
+// and the result is e itself) without a division.
 __device__ __forceinline__ float softplus_f32(float s) {
   const float e = exp2_hw(-fabsf(s) * kLog2e);
   const float w = 1.0f + e;
-  const float wm1 = w - 1.0f;
-  const float lw = log2_hw(w) * kLn2;
-  const float lp = (wm1 == 0.0f) ? e : lw * (e * rcp_hw(wm1));
-  return fmaxf(s, 0.0f) + lp;
+  const float r = e - (w - 1.0f);
+  return fmaxf(s, 0.0f) + fmaf(log2_hw(w), kLn2, r);
 }
 
 // Input coefficient of the exact zero-order-hold discretisation for a
