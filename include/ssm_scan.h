@@ -161,9 +161,11 @@ int selective_state_update_ex(float* state, const void* x, const void* dt,
  *   sum(dout * out) + sum(dlast * last_state)
  * with respect to every input, by the chain rule through the recurrence with
  * the adjoint state run backwards in time.  The intermediate states are not
- * stored: one state per 8-step chunk is kept in scratch and the states inside
- * a chunk are recomputed on chip (reading guide, Hardware-aware state
- * expansion; aigcdaily "Mamba：我们所知的ChatGPT时代的终结者？", Mamba block).
+ * stored: the forward's training mode (selective_scan_fwd_train, below) is
+ * run first into scratch, keeping one state per 8-step chunk and the readout
+ * before the gate, and the states inside a chunk are recomputed on chip
+ * (reading guide, Hardware-aware state expansion; aigcdaily "Mamba：我们所知的
+ * ChatGPT时代的终结者？", Mamba block).
  *   u, delta, A, B, C, D, z, dt_bias, softplus, h0 : the forward's inputs
  *   dout        : [B][L][D] of dtype, gradient of out
  *   dlast       : [B][D][N] float32 (nullable = zeros), gradient of last_state
@@ -175,7 +177,7 @@ int selective_state_update_ex(float* state, const void* x, const void* dt,
  *   dz          : [B][L][D] of dtype (nullable; must be NULL when z is NULL)
  *   dh0         : [B][D][N] float32 (nullable), gradient of the initial state
  * Outputs must not alias inputs or each other (SSM_EINVAL).  Scratch of
- * about 4*N*(64*B*ceil(D/64)*ceil(L/8) + 2*ceil(D/64)*B*L) bytes is allocated
+ * about ssm_ckpt_bytes(dims) + 8*N*ceil(D/64)*B*L bytes is allocated
  * stream-ordered and freed on the stream (SSM_ENOMEM on failure).  Sums over
  * channel blocks and batch rows are done in a fixed order (deterministic).
  */
@@ -272,7 +274,11 @@ int mamba_block_fwd(const void* x_in, const mamba_block_weights* weights, void* 
  *   ckpt : float32 device buffer of ssm_ckpt_bytes(dims) bytes holding the
  *          state before every 8th step of every (batch row, block of 64
  *          channels) -- one state per 8 steps, the backward's recompute
- *          granularity; its layout is internal to the library.
+ *          granularity -- and the readout before the gate, y = C.h + D u, of
+ *          every (batch row, step, channel) in float32 (the backward forms
+ *          dz from it); about (8 N / 8 + 4) bytes per token and channel.  Its
+ *          layout is internal to the library; 16-byte alignment lets the
+ *          kernels move it in vectors.
  * selective_scan_fwd_train is selective_scan_fwd_h0 (Delta*B input) that
  * also writes ckpt (which must not alias another argument); its out and
  * last_state are identical to selective_scan_fwd_h0's.

@@ -130,14 +130,25 @@ int check_dims(const ssm_dims* dims) {
   return SSM_OK;
 }
 
+// Bytes of the training mode's chunk-start states, and the offset of its
+// saved readouts (the rest of the checkpoint buffer).
+int64_t ckpt_state_bytes(const ssm_dims* dims) {
+  return dims->batch * div_up(dims->dim, 64) * div_up(dims->seqlen, ssm::kBwdChunk) *
+         dims->dstate * 64 * 4;
+}
+int64_t ckpt_y_offset(const ssm_dims* dims) { return div_up(ckpt_state_bytes(dims), 256) * 256; }
+
+// out may be NULL only for the backward's own forward pass (no_out), which
+// keeps just the checkpoint buffer.
 int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
              const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
              int bbar, void* out, float* last_state, float* ckpt, const ssm_dims* dims,
-             void* stream) {
+             void* stream, bool no_out = false) {
   int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
   if (bbar != SSM_BBAR_DELTA && bbar != SSM_BBAR_ZOH) return SSM_EINVAL;
-  if (!u || !delta || !A || !B || !C || !out) return SSM_EINVAL;
+  if (!u || !delta || !A || !B || !C || (!out && !no_out) || (no_out && !ckpt))
+    return SSM_EINVAL;
   const void* ptrs[] = {u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
   for (const void* p : ptrs)
     if (p && !aligned(p, 4)) return SSM_EALIGN;
@@ -181,6 +192,8 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sc.agg_s = reinterpret_cast<float*>(scratch + off_inc + inc_bytes + aggb_bytes);
   sc.spin_limit = env_int("SSM_TEST_SPIN_LIMIT", kDefaultSpinLimit);
   sc.ckpt = ckpt;
+  sc.ysave = ckpt ? reinterpret_cast<float*>(reinterpret_cast<char*>(ckpt) + ckpt_y_offset(dims))
+                  : nullptr;
 
   ssm::FwdShape sh;
   sh.seqlen = dims->seqlen;
@@ -208,6 +221,8 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     const void* acts[] = {u, delta, z, out};
     for (const void* a : acts)
       if (a && !aligned(a, need)) ok = false;
+    if (sc.ysave && !aligned(sc.ysave, static_cast<uintptr_t>(ept * 4 >= 16 ? 16 : ept * 4)))
+      ok = false;
     sh.vec_io = ok ? 1 : 0;
   }
 
@@ -295,19 +310,18 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const int64_t cblk = div_up(dims->dim, 64);
   const int64_t nck = div_up(dims->seqlen, ssm::kBwdChunk);
   auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
-  // Plan.  With the forward's checkpoints the state at any chunk start is
-  // known, so the chains beyond a multiple of the CU count can be split into
-  // segments that exchange only the adjoint carry (reverse look-back), as the
-  // forward does; without them every chain runs whole.
+  // Plan.  The state at any chunk start is known from the checkpoints, so
+  // the chains beyond a multiple of the CU count can be split into segments
+  // that exchange only the adjoint carry (reverse look-back), as the forward
+  // does.  With at most half as many chains as CUs (K = 0) every chain is
+  // split, into enough segments for ~4 workgroups per CU (measured best at
+  // the million-token shape: 64, 128, 256 segments per chain took 16.4,
+  // 10.4, 9.6 ms; with 192 chains, 130M, splitting measured slower);
+  // otherwise the remainder chains get ~one segment per CU (4 of 2, 3, 4, 8,
+  // 16 measured best at the 2.8B layer).  Segments are at least 512 steps.
   const int64_t chains = dims->batch * cblk;
   int64_t n_full = chains, n_seg = 1, seg_len = dims->seqlen;
-  if (ckpt_in) {
-    // With at most half as many chains as CUs (K = 0) every chain is split,
-    // into enough segments for ~4 workgroups per CU (measured best at the
-    // million-token shape: 64, 128, 256 segments per chain took 16.4, 10.4,
-    // 9.6 ms; with 192 chains, 130M, splitting measured slower); otherwise
-    // the remainder chains get ~one segment per CU (4 of 2, 3, 4, 8, 16
-    // measured best at the 2.8B layer).  Segments are at least 512 steps.
+  {
     const int64_t K = (chains / kComputeUnits) * kComputeUnits;
     const int64_t M = chains - K;
     int64_t S = M == 0 ? 1
@@ -322,7 +336,7 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
       kf = force_whole >= 0 && force_whole <= chains ? force_whole : K;
     }
     if (S > 1 && kf < chains) {
-      int64_t sl = div_up(div_up(dims->seqlen, S), ssm::kBwdFwdChunk) * ssm::kBwdFwdChunk;
+      int64_t sl = div_up(div_up(dims->seqlen, S), ssm::kBwdSegQuantum) * ssm::kBwdSegQuantum;
       if (force_split < 1 && sl < 512) sl = 512;
       if (div_up(dims->seqlen, sl) > 1) {
         n_full = kf;
@@ -333,7 +347,9 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   }
   const int64_t recs = (chains - n_full) * n_seg;
   const int64_t groups = bwd_groups(N);
-  const int64_t b_ckpt = ckpt_in ? 0 : up256(dims->batch * cblk * nck * N * 64 * 4);
+  // without the forward's checkpoint buffer, the backward runs the forward's
+  // training mode into scratch first
+  const int64_t b_ckpt = ckpt_in ? 0 : up256(ssm_ckpt_bytes(dims));
   const int64_t b_bc = up256(cblk * dims->batch * dims->seqlen * 2 * N * 4);
   const int64_t b_a = up256(dims->batch * n_seg * dims->dim * N * 4);
   const int64_t b_d = up256(dims->batch * n_seg * dims->dim * 4);
@@ -352,10 +368,18 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
       !scratch)
     return SSM_ENOMEM;
 
-  ssm::BwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, dout, dlast, ckpt_in, du, ddelta, dA,
-                 dB, dC, dD, dz, ddt_bias, dh0, nullptr, nullptr, nullptr, nullptr, nullptr};
-  // with the forward's checkpoints the backward skips its own forward pass
-  p.ckpt = ckpt_in ? const_cast<float*>(ckpt_in) : reinterpret_cast<float*>(scratch);
+  const float* ckpt = ckpt_in ? ckpt_in : reinterpret_cast<const float*>(scratch);
+  rc = SSM_OK;
+  if (!ckpt_in) {
+    rc = fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, SSM_BBAR_DELTA, nullptr,
+                  nullptr, reinterpret_cast<float*>(scratch), dims, stream, /*no_out=*/true);
+  }
+  const float* ysave =
+      reinterpret_cast<const float*>(reinterpret_cast<const char*>(ckpt) + ckpt_y_offset(dims));
+
+  ssm::BwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, dout, dlast, ckpt, ysave, du, ddelta,
+                 dA, dB, dC, dD, dz, ddt_bias, dh0, nullptr, nullptr, nullptr, nullptr,
+                 nullptr, nullptr, nullptr, nullptr, nullptr};
   p.part_bc = reinterpret_cast<float*>(scratch + b_ckpt);
   p.part_a = reinterpret_cast<float*>(scratch + b_ckpt + b_bc);
   p.part_d = reinterpret_cast<float*>(scratch + b_ckpt + b_bc + b_a);
@@ -387,23 +411,22 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.has_h0 = h0 != nullptr;
   sh.has_dlast = dlast != nullptr;
   {
-    // a run of ept channels may move as one vector when every run is whole
-    // and aligned
+    // the helpers' runs of ept = kBwdChunk / 4 channels may move as one
+    // vector when every run is whole and aligned (the saved readouts are
+    // float32 runs)
+    const int64_t ept = ssm::kBwdChunk / 4;
     const int64_t esz = dims->dtype == SSM_BF16 ? 2 : 4;
-    auto vec_ok = [&](int64_t ept) {
-      const uintptr_t need = static_cast<uintptr_t>(ept * esz >= 16 ? 16 : ept * esz);
-      bool ok = ept * esz >= 4 && dims->dim % ept == 0;
-      const void* acts[] = {u, delta, z, dout, du, ddelta, dz};
-      for (const void* a : acts)
-        if (a && !aligned(a, need)) ok = false;
-      return ok ? 1 : 0;
-    };
-    sh.vec_io = vec_ok(ssm::kBwdChunk / bwd_groups(N));
-    sh.vec_io_f = vec_ok(ssm::kBwdFwdChunk / bwd_groups(N));
+    const uintptr_t need = static_cast<uintptr_t>(ept * esz >= 16 ? 16 : ept * esz);
+    bool ok = ept * esz >= 4 && dims->dim % ept == 0 &&
+              aligned(ysave, static_cast<uintptr_t>(ept * 4 >= 16 ? 16 : ept * 4));
+    const void* acts[] = {u, delta, z, dout, du, ddelta, dz};
+    for (const void* a : acts)
+      if (a && !aligned(a, need)) ok = false;
+    sh.vec_io = ok ? 1 : 0;
   }
 
-  rc = SSM_OK;
-  if (ssm::launch_scan_bwd(dims->dtype, static_cast<int>(N), p, sh, st) != hipSuccess)
+  if (rc == SSM_OK && ssm::launch_scan_bwd(dims->dtype, static_cast<int>(N), p, sh, st) !=
+                          hipSuccess)
     rc = SSM_ELAUNCH;
   if (hipFreeAsync(scratch, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
   return rc;
@@ -584,8 +607,7 @@ int selective_scan_fwd_train(const void* u, const void* delta, const float* A, c
 int64_t ssm_ckpt_bytes(const ssm_dims* dims) {
   const int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
-  return dims->batch * div_up(dims->dim, 64) * div_up(dims->seqlen, ssm::kBwdChunk) *
-         dims->dstate * 64 * 4;
+  return ckpt_y_offset(dims) + dims->batch * dims->seqlen * dims->dim * 4;
 }
 
 int selective_state_update(float* state, const void* x, const void* dt, const float* A,

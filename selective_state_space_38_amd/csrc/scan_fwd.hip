@@ -335,18 +335,21 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
       const int n = chunk_rows(c);
       const int buf = c & 1;
       if (tr < n && run_valid) {
-        float yv[EPT];
+        float yv[EPT], yg[EPT];
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
           float y = s_y[buf][0][tr][tc + k];
 #pragma unroll
           for (int q = 1; q < NG; ++q) y += s_y[buf][q][tr][tc + k];
           y += sk[k];
-          if (sh.has_z) y = silu_gate(y, zf[k]);
           yv[k] = y;
+          yg[k] = sh.has_z ? silu_gate(y, zf[k]) : y;
         }
         const int64_t c0 = t_begin + static_cast<int64_t>(c) * TC;
-        store_run<T, EPT>(out + (row0 + c0 + tr) * dim + tch, yv, run_vec, run_last);
+        const int64_t o = (row0 + c0 + tr) * dim + tch;
+        if (out) store_run<T, EPT>(out + o, yg, run_vec, run_last);
+        // training mode: the readout before the gate, for the backward
+        if (sc.ysave) store_run<float, EPT>(sc.ysave + o, yv, run_vec, run_last);
       }
     };
 

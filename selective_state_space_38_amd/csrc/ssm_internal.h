@@ -25,6 +25,8 @@ struct FwdScratch {
   int spin_limit;    // bound on each carry wait (iterations of s_sleep)
   float* ckpt;       // nullable: [chains][n_ckpt][N][64] state before every
                      // kBwdChunk-th step, for the backward (training mode)
+  float* ysave;      // nullable: [batch][L][D] readout before the gate (y = C.h +
+                     // D u), for the backward (training mode)
 };
 
 struct FwdShape {
@@ -110,7 +112,9 @@ struct BwdPtrs {
   const float* h0;
   const void* dout;
   const float* dlast;
-  const float* ckpt_in;  // nullable: checkpoints written by the forward's training mode
+  // written by the forward's training mode on the same inputs
+  const float* ckpt;   // [batch * channel blocks][chunks][N][64] chunk-start states
+  const float* ysave;  // [batch][L][D] readout before the gate
   void* du;
   void* ddelta;
   float* dA;
@@ -121,7 +125,6 @@ struct BwdPtrs {
   float* ddt_bias;
   float* dh0;
   // scratch
-  float* ckpt;       // [batch * channel blocks][chunks][N][64] chunk-start states
   float* part_bc;    // [channel blocks][batch][L][2N] per-block dB | dC rows
   float* part_a;     // [batch][n_seg][dim][N] per-(batch, segment) dA
   float* part_d;     // [batch][n_seg][dim] per-(batch, segment) dD
@@ -142,17 +145,16 @@ struct BwdShape {
   int32_t chains;    // batch * channel blocks
   int32_t n_full;    // chains 0 .. n_full-1 run whole (workgroup = chain)
   int32_t n_seg;     // segments per split chain (1: no split)
-  int64_t seg_len;   // steps per segment of a split chain (multiple of kBwdFwdChunk)
+  int64_t seg_len;   // steps per segment of a split chain (multiple of kBwdSegQuantum)
   int32_t spin_limit;  // bound on each carry wait
   int64_t nchunks;   // ceil(seqlen / kBwdChunk)
   int32_t softplus;
   int32_t has_D, has_z, has_bias, has_h0, has_dlast;
-  int32_t vec_io;    // phase R runs (kBwdChunk / waves channels) may be vector moves
-  int32_t vec_io_f;  // phase F runs (kBwdFwdChunk / waves channels) may be vector moves
+  int32_t vec_io;    // the helpers' runs (kBwdChunk / 4 channels) may be vector moves
 };
 
-// Steps staged at a time by the backward's checkpointing forward phase.
-constexpr int kBwdFwdChunk = 32;
+// Segment lengths of the backward's split chains are multiples of this.
+constexpr int kBwdSegQuantum = 32;
 
 // Launches the backward kernel for (dtype, N) and the reductions over channel
 // blocks and batch.  Returns hipErrorInvalidValue for an unsupported N.

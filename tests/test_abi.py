@@ -192,8 +192,10 @@ def test_conv_validation():
 def test_training_pair_validation():
     lib = _lib.load()
     d = _dims(b=2, L=20, d=100, n=16)
-    # 2 rows x 2 channel blocks x ceil(20/8) checkpoints x 16 states x 64 lanes x 4 bytes
-    assert lib.ssm_ckpt_bytes(ctypes.byref(d)) == 2 * 2 * 3 * 16 * 64 * 4
+    # states: 2 rows x 2 channel blocks x ceil(20/8) checkpoints x 16 states x 64 lanes x
+    # 4 bytes, padded to 256 bytes; then the readouts: 2 x 20 x 100 float32
+    states = 2 * 2 * 3 * 16 * 64 * 4
+    assert lib.ssm_ckpt_bytes(ctypes.byref(d)) == -(-states // 256) * 256 + 2 * 20 * 100 * 4
     assert lib.ssm_ckpt_bytes(ctypes.byref(_dims(n=5))) == SSM_EINVAL
     rc = lib.selective_scan_fwd_train(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None,
                                       P[5], None, None, ctypes.byref(d), None)
