@@ -110,8 +110,9 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
   constexpr int BCPT = (BC_UNITS + PT - 1) / PT;          // B/C dwords (or elements) per thread
   using TileRun = Run<T, EPT>;
 
-  __shared__ float s_delta[2][TC][64];
-  __shared__ float s_du[2][TC][64];
+  // Delta and Delta*u (u with ZOH) side by side per channel: one 8-byte
+  // read per step
+  __shared__ __align__(16) float2 s_dd[2][TC][64];
   __shared__ __align__(16) float s_B[2][TC][N];
   __shared__ __align__(16) float s_C[2][TC][N];
   __shared__ __align__(16) float s_y[2][NG][TC][64];
@@ -139,6 +140,18 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     if (tid == 0) s_ticket = atomicAdd(sc.ticket, 1);
     __syncthreads();
     ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+  }
+  // Issue priority (the wave's own, for the SIMD's arbiter): the scan waves
+  // of whole chains are the critical path, their helpers next, the split
+  // chains' segments fill the gaps.
+  if (whole) {
+    if (scan_wave) {
+      __builtin_amdgcn_s_setprio(3);
+    } else {
+      __builtin_amdgcn_s_setprio(2);
+    }
+  } else if (scan_wave) {
+    __builtin_amdgcn_s_setprio(1);
   }
   const int n_split = sh.chains - sh.n_full;
   const int seg = whole ? 0 : ticket / n_split;
@@ -287,8 +300,7 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
       if (tr < n) {
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
-          s_delta[buf][tr][tc + k] = dl[k];
-          s_du[buf][tr][tc + k] = du[k];
+          s_dd[buf][tr][tc + k] = make_float2(dl[k], du[k]);
         }
       }
       float* sb = &s_B[buf][0][0];
@@ -410,8 +422,8 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
       const int n = chunk_rows(c);
       const int buf = c & 1;
       auto step = [&](int lt) {
-        const float dl = s_delta[buf][lt][lane];
-        const float du = s_du[buf][lt][lane];
+        const float2 dd = s_dd[buf][lt][lane];
+        const float dl = dd.x, du = dd.y;
         float bv[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) bv[g] = s_B[buf][lt][gidx + g];
@@ -457,8 +469,9 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
         constexpr int PD = 2;
         float pdl[PD + 1], pdu[PD + 1], pb[PD + 1][G], pc[PD + 1][G];
         auto rd = [&](int lt, int slot) {
-          pdl[slot] = s_delta[buf][lt][lane];
-          pdu[slot] = s_du[buf][lt][lane];
+          const float2 dd = s_dd[buf][lt][lane];
+          pdl[slot] = dd.x;
+          pdu[slot] = dd.y;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             pb[slot][g] = s_B[buf][lt][gidx + g];
@@ -487,8 +500,8 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
       } else {
         for (int lt = 0; lt < n; ++lt) {
           if (ckpt_on && (lt % kBwdChunk) == 0) save_ckpt(c0 + lt, h);
-          const float dl = s_delta[buf][lt][lane];
-          const float du = s_du[buf][lt][lane];
+          const float2 dd = s_dd[buf][lt][lane];
+          const float dl = dd.x, du = dd.y;
           float y = 0.0f;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
