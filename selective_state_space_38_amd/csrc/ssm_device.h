@@ -180,8 +180,11 @@ __device__ __forceinline__ void store_run(T* p, const float (&v)[EPT], bool vec,
 }
 
 // Sum over the four lanes of a quad (lanes 4i .. 4i+3), returned in all four,
-// with two DPP exchanges (quad_perm [1,0,3,2] then [2,3,0,1]).
+// with two DPP exchanges (quad_perm [1,0,3,2] then [2,3,0,1]).  Contraction is
+// off so that a product summed here stays a product plus a DPP add (two
+// v_add_f32_dpp); fused into an FMA, the exchange would need its own move.
 __device__ __forceinline__ float quad_sum(float v) {
+#pragma clang fp contract(off)
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
                                                           0xF, 0xF, true));
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
