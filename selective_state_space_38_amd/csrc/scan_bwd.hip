@@ -461,6 +461,9 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         for (int g = 0; g < G; ++g) {
           pB[g] = quad_sum(pB[g]);
           pC[g] = quad_sum(pC[g]);
+          // the sums are formed by every lane before the leaders' branch (if
+          // the adds sink into it, the DPP exchange can no longer fold into them)
+          asm volatile("" : : "v"(pB[g]), "v"(pC[g]));
         }
         if ((lane & 3) == 0) {
           const int q = lane >> 2;
