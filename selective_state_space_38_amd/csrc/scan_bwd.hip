@@ -68,8 +68,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
 
   // one chunk's staged inputs
   struct Tile {
-    float dl[TC][64];
-    float du[TC][64];
+    float2 dd[TC][64];         // Delta, Delta*u: one 8-byte read per step
     float dy[TC][64];
     float B[TC][N];
     float C[TC][N];
@@ -276,8 +275,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         v.dl[e] = ok ? dl : 0.0f;
         v.sig[e] = sh.softplus ? sigmoid_f32(s) : 1.0f;
         v.dy[e] = ok ? dyv : 0.0f;
-        tl.dl[tr][tc + e] = v.dl[e];
-        tl.du[tr][tc + e] = ok ? dl * uv : 0.0f;
+        tl.dd[tr][tc + e] = make_float2(v.dl[e], ok ? dl * uv : 0.0f);
         tl.dy[tr][tc + e] = v.dy[e];
         if (out_mode) dD_acc[e] = fmaf(v.dy[e], uv, dD_acc[e]);
       }
@@ -391,7 +389,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
       const Tile& tl = s_tile[k & 1];
 #pragma unroll
       for (int t = TC - 1; t >= 0; --t) {
-        const float dl = tl.dl[t][lane];
+        const float dl = tl.dd[t][lane].x;
         const float dyt = tl.dy[t][lane];
         sum_delta += dl;
 #pragma unroll
@@ -420,13 +418,15 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
       load_ck(k + 1, hnext);
       const Tile& tl = s_tile[k & 1];
       Red& rd = s_red[k % NRED];
-      float h[G], hs[TC][G], as[TC][G];
+      float h[G], hs[TC][G], as[TC][G], rdl[TC], rdu[TC];
 #pragma unroll
       for (int g = 0; g < G; ++g) h[g] = hstart[g];
 #pragma unroll
       for (int t = 0; t < TC; ++t) {
-        const float dl = tl.dl[t][lane];
-        const float du = tl.du[t][lane];
+        const float2 dd = tl.dd[t][lane];
+        const float dl = dd.x, du = dd.y;
+        rdl[t] = dl;   // kept for the adjoint
+        rdu[t] = du;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float a = exp2_hw(dl * A2[g]);
@@ -438,8 +438,8 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
       if constexpr (!kRed2) lds_barrier();  // the helpers have read the previous sums
 #pragma unroll
       for (int t = TC - 1; t >= 0; --t) {
-        const float dl = tl.dl[t][lane];
-        const float du = tl.du[t][lane];
+        const float dl = rdl[t];
+        const float du = rdu[t];
         const float dyt = tl.dy[t][lane];
         float s1 = 0.0f, s2 = 0.0f;
         float pB[G], pC[G];
@@ -461,11 +461,11 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         for (int g = 0; g < G; ++g) {
           pB[g] = quad_sum(pB[g]);
           pC[g] = quad_sum(pC[g]);
-          // the sums are formed by every lane before the leaders' branch (if
-          // the adds sink into it, the DPP exchange can no longer fold into them)
-          asm volatile("" : : "v"(pB[g]), "v"(pC[g]));
         }
-        if ((lane & 3) == 0) {
+        // the four lanes of a quad hold the same sums and store them to the
+        // same place (no branch on the lane; equal values, so whichever
+        // store lands last leaves the same result)
+        {
           const int q = lane >> 2;
           const int col = (w ^ swz(q)) * G;
 #pragma unroll
@@ -515,8 +515,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
     // wave has passed the passes' last barrier, so the tiles are free)
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      s_tile[0].dl[tr][tc + e] = dD_acc[e];
-      s_tile[0].du[tr][tc + e] = dbias_acc[e];
+      s_tile[0].dd[tr][tc + e] = make_float2(dD_acc[e], dbias_acc[e]);
     }
     lds_barrier();
     const int64_t pslot = static_cast<int64_t>(b) * sh.n_seg + slot;
@@ -524,8 +523,8 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
       float sd = 0.0f, sbias = 0.0f;
 #pragma unroll
       for (int t = 0; t < TC; ++t) {
-        sd += s_tile[0].dl[t][ptid];
-        sbias += s_tile[0].du[t][ptid];
+        sd += s_tile[0].dd[t][ptid].x;
+        sbias += s_tile[0].dd[t][ptid].y;
       }
       p.part_d[pslot * dim + ch0 + ptid] = sd;
       p.part_bias[pslot * dim + ch0 + ptid] = sbias;
