@@ -254,15 +254,16 @@ typedef struct {
  * Forward of one Mamba block:
  *   x, z  = x_in in_x, x_in in_z                      (rocBLAS GEMMs)
  *   u     = SiLU(causal_conv1d(x) + conv_b)            (causal_conv1d_fwd)
- *   dt_low, B, C = u x_dt, u x_B, u x_C;  dt = dt_low dt   (GEMMs)
+ *   dt_low, B, C = u x_dt, u x_B, u x_C;  dt = dt_low dt   (GEMMs; the three
+ *           projections of u run as one GEMM against [x_dt | x_B | x_C])
  *   y     = selective scan of u with Delta = softplus(dt + dt_bias), gated
  *           by SiLU(z)                                 (selective_scan_fwd)
  *   out   = y out                                      (GEMM)
  *   x_in, out : [batch][seqlen][d_model] of dtype; out must not alias x_in.
  * GEMMs accumulate in float32; intermediates are stored in dtype.  Scratch
- * for the intermediates (about (4 d_inner + dt_rank + 2 d_state) * batch *
- * seqlen elements of dtype) is allocated stream-ordered and freed on the
- * stream.  Normalisation and the residual connection are the caller's.
+ * for the intermediates (about (5 d_inner + dt_rank + 4 d_state) * batch *
+ * seqlen elements of dtype, plus a d_inner x (dt_rank + 2 d_state) copy of
+ * the x_proj weights) is allocated stream-ordered and freed on the stream.  Normalisation and the residual connection are the caller's.
  * Returns an ssm_status (SSM_ELAUNCH if rocBLAS fails).
  */
 int mamba_block_fwd(const void* x_in, const mamba_block_weights* weights, void* out,

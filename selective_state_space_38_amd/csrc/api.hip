@@ -512,10 +512,16 @@ int block_impl(const void* x_in, const mamba_block_weights* w, void* out,
 
   const int64_t esz = bd->dtype == SSM_BF16 ? 2 : 4;
   auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
+  // u feeds three projections (the low-rank dt, B, C): one GEMM against the
+  // side-by-side weights [x_dt | x_B | x_C] reads u once (each projection is
+  // HBM-bound on u); B and C are then copied out as the scan's contiguous
+  // [rows][N] operands
+  const int64_t nx = r + 2 * n;
   const int64_t b_act = up256(M * di * esz);
-  const int64_t b_low = up256(M * r * esz);
+  const int64_t b_xo = up256(M * nx * esz);
   const int64_t b_bc = up256(M * n * esz);
-  const int64_t total = 5 * b_act + b_low + 2 * b_bc;  // x, z, u, dt, y; dt_low; B, C
+  const int64_t b_wx = up256(di * nx * esz);
+  const int64_t total = 5 * b_act + b_xo + 2 * b_bc + b_wx;  // x, z, u, dt, y; x_proj; B, C
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (env_int("SSM_TEST_FAIL_ALLOC", 0) == 1) return SSM_ENOMEM;
   char* ws = nullptr;
@@ -528,9 +534,10 @@ int block_impl(const void* x_in, const mamba_block_weights* w, void* out,
   char* u = z + b_act;
   char* dt = u + b_act;
   char* y = dt + b_act;
-  char* low = y + b_act;
-  char* Bm = low + b_low;
+  char* xo = y + b_act;
+  char* Bm = xo + b_xo;
   char* Cm = Bm + b_bc;
+  char* wx = Cm + b_bc;
   const int dtype = bd->dtype;
 
   int rc = SSM_OK;
@@ -548,10 +555,24 @@ int block_impl(const void* x_in, const mamba_block_weights* w, void* out,
     rc = conv_fwd_impl(x, w->conv_w, w->conv_b, nullptr, bd->conv_width, 1, u, nullptr, &cd,
                        stream);
   }
-  gemm(M, r, di, u, w->x_dt, low);
-  gemm(M, n, di, u, w->x_B, Bm);
-  gemm(M, n, di, u, w->x_C, Cm);
-  gemm(M, di, r, low, w->dt, dt);
+  auto copy2d = [&](void* dst, int64_t dpitch, const void* src, int64_t spitch, int64_t width,
+                    int64_t height) {
+    if (rc == SSM_OK &&
+        hipMemcpy2DAsync(dst, static_cast<size_t>(dpitch), src, static_cast<size_t>(spitch),
+                         static_cast<size_t>(width), static_cast<size_t>(height),
+                         hipMemcpyDeviceToDevice, st) != hipSuccess)
+      rc = SSM_ELAUNCH;
+  };
+  copy2d(wx, nx * esz, w->x_dt, r * esz, r * esz, di);
+  copy2d(wx + r * esz, nx * esz, w->x_B, n * esz, n * esz, di);
+  copy2d(wx + (r + n) * esz, nx * esz, w->x_C, n * esz, n * esz, di);
+  gemm(M, nx, di, u, wx, xo);
+  copy2d(Bm, n * esz, xo + r * esz, nx * esz, n * esz, M);
+  copy2d(Cm, n * esz, xo + (r + n) * esz, nx * esz, n * esz, M);
+  // dt = dt_low W_dt with dt_low the first r columns of the x_proj output
+  if (rc == SSM_OK && ssm::gemm_rowmajor(dtype, M, di, r, xo, nx, w->dt, di, dt, di, st) !=
+                          hipSuccess)
+    rc = SSM_ELAUNCH;
   if (rc == SSM_OK) {
     ssm_dims sd{bd->batch, bd->seqlen, di, n, dtype};
     rc = fwd_impl(u, dt, w->A, Bm, Cm, w->D, z, w->dt_bias, 1, nullptr, SSM_BBAR_DELTA, y,
