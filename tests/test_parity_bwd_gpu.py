@@ -250,6 +250,22 @@ def test_training_pair_split_chains(split, whole, L):
     check_grads(got, ref, "f32")
 
 
+@pytest.mark.parametrize("n,tag", [(32, "f32"), (64, "f32"), (64, "bf16"), (8, "bf16")])
+def test_training_pair_split_other_state_counts(n, tag):
+    """The split backward with other state counts: 8 state groups (N = 32,
+    64; N = 64 keeps one partial-sum buffer and a mid-chunk barrier) and two
+    (N = 8), through the aggregate pass and the look-back."""
+    wl = "mamba130m" if tag == "f32" else "mamba2p8b"
+    x = synth.make(wl, batch=2, seqlen=300, dim=70, dstate=n, a_init="random")
+    g = _grads_in(x, tag, 40 + n)
+    _, ck = gpu_forward_train(x, tag, g)
+    _log(f"split bwd n{n} {tag}")
+    with env(SSM_FORCE_BWD_SPLIT=3, SSM_FORCE_BWD_WHOLE=1):
+        got = gpu_backward(x, tag, g, ckpt=ck)
+    ref = oracle_backward(x, g)
+    check_grads(got, ref, tag)
+
+
 def test_split_backward_without_dlast_and_h0():
     x = synth.make("mamba2p8b", batch=1, seqlen=400, dim=200, dstate=16, a_init="random")
     g = _grads_in(x, "bf16", 15, dlast=False, h0=False)
