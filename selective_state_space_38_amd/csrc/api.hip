@@ -127,6 +127,8 @@ int check_dims(const ssm_dims* dims) {
   const int64_t cblk = div_up(dims->dim, 64);
   if (dims->batch * cblk > (1LL << 30)) return SSM_EINVAL;
   if (dims->seqlen > (1LL << 31) - 1024) return SSM_EINVAL;
+  // the kernels address a chunk's rows with 32-bit offsets
+  if (dims->dim > (1LL << 24)) return SSM_EINVAL;
   return SSM_OK;
 }
 

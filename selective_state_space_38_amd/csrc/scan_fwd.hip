@@ -180,9 +180,11 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     const int it = out_mode ? n_chunks + 1 : n_chunks;
     return (it + 1) & ~1;
   };
+  // rows of chunk c: TC for all but the last chunk (32-bit, so the test stays
+  // in scalar registers)
+  const int last_rows = static_cast<int>(t_end - t_begin - static_cast<int64_t>(n_chunks - 1) * TC);
   auto chunk_rows = [&](int c) -> int {
-    const int64_t r = t_end - (t_begin + static_cast<int64_t>(c) * TC);
-    return r <= 0 ? 0 : (r < TC ? static_cast<int>(r) : TC);
+    return c < n_chunks - 1 ? TC : (c == n_chunks - 1 ? last_rows : 0);
   };
 
   // =========================================================================
@@ -195,7 +197,12 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     TileRun dt, uu, zz;
     uint32_t bc[2][BCPT];
   };
-  auto helper_loop = [&](bool out_mode) {
+  auto helper_loop = [&](auto out_c, auto fast_c) {
+    // OUT: the output pass (else the aggregate pass of a look-back segment).
+    // FAST: softplus on and, in the output pass, a gate: the layer's usual
+    // configuration, compiled without per-element selects on the flags.
+    constexpr bool OUT = decltype(out_c)::value;
+    constexpr bool FAST = decltype(fast_c)::value;
     const int ptid = tid - 64 * NG;
     const int tr = ptid / TPR;
     const int tc = (ptid - tr * TPR) * EPT;
@@ -211,8 +218,8 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     // set being consumed.
     constexpr bool run_vec = VEC && TileRun::kCanVec;
     const int64_t tch_c = run_valid ? tch : (run_vec ? dim - EPT : dim - 1);
-    const bool use_sp = sh.softplus != 0;
-    const bool with_z = out_mode && sh.has_z;
+    const bool use_sp = FAST || sh.softplus != 0;
+    const bool with_z = OUT && (FAST || sh.has_z);
     // without a gate the output pass still loads a z tile (u's, unused) so
     // the loads in flight do not depend on it
     const T* const zsrc = sh.has_z ? zp : u;
@@ -224,43 +231,59 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
       rbias[k] = sh.has_bias ? bias[ck] : 0.0f;
     }
 
+    // Addresses: a chunk base that is the same for the whole workgroup (kept
+    // in scalar registers) plus this thread's byte offset inside the chunk,
+    // computed once.  Rows past the end of a ragged last chunk are clamped to
+    // its last row.  The host keeps TC * dim * 4 bytes below 2^31.
+    const int cofs = static_cast<int>(tch_c - ch0);
+    const int dim32 = static_cast<int>(dim);
+    const int r_last = tr < last_rows ? tr : last_rows - 1;
+    const uint32_t el_full = static_cast<uint32_t>(tr * dim32 + cofs);
+    const uint32_t el_last = static_cast<uint32_t>(r_last * dim32 + cofs);
+    const uint32_t ob_full = el_full * ESZ, ob_last = el_last * ESZ;
+    auto chunk_el = [&](int c) -> int64_t {       // element (row of chunk c, channel ch0)
+      return (row0 + t_begin + static_cast<int64_t>(c) * TC) * dim + ch0;
+    };
+    // B/C: byte offsets of this thread's words (or elements) in a chunk's rows
+    uint32_t bo_full[BCPT], bo_last[BCPT];
+    {
+      constexpr int kUnit = kBCWords ? 4 : ESZ;
+      const int nu_full = kBCWords ? TC * N * ESZ / 4 : TC * N;
+      const int nu_last = kBCWords ? last_rows * N * ESZ / 4 : last_rows * N;
+#pragma unroll
+      for (int k = 0; k < BCPT; ++k) {
+        const int e = ptid + k * PT;
+        bo_full[k] = static_cast<uint32_t>((e < nu_full ? e : nu_full - 1) * kUnit);
+        bo_last[k] = static_cast<uint32_t>((e < nu_last ? e : nu_last - 1) * kUnit);
+      }
+    }
+
     // loads of chunk c (clamped to the last chunk, so every iteration loads
     // and consumes the same registers unconditionally)
     auto load_p = [&](int c, Prefetch& pf) {
       const int cc = c < n_chunks ? c : n_chunks - 1;
-      const int n = chunk_rows(cc);
-      const int64_t c0 = t_begin + static_cast<int64_t>(cc) * TC;
-      const int r = tr < n ? tr : n - 1;               // ragged chunk: clamp the row
-      const int64_t off = (row0 + c0 + r) * dim + tch_c;
+      const bool lastc = cc == n_chunks - 1;
+      const int64_t ce = chunk_el(cc);
+      const uint32_t ob = lastc ? ob_last : ob_full;
       if constexpr (run_vec) {
-        pf.dt.load_vec(dtp + off);
-        pf.uu.load_vec(u + off);
-        if (out_mode) pf.zz.load_vec(zsrc + off);
+        pf.dt.load_vec(add_bytes(dtp + ce, ob));
+        pf.uu.load_vec(add_bytes(u + ce, ob));
+        if constexpr (OUT) pf.zz.load_vec(add_bytes(zsrc + ce, ob));
       } else {
-        pf.dt.load_elems(dtp + off, run_last);
-        pf.uu.load_elems(u + off, run_last);
-        if (out_mode) pf.zz.load_elems(zsrc + off, run_last);
+        pf.dt.load_elems(add_bytes(dtp + ce, ob), run_last);
+        pf.uu.load_elems(add_bytes(u + ce, ob), run_last);
+        if constexpr (OUT) pf.zz.load_elems(add_bytes(zsrc + ce, ob), run_last);
       }
-      const int64_t base = (row0 + c0) * N;  // first B/C element of the chunk
-      if constexpr (kBCWords) {
-        const int nw = n * N * ESZ / 4;
-        const uint32_t* qb = reinterpret_cast<const uint32_t*>(Bm + base);
-        const uint32_t* qc = reinterpret_cast<const uint32_t*>(Cm + base);
+      const int64_t base = (row0 + t_begin + static_cast<int64_t>(cc) * TC) * N;  // first B/C element
 #pragma unroll
-        for (int k = 0; k < BCPT; ++k) {
-          const int e = ptid + k * PT;
-          const int ec = e < nw ? e : nw - 1;
-          pf.bc[0][k] = qb[ec];
-          if (out_mode) pf.bc[1][k] = qc[ec];
-        }
-      } else {
-        const int ne = n * N;
-#pragma unroll
-        for (int k = 0; k < BCPT; ++k) {
-          const int e = ptid + k * PT;
-          const int ec = e < ne ? e : ne - 1;
-          pf.bc[0][k] = static_cast<uint32_t>(Bm[base + ec]);
-          if (out_mode) pf.bc[1][k] = static_cast<uint32_t>(Cm[base + ec]);
+      for (int k = 0; k < BCPT; ++k) {
+        const uint32_t o = lastc ? bo_last[k] : bo_full[k];
+        if constexpr (kBCWords) {
+          pf.bc[0][k] = *add_bytes(reinterpret_cast<const uint32_t*>(Bm + base), o);
+          if constexpr (OUT) pf.bc[1][k] = *add_bytes(reinterpret_cast<const uint32_t*>(Cm + base), o);
+        } else {
+          pf.bc[0][k] = static_cast<uint32_t>(*add_bytes(Bm + base, o));
+          if constexpr (OUT) pf.bc[1][k] = static_cast<uint32_t>(*add_bytes(Cm + base, o));
         }
       }
     };
@@ -279,11 +302,11 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     auto compute_p = [&](int c, const Prefetch& pf, float (&sk)[EPT], float (&zf)[EPT]) {
       pf.dt.consume_all();
       pf.uu.consume_all();
-      if (out_mode) pf.zz.consume_all();
+      if constexpr (OUT) pf.zz.consume_all();
 #pragma unroll
       for (int k = 0; k < BCPT; ++k) {
         consume(pf.bc[0][k]);
-        if (out_mode) consume(pf.bc[1][k]);
+        if constexpr (OUT) consume(pf.bc[1][k]);
       }
       const int n = chunk_rows(c);
       const int buf = c & 1;
@@ -294,8 +317,10 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
         const float s = pf.dt.get(k) + rbias[k];
         dl[k] = use_sp ? softplus_f32(s) : s;
         du[k] = ZOH ? uv : dl[k] * uv;
-        sk[k] = rD[k] * uv;
-        zf[k] = with_z ? pf.zz.get(k) : 0.0f;
+        if constexpr (OUT) {
+          sk[k] = rD[k] * uv;
+          zf[k] = with_z ? pf.zz.get(k) : 0.0f;
+        }
       }
       if (tr < n) {
 #pragma unroll
@@ -311,16 +336,16 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
         for (int k = 0; k < BCPT; ++k) {
           const int e = ptid + k * PT;
           const float b0 = bc_float(pf.bc[0][k], 0), b1 = bc_float(pf.bc[0][k], 1);
-          const float c0v = out_mode ? bc_float(pf.bc[1][k], 0) : 0.0f;
-          const float c1v = out_mode ? bc_float(pf.bc[1][k], 1) : 0.0f;
+          const float c0v = OUT ? bc_float(pf.bc[1][k], 0) : 0.0f;
+          const float c1v = OUT ? bc_float(pf.bc[1][k], 1) : 0.0f;
           if (e < nw) {
             if constexpr (ESZ == 4) {
               sb[e] = b0;
-              if (out_mode) scc[e] = c0v;
+              if constexpr (OUT) scc[e] = c0v;
             } else {
               sb[2 * e] = b0;
               sb[2 * e + 1] = b1;
-              if (out_mode) {
+              if constexpr (OUT) {
                 scc[2 * e] = c0v;
                 scc[2 * e + 1] = c1v;
               }
@@ -333,16 +358,17 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
         for (int k = 0; k < BCPT; ++k) {
           const int e = ptid + k * PT;
           const float bv = to_f32(static_cast<T>(pf.bc[0][k]));
-          const float cv = out_mode ? to_f32(static_cast<T>(pf.bc[1][k])) : 0.0f;
+          const float cv = OUT ? to_f32(static_cast<T>(pf.bc[1][k])) : 0.0f;
           if (e < ne) {
             sb[e] = bv;
-            if (out_mode) scc[e] = cv;
+            if constexpr (OUT) scc[e] = cv;
           }
         }
       }
     };
     // Phase E of chunk c: sum the NG partial readouts, add D*u, gate with
     // SiLU(z), round and store this thread's run.
+    const uint32_t ob_f32 = el_full * 4u;
     auto finish_e = [&](int c, const float (&sk)[EPT], const float (&zf)[EPT]) {
       const int n = chunk_rows(c);
       const int buf = c & 1;
@@ -355,13 +381,12 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
           for (int q = 1; q < NG; ++q) y += s_y[buf][q][tr][tc + k];
           y += sk[k];
           yv[k] = y;
-          yg[k] = sh.has_z ? silu_gate(y, zf[k]) : y;
+          yg[k] = with_z ? silu_gate(y, zf[k]) : y;
         }
-        const int64_t c0 = t_begin + static_cast<int64_t>(c) * TC;
-        const int64_t o = (row0 + c0 + tr) * dim + tch;
-        if (out) store_run<T, EPT>(out + o, yg, run_vec, run_last);
+        const int64_t ce = chunk_el(c);
+        if (out) store_run<T, EPT>(add_bytes(out + ce, ob_full), yg, run_vec, run_last);
         // training mode: the readout before the gate, for the backward
-        if (sc.ysave) store_run<float, EPT>(sc.ysave + o, yv, run_vec, run_last);
+        if (sc.ysave) store_run<float, EPT>(add_bytes(sc.ysave + ce, ob_f32), yv, run_vec, run_last);
       }
     };
 
@@ -378,12 +403,14 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     // half the compiler must assume the set consumed next was loaded just
     // before, and waits for every outstanding load and store.
     auto iter = [&](int c, Prefetch& pf, float (&sk)[EPT], float (&zf)[EPT]) {
-      if (out_mode && c >= 1 && c <= n_chunks) finish_e(c - 1, sk, zf);
+      if constexpr (OUT) {
+        if (c >= 1 && c <= n_chunks) finish_e(c - 1, sk, zf);
+      }
       compute_p(c + 1, pf, sk, zf);
       load_p(c + 3, pf);
       lds_barrier();
     };
-    const int iters = pass_iterations(out_mode);
+    const int iters = pass_iterations(OUT);
     for (int c = 0; c < iters; c += 2) {
       iter(c, pf1, sk1, zf1);
       iter(c + 1, pf0, sk0, zf0);
@@ -540,8 +567,15 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
   const bool run_aggregate = seg != 0 && sh.lookback && !pred_final;
 
   if (!scan_wave) {
-    if (run_aggregate) helper_loop(false);
-    helper_loop(true);
+    using kOn = std::integral_constant<bool, true>;
+    using kOff = std::integral_constant<bool, false>;
+    if (sh.softplus != 0 && sh.has_z) {
+      if (run_aggregate) helper_loop(kOff{}, kOn{});
+      helper_loop(kOn{}, kOn{});
+    } else {
+      if (run_aggregate) helper_loop(kOff{}, kOff{});
+      helper_loop(kOn{}, kOff{});
+    }
     return;
   }
 

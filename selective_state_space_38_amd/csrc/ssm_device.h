@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -18,10 +20,27 @@ __device__ __forceinline__ float to_f32(bf16_t v) {
 }
 
 __device__ __forceinline__ void store_act(float* p, int64_t i, float v) { p[i] = v; }
+
+// Two floats rounded to bfloat16 (nearest even) and packed, lo in bits 0-15:
+// one v_cvt_pk_bf16_f32 on gfx950.
+typedef float f32x2_vt __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_vt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_vt v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_vt));
+}
 __device__ __forceinline__ void store_act(bf16_t* p, int64_t i, float v) {
   // gfx950 converts with round-to-nearest-even in one instruction.
   const __bf16 r = static_cast<__bf16>(v);
   p[i] = __builtin_bit_cast(bf16_t, r);
+}
+
+// p advanced by a byte offset held in 32 bits: with p the same for the whole
+// wave, the access can take the scalar-base + 32-bit vector-offset form.
+template <typename P>
+__device__ __forceinline__ P* add_bytes(P* p, uint32_t bytes) {
+  using C = typename std::conditional<std::is_const<P>::value, const char, char>::type;
+  return reinterpret_cast<P*>(reinterpret_cast<C*>(p) + bytes);
 }
 
 // Hardware transcendentals (v_exp_f32 / v_log_f32 / v_rcp_f32, base 2).
@@ -148,35 +167,32 @@ struct Run {
 template <typename T, int EPT>
 __device__ __forceinline__ void store_run(T* p, const float (&v)[EPT], bool vec, int last) {
   using R = Run<T, EPT>;
-  if (R::kCanVec && vec) {
-    R o;
-#pragma unroll
-    for (int i = 0; i < R::NW; ++i) o.w[i] = 0;
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      T t;
-      store_act(&t, 0, v[k]);
+  if constexpr (R::kCanVec) {
+    if (vec) {
+      R o;
       if constexpr (sizeof(T) == 4) {
-        o.w[k] = __builtin_bit_cast(uint32_t, t);
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) o.w[k] = __float_as_uint(v[k]);
       } else {
-        o.w[k / 2] |= static_cast<uint32_t>(t) << (16 * (k % 2));
+#pragma unroll
+        for (int i = 0; i < R::NW; ++i) o.w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
       }
-    }
-    uint32_t* q = reinterpret_cast<uint32_t*>(p);
-    if constexpr (R::NW >= 4) {
+      uint32_t* q = reinterpret_cast<uint32_t*>(p);
+      if constexpr (R::NW >= 4) {
 #pragma unroll
-      for (int i = 0; i < R::NW; i += 4)
-        *reinterpret_cast<uint4*>(q + i) = make_uint4(o.w[i], o.w[i + 1], o.w[i + 2], o.w[i + 3]);
-    } else if constexpr (R::NW == 2) {
-      *reinterpret_cast<uint2*>(q) = make_uint2(o.w[0], o.w[1]);
-    } else {
-      q[0] = o.w[0];
+        for (int i = 0; i < R::NW; i += 4)
+          *reinterpret_cast<uint4*>(q + i) = make_uint4(o.w[i], o.w[i + 1], o.w[i + 2], o.w[i + 3]);
+      } else if constexpr (R::NW == 2) {
+        *reinterpret_cast<uint2*>(q) = make_uint2(o.w[0], o.w[1]);
+      } else {
+        q[0] = o.w[0];
+      }
+      return;
     }
-  } else {
-#pragma unroll
-    for (int k = 0; k < EPT; ++k)
-      if (k <= last) store_act(p, k, v[k]);
   }
+#pragma unroll
+  for (int k = 0; k < EPT; ++k)
+    if (k <= last) store_act(p, k, v[k]);
 }
 
 // Sum over the four lanes of a quad (lanes 4i .. 4i+3), returned in all four,
