@@ -40,8 +40,9 @@
  *     h0 (zeros), last_state (not written).
  *   - Errors are reported only through the return value (an ssm_status);
  *     nothing is printed and nothing is thrown.  Argument validation happens
- *     on the host before any HIP call: dims must be > 0, dstate must be one of
- *     1, 2, 4, 8, 16, 32, 64, required pointers non-null, pointers 4-byte
+ *     on the host before any HIP call: dims must be > 0, dim at most 2^24
+ *     (the kernels address a chunk's rows with 32-bit offsets), dstate must
+ *     be one of 1, 2, 4, 8, 16, 32, 64, required pointers non-null, pointers 4-byte
  *     aligned, `out` must not alias an input.  A failed launch returns
  *     SSM_ELAUNCH; faults inside a kernel surface at the caller's next
  *     synchronisation, as for any HIP kernel.

@@ -125,6 +125,11 @@ def test_plan_query():
     # 320 chains on 256 CUs: 256 run whole, the other 64 are split
     assert plan.whole_chains == 256 and plan.segments == 4 and plan.lookback == 1
     assert lib.ssm_fwd_plan_for(ctypes.byref(_dims(n=5)), ctypes.byref(plan)) == SSM_EINVAL
+    # channel counts past 2^24 do not fit the kernels' 32-bit chunk offsets
+    assert lib.ssm_fwd_plan_for(ctypes.byref(_dims(b=1, L=16, d=1 << 24, n=16)),
+                                ctypes.byref(plan)) == SSM_OK
+    assert lib.ssm_fwd_plan_for(ctypes.byref(_dims(b=1, L=16, d=(1 << 24) + 64, n=16)),
+                                ctypes.byref(plan)) == SSM_EINVAL
 
 
 def test_plan_covers_every_supported_state_size():
