@@ -44,13 +44,16 @@
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
+
 namespace ssm {
 
 __device__ unsigned g_bwd_carry_timeouts;
 
 enum : int { kBwdEmpty = 0, kBwdAggregate = 1, kBwdInclusive = 2 };
 
-template <typename T, int NG, int G, int NP, int TC, bool VEC>
+// FAST: softplus on and a gate (the layer's usual configuration), compiled as
+// its own kernel so the helpers test neither flag per element.
+template <typename T, int NG, int G, int NP, int TC, bool VEC, bool FAST>
 // Up to four state groups, two workgroups must share a CU (whole chains plus
 // the split chains' segments): that caps the registers at 128.
 __global__ __launch_bounds__(64 * (NG + NP)) __attribute__((amdgpu_waves_per_eu(NG <= 4 ? 4 : 1)))
@@ -60,7 +63,8 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
   constexpr int NQ = 16;                       // quads per wave
   constexpr int EPT = TC / NP;                 // tile elements per helper thread
   constexpr int TPR = 64 / EPT;
-  constexpr int BCE = (TC * N + PT - 1) / PT;  // (t, n) pairs per helper thread
+  constexpr int BCE = (TC * N + PT - 1) / PT;  // B/C elements staged per helper thread
+  constexpr int ESZ = static_cast<int>(sizeof(T));
   static_assert(TC % NP == 0 && EPT >= 1 && 64 % EPT == 0, "tile must split over the helpers");
   static_assert(TC == kBwdChunk, "one chunk per checkpoint");
   using RunT = Run<T, EPT>;
@@ -142,10 +146,11 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
   const int n_chunks = static_cast<int>(c_hi - c_lo + 1);
   const int rec = whole ? 0 : (chain - sh.n_full) * sh.n_seg + seg;
   const int slot = whole ? 0 : seg;               // partial-sum slot of dA, dD, ddt_bias
-  auto chunk_rows = [&](int64_t c) -> int {
-    const int64_t r = L - c * TC;
-    return r < TC ? static_cast<int>(r) : TC;
-  };
+  // chunks sit on multiples of TC, so only the sequence's last chunk can be
+  // ragged
+  const int64_t c_rag = (L - 1) / TC;
+  const int rag_rows = static_cast<int>(L - c_rag * TC);
+  auto chunk_rows = [&](int64_t c) -> int { return c == c_rag ? rag_rows : TC; };
   // Barrier-separated iterations of a pass after its prologue: one per chunk
   // (plus one for the last chunk's finish in the output pass), rounded up to
   // even so both halves of the helpers' unrolled loop always run; both roles
@@ -183,7 +188,23 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
   constexpr bool run_vec = VEC && RunT::kCanVec;
   const int64_t tch_c = run_valid ? tch : (run_vec ? dim - EPT : dim - 1);
 
-  auto helper_loop = [&](bool out_mode) {
+  // dB / dC rows: the TC*N (t, n) pairs of a chunk over the helper threads,
+  // SPL lanes per pair (each adds NQ/SPL of the quad sums, then one or two
+  // DPP exchanges join them) when there are fewer pairs than threads, else
+  // PPT pairs per thread, so every helper wave does the same share
+  constexpr int NPAIR = TC * N;
+  constexpr int SPL = NPAIR >= PT ? 1 : (PT / NPAIR >= 4 ? 4 : PT / NPAIR);
+  constexpr int PPT = NPAIR >= PT ? NPAIR / PT : 1;
+  constexpr int QPL = NQ / SPL;
+  static_assert(NPAIR < PT || NPAIR % PT == 0, "pairs must split evenly over the helpers");
+
+  auto helper_loop = [&](auto out_c) {
+    // OUT: the output pass (else the aggregate pass of a split segment)
+    constexpr bool OUT = decltype(out_c)::value;
+    using kOn = std::integral_constant<bool, true>;
+    using kOff = std::integral_constant<bool, false>;
+    const bool use_sp = FAST || sh.softplus != 0;
+    const bool has_z = FAST || sh.has_z != 0;
     float rD[EPT], rbias[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
@@ -191,7 +212,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
       rD[k] = sh.has_D ? p.D[ck] : 0.0f;
       rbias[k] = sh.has_bias ? p.dt_bias[ck] : 0.0f;
     }
-    const T* const zsrc = sh.has_z ? xz : xu;  // without a gate: u's tile, unused
+    const T* const zsrc = has_z ? xz : xu;  // without a gate: u's tile, unused
     auto raw_bits = [](T v) -> uint32_t {
       if constexpr (sizeof(T) == 4) {
         return __builtin_bit_cast(uint32_t, v);
@@ -199,34 +220,55 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         return static_cast<uint32_t>(v);
       }
     };
+    // Addresses: a chunk base that is the same for the whole workgroup (kept
+    // in scalar registers) plus this thread's byte offset inside the chunk,
+    // computed once; rows past the end of the ragged last chunk are clamped
+    // to its last row.  The host keeps TC * dim * 4 bytes below 2^31.
+    const int cofs = static_cast<int>(tch_c - ch0);
+    const int dim32 = static_cast<int>(dim);
+    const int r_rag = tr < rag_rows ? tr : rag_rows - 1;
+    const uint32_t el_full = static_cast<uint32_t>(tr * dim32 + cofs);
+    const uint32_t el_rag = static_cast<uint32_t>(r_rag * dim32 + cofs);
+    const uint32_t ob_full = el_full * ESZ, ob_rag = el_rag * ESZ;
+    const uint32_t of_full = el_full * 4u, of_rag = el_rag * 4u;
+    auto chunk_el = [&](int64_t c) -> int64_t { return (row0 + c * TC) * dim + ch0; };
+    uint32_t bo_full[BCE], bo_rag[BCE];
+#pragma unroll
+    for (int j = 0; j < BCE; ++j) {
+      const int e = ptid + j * PT;
+      bo_full[j] = static_cast<uint32_t>((e < TC * N ? e : 0) * ESZ);
+      bo_rag[j] = static_cast<uint32_t>((e < rag_rows * N ? e : 0) * ESZ);
+    }
+    // every run of this wave whole and inside dim: full chunks need no
+    // per-element masks
+    const bool wave_runs_ok = __all(run_valid && run_last == EPT - 1);
+
     // loads of pass chunk k (clamped to the pass, so every iteration loads
     // and consumes the same registers)
     auto load = [&](int k, Raw& r) {
       const int64_t c = c_hi - (k < n_chunks ? k : n_chunks - 1);
-      const int64_t c0 = c * TC;
-      const int n = chunk_rows(c);
-      const int rr = tr < n ? tr : n - 1;
-      const int64_t off = (row0 + c0 + rr) * dim + tch_c;
+      const bool rag = c == c_rag;
+      const int64_t ce = chunk_el(c);
+      const uint32_t ob = rag ? ob_rag : ob_full;
       if constexpr (run_vec) {
-        r.dt.load_vec(xdt + off);
-        r.u.load_vec(xu + off);
-        r.z.load_vec(zsrc + off);
-        r.dout.load_vec(xdo + off);
-        if (out_mode) r.y.load_vec(p.ysave + off);
+        r.dt.load_vec(add_bytes(xdt + ce, ob));
+        r.u.load_vec(add_bytes(xu + ce, ob));
+        r.z.load_vec(add_bytes(zsrc + ce, ob));
+        r.dout.load_vec(add_bytes(xdo + ce, ob));
+        if constexpr (OUT) r.y.load_vec(add_bytes(p.ysave + ce, rag ? of_rag : of_full));
       } else {
-        r.dt.load_elems(xdt + off, run_last);
-        r.u.load_elems(xu + off, run_last);
-        r.z.load_elems(zsrc + off, run_last);
-        r.dout.load_elems(xdo + off, run_last);
-        if (out_mode) r.y.load_elems(p.ysave + off, run_last);
+        r.dt.load_elems(add_bytes(xdt + ce, ob), run_last);
+        r.u.load_elems(add_bytes(xu + ce, ob), run_last);
+        r.z.load_elems(add_bytes(zsrc + ce, ob), run_last);
+        r.dout.load_elems(add_bytes(xdo + ce, ob), run_last);
+        if constexpr (OUT) r.y.load_elems(add_bytes(p.ysave + ce, rag ? of_rag : of_full), run_last);
       }
-      const int64_t base = (row0 + c0) * N;
+      const int64_t base = (row0 + c * TC) * N;
 #pragma unroll
       for (int j = 0; j < BCE; ++j) {
-        const int e = ptid + j * PT;
-        const int64_t ec = base + ((e < n * N) ? e : 0);
-        r.bb[j] = raw_bits(xB[ec]);
-        r.cc[j] = raw_bits(xC[ec]);
+        const uint32_t o = rag ? bo_rag[j] : bo_full[j];
+        r.bb[j] = raw_bits(*add_bytes(xB + base, o));
+        r.cc[j] = raw_bits(*add_bytes(xC + base, o));
       }
     };
     auto to_float = [&](uint32_t v) -> float {
@@ -236,19 +278,11 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         return __uint_as_float(v << 16);
       }
     };
-    // stage pass chunk k into tile k % 2 (nothing past the pass's chunks);
-    // the output pass also forms dz and stores it
-    auto stage = [&](int k, const Raw& r, Vals& v) {
-      r.dt.consume_all();
-      r.u.consume_all();
-      r.z.consume_all();
-      r.dout.consume_all();
-      if (out_mode) r.y.consume_all();
-#pragma unroll
-      for (int j = 0; j < BCE; ++j) {
-        consume(r.bb[j]);
-        consume(r.cc[j]);
-      }
+    // stage pass chunk k into tile k % 2 (zeros past the pass's chunks); the
+    // output pass also forms dz and stores it.  ALLOK: a full chunk and every
+    // run of the wave inside dim, so no element needs masking.
+    auto stage = [&](int k, const Raw& r, Vals& v, auto allok_c) {
+      constexpr bool ALLOK = decltype(allok_c)::value;
       const bool live = k < n_chunks;
       const int64_t c = c_hi - (live ? k : 0);
       const int n = live ? chunk_rows(c) : 0;
@@ -258,48 +292,71 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
       for (int e = 0; e < EPT; ++e) {
         // only channels inside dim are live: the lanes past it must add
         // nothing to the sums over channels (dB, dC)
-        const bool ok = tr < n && run_valid && e <= run_last;
+        const bool ok = ALLOK || (tr < n && run_valid && e <= run_last);
         const float s = r.dt.get(e) + rbias[e];
-        const float dl = sh.softplus ? softplus_f32(s) : s;
+        float dl = s, sg_s = 1.0f;
+        if (use_sp) dl = softplus_sigmoid(s, sg_s);
         const float uv = r.u.get(e);
         const float go = r.dout.get(e);
         float dyv = go;
         dzv[e] = 0.0f;
-        if (sh.has_z) {
+        if (has_z) {
           const float zv = r.z.get(e);
           const float sg = sigmoid_f32(zv);
           dyv = go * (zv * sg);
-          if (out_mode) dzv[e] = go * r.y.get(e) * (sg * fmaf(zv, 1.0f - sg, 1.0f));
+          if constexpr (OUT) dzv[e] = go * r.y.get(e) * (sg * fmaf(zv, 1.0f - sg, 1.0f));
         }
         v.u[e] = uv;
         v.dl[e] = ok ? dl : 0.0f;
-        v.sig[e] = sh.softplus ? sigmoid_f32(s) : 1.0f;
+        v.sig[e] = sg_s;
         v.dy[e] = ok ? dyv : 0.0f;
         tl.dd[tr][tc + e] = make_float2(v.dl[e], ok ? dl * uv : 0.0f);
         tl.dy[tr][tc + e] = v.dy[e];
-        if (out_mode) dD_acc[e] = fmaf(v.dy[e], uv, dD_acc[e]);
+        if constexpr (OUT) dD_acc[e] = fmaf(v.dy[e], uv, dD_acc[e]);
       }
 #pragma unroll
       for (int j = 0; j < BCE; ++j) {
         const int e = ptid + j * PT;
         if (e < TC * N) {
-          tl.B[e / N][e % N] = e < n * N ? to_float(r.bb[j]) : 0.0f;
-          tl.C[e / N][e % N] = e < n * N ? to_float(r.cc[j]) : 0.0f;
+          const bool in = ALLOK || e < n * N;
+          tl.B[e / N][e % N] = in ? to_float(r.bb[j]) : 0.0f;
+          tl.C[e / N][e % N] = in ? to_float(r.cc[j]) : 0.0f;
         }
       }
-      if (out_mode && sh.has_z && gdz && tr < n && run_valid)
-        store_run<T, EPT>(gdz + (row0 + c * TC + tr) * dim + tch, dzv, run_vec, run_last);
+      if constexpr (OUT) {
+        if (has_z && gdz && (ALLOK || (tr < n && run_valid)))
+          store_run<T, EPT>(add_bytes(gdz + chunk_el(c), ob_full), dzv, run_vec, run_last);
+      }
+    };
+    auto stage_any = [&](int k, const Raw& r, Vals& v) {
+      r.dt.consume_all();
+      r.u.consume_all();
+      r.z.consume_all();
+      r.dout.consume_all();
+      if constexpr (OUT) r.y.consume_all();
+#pragma unroll
+      for (int j = 0; j < BCE; ++j) {
+        consume(r.bb[j]);
+        consume(r.cc[j]);
+      }
+      if constexpr (FAST) {
+        if (wave_runs_ok && k < n_chunks && c_hi - k != c_rag) {
+          stage(k, r, v, kOn{});
+          return;
+        }
+      }
+      stage(k, r, v, kOff{});
     };
     // finish pass chunk k from partial-sum buffer k % NRED
-    auto finish = [&](int k, const Vals& v) {
+    auto finish = [&](int k, const Vals& v, auto allok_c) {
+      constexpr bool ALLOK = decltype(allok_c)::value;
       const int64_t c = c_hi - k;
-      const int64_t c0 = c * TC;
       const int n = chunk_rows(c);
       const Red& rd = s_red[k % NRED];
       float duv[EPT], ddv[EPT];
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
-        const bool ok = tr < n && run_valid && e <= run_last;
+        const bool ok = ALLOK || (tr < n && run_valid && e <= run_last);
         float S1 = rd.p1[0][tr][tc + e];
         float S2 = rd.p2[0][tr][tc + e];
 #pragma unroll
@@ -311,53 +368,74 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         ddv[e] = fmaf(v.u[e], S1, S2) * v.sig[e];
         dbias_acc[e] += ok ? ddv[e] : 0.0f;
       }
-      if (tr < n && run_valid) {
-        const int64_t o = (row0 + c0 + tr) * dim + tch;
-        store_run<T, EPT>(gdu + o, duv, run_vec, run_last);
-        store_run<T, EPT>(gddl + o, ddv, run_vec, run_last);
+      if (ALLOK || (tr < n && run_valid)) {
+        const int64_t ce = chunk_el(c);
+        store_run<T, EPT>(add_bytes(gdu + ce, ob_full), duv, run_vec, run_last);
+        store_run<T, EPT>(add_bytes(gddl + ce, ob_full), ddv, run_vec, run_last);
       }
-      // this channel block's dB / dC rows: add the 16 quad sums
-      float* part_bc = p.part_bc + (static_cast<int64_t>(cblk) * bsz + b) * L * (2 * N);
+      // this channel block's dB / dC rows: add the 16 quad sums of each pair
+      float* const part_bc =
+          p.part_bc + ((static_cast<int64_t>(cblk) * bsz + b) * L + c * TC) * (2 * N);
 #pragma unroll
-      for (int j = 0; j < BCE; ++j) {
-        const int e = ptid + j * PT;
-        if (e < TC * N) {
-          const int row = e / N;
-          const int nn = e - row * N;
+      for (int j = 0; j < PPT; ++j) {
+        const int pr = SPL > 1 ? ptid / SPL : ptid + j * PT;
+        const int part = SPL > 1 ? ptid % SPL : 0;
+        if (pr < NPAIR) {
+          const int row = pr / N;
+          const int nn = pr - row * N;
           const int grp = nn / G, gi = nn - grp * G;
           float sb = 0.0f, scv = 0.0f;
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) {
+          for (int qq = 0; qq < QPL; ++qq) {
+            const int q = part * QPL + qq;
             const int col = ((grp ^ swz(q)) * G) + gi;
             sb += rd.rB[row][q][col];
             scv += rd.rC[row][q][col];
           }
-          if (row < n) {
-            float* pr = part_bc + (c0 + row) * (2 * N);
-            pr[nn] = sb;
-            pr[N + nn] = scv;
+          if constexpr (SPL == 2) {
+            sb = pair_sum(sb);
+            scv = pair_sum(scv);
+          } else if constexpr (SPL == 4) {
+            sb = quad_sum(sb);
+            scv = quad_sum(scv);
+          }
+          if (part == 0 && (ALLOK || row < n)) {
+            float* const prow = part_bc + row * (2 * N);
+            prow[nn] = sb;
+            prow[N + nn] = scv;
           }
         }
       }
+    };
+    auto finish_any = [&](int k, const Vals& v) {
+      if constexpr (FAST) {
+        if (wave_runs_ok && c_hi - k != c_rag) {
+          finish(k, v, kOn{});
+          return;
+        }
+      }
+      finish(k, v, kOff{});
     };
 
     Raw r0, r1;
     Vals v0, v1;
     load(0, r0);
     load(1, r1);
-    stage(0, r0, v0);
+    stage_any(0, r0, v0);
     load(2, r0);
     lds_barrier();
     // iteration k (scan waves on pass chunk k): finish k - 1, stage k + 1,
     // loads of k + 3; pass chunk j uses register sets r(j % 2), v(j % 2)
     auto iter = [&](int k, Raw& r, Vals& v) {
-      if (out_mode && k >= 1 && k <= n_chunks) finish(k - 1, v);
-      if (!kRed2 && out_mode) lds_barrier();  // the partial sums are free again
-      stage(k + 1, r, v);
+      if constexpr (OUT) {
+        if (k >= 1 && k <= n_chunks) finish_any(k - 1, v);
+        if (!kRed2) lds_barrier();  // the partial sums are free again
+      }
+      stage_any(k + 1, r, v);
       load(k + 3, r);
       lds_barrier();
     };
-    const int iters = pass_iterations(out_mode);
+    const int iters = pass_iterations(OUT);
     for (int k = 0; k < iters; k += 2) {
       iter(k, r1, v1);
       iter(k + 1, r0, v0);
@@ -418,15 +496,13 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
       load_ck(k + 1, hnext);
       const Tile& tl = s_tile[k & 1];
       Red& rd = s_red[k % NRED];
-      float h[G], hs[TC][G], as[TC][G], rdl[TC], rdu[TC];
+      float h[G], hs[TC][G], as[TC][G];
 #pragma unroll
       for (int g = 0; g < G; ++g) h[g] = hstart[g];
 #pragma unroll
       for (int t = 0; t < TC; ++t) {
         const float2 dd = tl.dd[t][lane];
         const float dl = dd.x, du = dd.y;
-        rdl[t] = dl;   // kept for the adjoint
-        rdu[t] = du;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float a = exp2_hw(dl * A2[g]);
@@ -436,19 +512,40 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         }
       }
       if constexpr (!kRed2) lds_barrier();  // the helpers have read the previous sums
-#pragma unroll
-      for (int t = TC - 1; t >= 0; --t) {
-        const float dl = rdl[t];
-        const float du = rdu[t];
-        const float dyt = tl.dy[t][lane];
-        float s1 = 0.0f, s2 = 0.0f;
-        float pB[G], pC[G];
+      // the adjoint, last step first; step t - 1's LDS operands are read
+      // while step t computes (scheduling barriers keep the reads early)
+      float qdl[2], qdu[2], qdy[2], qB[2][G], qC[2][G];
+      auto read_step = [&](int t) {
+        const int q = t & 1;
+        const float2 dd = tl.dd[t][lane];
+        qdl[q] = dd.x;
+        qdu[q] = dd.y;
+        qdy[q] = tl.dy[t][lane];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float lam = fmaf(dyt, tl.C[t][gidx + g], lamn[g]);
+          qB[q][g] = tl.B[t][gidx + g];
+          qC[q][g] = tl.C[t][gidx + g];
+        }
+      };
+      read_step(TC - 1);
+#pragma unroll
+      for (int t = TC - 1; t >= 0; --t) {
+        if (t > 0) read_step(t - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int q = t & 1;
+        const float dl = qdl[q];
+        const float du = qdu[q];
+        const float dyt = qdy[q];
+        float s1 = 0.0f, s2 = 0.0f;
+        float pBC[2 * G];  // lambda Delta u (dB), then dy h (dC), per state
+        float* const pB = pBC;
+        float* const pC = pBC + G;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float lam = fmaf(dyt, qC[q][g], lamn[g]);
           pC[g] = dyt * hs[t][g];
           pB[g] = lam * du;
-          s1 = fmaf(lam, tl.B[t][gidx + g], s1);
+          s1 = fmaf(lam, qB[q][g], s1);
           const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][g] : hstart[g];
           lamn[g] = as[t][g] * lam;               // Abar_t lambda_t, carried to step t-1
           const float lq = lamn[g] * hp;          // lambda_t Abar_t h_{t-1}
@@ -457,11 +554,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         }
         rd.p1[w][t][lane] = s1;
         rd.p2[w][t][lane] = s2;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          pB[g] = quad_sum(pB[g]);
-          pC[g] = quad_sum(pC[g]);
-        }
+        quad_sum_all(pBC);
         // the four lanes of a quad hold the same sums and store them to the
         // same place (no branch on the lane; equal values, so whichever
         // store lands last leaves the same result)
@@ -509,8 +602,10 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
   const bool run_aggregate = !next_final;
 
   if (!scan_wave) {
-    if (run_aggregate) helper_loop(false);
-    helper_loop(true);
+    using kOn = std::integral_constant<bool, true>;
+    using kOff = std::integral_constant<bool, false>;
+    if (run_aggregate) helper_loop(kOff{});
+    helper_loop(kOn{});
     // dD and ddt_bias: sum each channel's column over the chunk rows (every
     // wave has passed the passes' last barrier, so the tiles are free)
 #pragma unroll
@@ -717,11 +812,23 @@ static hipError_t launch_bwd_typed(const BwdPtrs& p, const BwdShape& sh, hipStre
   }
   const int64_t workgroups = sh.n_full + static_cast<int64_t>(sh.chains - sh.n_full) * sh.n_seg;
   const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * (NG + NP));
+  const bool fast = sh.softplus != 0 && sh.has_z != 0;
+#define SSM_LAUNCH_BWD(V, F) \
+  hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, NP, TC, V, F>), grid, block, 0, st, p, sh)
   if (sh.vec_io) {
-    hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, NP, TC, true>), grid, block, 0, st, p, sh);
+    if (fast) {
+      SSM_LAUNCH_BWD(true, true);
+    } else {
+      SSM_LAUNCH_BWD(true, false);
+    }
   } else {
-    hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, NP, TC, false>), grid, block, 0, st, p, sh);
+    if (fast) {
+      SSM_LAUNCH_BWD(false, true);
+    } else {
+      SSM_LAUNCH_BWD(false, false);
+    }
   }
+#undef SSM_LAUNCH_BWD
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int N = NG * G;

@@ -60,6 +60,16 @@ __device__ __forceinline__ float softplus_f32(float s) {
   return fmaxf(s, 0.0f) + fmaf(log2_hw(w), kLn2, r);
 }
 
+// softplus(s) and its derivative sigmoid(s) = exp(s - softplus(s)), which
+// reuses the softplus value: the difference is exact enough (for large s it
+// is -e^-s to within an ulp of s, for very negative s it is s) for a result
+// within a few ulp.
+__device__ __forceinline__ float softplus_sigmoid(float s, float& sig) {
+  const float sp = softplus_f32(s);
+  sig = exp2_hw((s - sp) * kLog2e);
+  return sp;
+}
+
 // Input coefficient of the exact zero-order-hold discretisation for a
 // diagonal A: Bbar / B = (exp(Delta A) - 1) / A = Delta * phi(x) with
 // x = Delta A and phi(x) = (e^x - 1) / x = sum_k x^k / (k+1)!.  Near x = 0
@@ -204,6 +214,29 @@ __device__ __forceinline__ float quad_sum(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
                                                           0xF, 0xF, true));
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
+                                                          0xF, 0xF, true));
+  return v;
+}
+
+// quad_sum of K values at once: the first exchange for all of them, then the
+// second, so no DPP read waits on the add just before it.
+template <int K>
+__device__ __forceinline__ void quad_sum_all(float (&v)[K]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+    v[i] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[i]), 0xB1,
+                                                               0xF, 0xF, true));
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+    v[i] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[i]), 0x4E,
+                                                               0xF, 0xF, true));
+}
+
+// Sum over lane pairs (2i, 2i+1), returned in both: one DPP exchange.
+__device__ __forceinline__ float pair_sum(float v) {
+#pragma clang fp contract(off)
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
                                                           0xF, 0xF, true));
   return v;
 }
