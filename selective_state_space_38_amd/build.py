@@ -36,8 +36,8 @@ HIPCC_FLAGS = [
 ]
 
 
-# rocBLAS runs the Mamba block's projection GEMMs
-LINK_LIBS = ["-L/opt/rocm/lib", "-lrocblas"]
+# hipBLASLt runs the Mamba block's projection GEMMs
+LINK_LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 
 
 def hipcc():
