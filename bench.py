@@ -380,7 +380,7 @@ def _time_ms(torch, fn, steps, warmup):
 def block_bench(args, torch, dev):
     """One Mamba block of the workload's model (B, L of the workload; d_model
     = d_inner / 2) with seeded random weights.  The conv1d and the scan are
-    also timed alone on the same shapes, so the projections' share (rocBLAS
+    also timed alone on the same shapes, so the projections' share (hipBLASLt
     GEMMs on MFMA) is the block time minus theirs."""
     from selective_state_space_38_amd import (causal_conv1d_fwd, mamba_block_fwd,
                                               selective_scan_fwd)

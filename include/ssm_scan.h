@@ -51,7 +51,7 @@
  *     stream-ordered (hipMallocAsync) and free it on the same stream;
  *     failure returns SSM_ENOMEM.  The only other state is a per-device count
  *     of timed-out carry waits (read by ssm_check_device_errors) and, for
- *     mamba_block_fwd, one rocBLAS handle per host thread and device, so
+ *     mamba_block_fwd, one hipBLASLt handle per host thread and device, so
  *     calls on different streams or host threads may run concurrently.
  */
 #ifndef SSM_SCAN_H
@@ -253,7 +253,7 @@ typedef struct {
 
 /*
  * Forward of one Mamba block:
- *   x, z  = x_in in_x, x_in in_z                      (rocBLAS GEMMs)
+ *   x, z  = x_in in_x, x_in in_z                      (hipBLASLt GEMMs)
  *   u     = SiLU(causal_conv1d(x) + conv_b)            (causal_conv1d_fwd)
  *   dt_low, B, C = u x_dt, u x_B, u x_C;  dt = dt_low dt   (GEMMs; the three
  *           projections of u run as one GEMM against [x_dt | x_B | x_C])
@@ -265,7 +265,7 @@ typedef struct {
  * for the intermediates (about (5 d_inner + dt_rank + 4 d_state) * batch *
  * seqlen elements of dtype, plus a d_inner x (dt_rank + 2 d_state) copy of
  * the x_proj weights) is allocated stream-ordered and freed on the stream.  Normalisation and the residual connection are the caller's.
- * Returns an ssm_status (SSM_ELAUNCH if rocBLAS fails).
+ * Returns an ssm_status (SSM_ELAUNCH if a GEMM fails).
  */
 int mamba_block_fwd(const void* x_in, const mamba_block_weights* weights, void* out,
                     const mamba_block_dims* dims, void* stream);

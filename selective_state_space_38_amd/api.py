@@ -311,7 +311,7 @@ BLOCK_WEIGHTS = ("in_x", "in_z", "conv_w", "conv_b", "x_dt", "x_B", "x_C", "dt",
 
 
 def mamba_block_fwd(x_in, weights, out=None):
-    """Forward of one Mamba block on the GPU (projections on rocBLAS, conv1d
+    """Forward of one Mamba block on the GPU (projections on hipBLASLt, conv1d
     + SiLU and the gated selective scan in this library's kernels).
 
     x_in: [batch, L, d_model] (float32 or bfloat16).  ``weights``: dict with

@@ -508,7 +508,7 @@ int block_impl(const void* x_in, const mamba_block_weights* w, void* out,
   if (out == x_in) return SSM_EINVAL;
   const int64_t M = bd->batch * bd->seqlen;
   const int64_t di = bd->d_inner, dm = bd->d_model, n = bd->d_state, r = bd->dt_rank;
-  // rocBLAS takes 32-bit sizes
+  // the GEMM library takes 32-bit sizes
   const int64_t lim = (1LL << 31) - 1;
   if (M > lim || di > lim || dm > lim || M * di > (1LL << 46)) return SSM_EINVAL;
 

@@ -200,7 +200,7 @@ hipError_t launch_conv1d_update(int dtype, int width, const ConvPtrs& p, const C
                                 hipStream_t stream);
 
 // Row-major C[M][N] = A[M][K] W[K][N] (leading dimensions in elements) on
-// rocBLAS, float32 accumulation; dtype 0 = float32, 1 = bfloat16 storage.
+// hipBLASLt, float32 accumulation; dtype 0 = float32, 1 = bfloat16 storage.
 hipError_t gemm_rowmajor(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
                          int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
                          hipStream_t stream);

@@ -1,4 +1,4 @@
-"""GPU parity of the Mamba block forward (mamba_block_fwd: rocBLAS
+"""GPU parity of the Mamba block forward (mamba_block_fwd: hipBLASLt
 projections around this library's conv1d and scan kernels) against the
 float64 oracle (oracle.mamba_block_fwd).  Tolerance: max-abs error <= tol *
 max |oracle output|, 1e-4 for float32 and 2e-2 for bfloat16 (the forward's
