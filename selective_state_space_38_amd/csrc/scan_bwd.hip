@@ -78,8 +78,8 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
     float C[TC][N];
   };
   // one chunk's partial sums from the scan waves; the quad sums' rows hold
-  // the G-state groups in a rotated order (swz below) so that the 16 quad
-  // leaders of a wave write their G floats to different banks
+  // the G-state groups in a rotated order (swz below) so that the 16 quads
+  // of a wave write their G floats to different banks
   struct Red {
     float p1[NG][TC][64];      // sum over the group's states of lambda B
     float p2[NG][TC][64];      // sum over the group's states of lambda Abar h_{t-1} A
