@@ -4,18 +4,27 @@
 One step = one selective_scan_fwd over the Mamba-2.8B-shaped layer
 (batch 4, L 8192, d_inner 5120, d_state 16, bfloat16 activations, float32
 state and arithmetic) followed by one selective_state_update over the decode
-workload (256 sequences x 5120 channels x 16 states).  Inputs are seeded
-synthetic data (synth.make) already resident in HBM; decode states rotate
-over six buffers (504 MB) so the 256 MB Infinity Cache cannot hold them
-between steps.
+workload (256 sequences x 5120 channels x 16 states): every step of the hot
+path once.  Inputs are seeded synthetic data (synth.make) already resident in
+HBM; decode states rotate over six buffers (504 MB) so the 256 MB Infinity
+Cache cannot hold them between steps.
 
-Prints one JSON line.  `value` is tokens*channels processed per second over
-the whole step (forward B*L*D plus decode B*D).  `roofline` describes the
-forward kernel (the dominant one); `cpu_baseline` times the float64 oracle on
+Prints one JSON line.  `value` is the forward's tokens*channels per second
+(B*L*D over the forward kernel's own time; the decode's rate is reported
+separately); `ms_per_step` is the wall time of a whole step.  Beside the
+timed step the same run measures:
+  * the ceilings the fractions are taken against (libssm_micro probes: fp32
+    FMA and v_exp_f32 rates, streaming HBM bandwidth);
+  * the million-token and 130M-shaped forwards (their own timing loops, not
+    part of the step), so every north-star configuration has a number;
+and reports per configuration the HBM fraction of 8 TB/s (the metric), the
+VALU fraction (lane-slots/s) and the transcendental fraction.  `roofline`
+describes the 2.8B forward kernel; `cpu_baseline` times the float64 oracle on
 a bounded sample of the same workload on the host.
 """
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -29,14 +38,14 @@ import numpy as np  # noqa: E402
 
 import synth  # noqa: E402
 
-# MI355X public figures: 256 CUs x 4 SIMD16 units at 2.4 GHz -> 39.3 T fp32
-# vector lane-operations per second without packed math (the published
-# 157.3 TFLOP/s counts an FMA as 2 flops and packed pairs as 2 lanes).
+# MI355X public figures: HBM3E at 8 TB/s; 256 CUs x 4 SIMD16 units at 2.4 GHz
+# -> 39.3 T fp32 vector lane-slots per second without packed math (the
+# published 157.3 TFLOP/s counts an FMA as 2 flops and packed pairs as 2
+# lanes; packed fp32 is off in this build).
 HBM_PEAK_GBS = 8000.0
-# v_exp_f32 throughput measured on gfx950 with 4 waves per SIMD (half the
-# FMA rate); the transcendental roofline of the forward
-EXP_PEAK_TPS = 18.47
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+COMPUTE_UNITS = 256
+VALU_PEAK_TSLOTS = COMPUTE_UNITS * 4 * 16 * 2.4e9 / 1e12
+ALU_UNIT = "T VALU lane-slots/s"
 
 METRIC = "selective-scan fwd tokens·channels/s and achieved HBM GB/s (% of peak), 1 GPU"
 
@@ -108,13 +117,24 @@ def parse():
     p.add_argument("--l-sweep", action="store_true",
                    help="instead of the step: time the forward alone over L = 2^10 .. 2^20 "
                         "at B=1, D=256, N=16, float32 (one JSON line per L)")
+    p.add_argument("--micro", action="store_true",
+                   help="instead of the step: the ceiling probes alone (VALU rates at 1-8 "
+                        "waves per SIMD, the full streaming sweep); one JSON line")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the million-token and 130M-shaped forwards timed beside the step")
+    p.add_argument("--extra-steps", type=int, default=20,
+                   help="timed launches of each extra forward workload")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="before timing, run one plain device copy of this many MiB "
                         "(a known-size reference for hardware byte counters)")
     return p.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_traffic_mamba2p8b.json")
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"scan_fwd_traffic_{workload}.json")
+
+
+
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_38_amd", "csrc", f)
                   for f in ("scan_fwd.hip", "ssm_device.h", "ssm_internal.h", "api.hip")]
 
@@ -132,7 +152,7 @@ def measured_traffic(workload):
     """HBM bytes per forward launch from the committed counter summary, or None
     when it was taken on another workload or the kernel sources changed since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -248,14 +268,15 @@ def bwd_bench(args, torch, dev):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": (t1 - t0) * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic (seeded N(0,1) activations and output gradient)",
+        "dtype": f"{w.dtype} io, f32 arithmetic",
+        "data": "synthetic (seeded N(0,1) activations and output gradient)",
         "config": {"workload": (f"{w.name} backward (B={w.batch}, L={w.seqlen}, D={w.dim}, "
                                 f"N={w.dstate}, {w.dtype} activations)"
                                 + (", from the training-mode forward's checkpoints"
                                    if args.train else ", recomputing its own checkpoints"))},
         "roofline": {
-            "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS, "unit": "TFLOP/s",
-            "frac": achieved / VALU_PEAK_TOPS, "traffic": None,
+            "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TSLOTS, "unit": ALU_UNIT,
+            "frac": achieved / VALU_PEAK_TSLOTS, "traffic": None,
             "kernel": "scan_bwd_kernel (+ reductions)",
             "ops_per_unit": f"{bwd_valu_slots_per_token_channel(w.dstate)} fp32 VALU issue "
                             "slots per token*channel",
@@ -338,7 +359,8 @@ def conv_bench(args, torch, dev):
         "value": tokch / (avg / 1e3), "unit": "tokens·channels/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": (t1 - t0) * 1e3 / args.steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{w.dtype} io, f32 arithmetic",
         "data": "synthetic (seeded N(0,1) activations and filters)",
         "config": {"workload": (f"{w.name} activations (B={w.batch}, L={w.seqlen}, "
                                 f"D={w.dim}, {w.dtype}), width {k}")},
@@ -495,9 +517,180 @@ def l_sweep(args, torch, dev):
             "l_sweep": True, "batch": w.batch, "seqlen": L, "dim": w.dim, "dstate": w.dstate,
             "dtype": "f32", "median_ms": med, "min_ms": float(np.min(ms)),
             "tokens_channels_per_s": tokch / (med / 1e3),
-            "alu_frac": slots / (med / 1e3) / 1e12 / VALU_PEAK_TOPS,
+            "alu_frac": slots / (med / 1e3) / 1e12 / VALU_PEAK_TSLOTS,
             "plan": fwd_plan(w.batch, L, w.dim, w.dstate, torch.float32),
         }), flush=True)
+
+
+# ------------------------------------------------------------ ceilings --
+
+def _ms(fn):
+    v = ctypes.c_float()
+    rc = fn(ctypes.byref(v))
+    if rc != 0:
+        raise RuntimeError(f"probe failed with status {rc}")
+    return float(v.value)
+
+
+def probe_valu(torch, dev, waves_per_simd=4, iters=256, reps=5):
+    """fp32 FMA, v_exp_f32 and mixed (1 exp : 4 FMA) rates in T lane-ops/s
+    from ssm_micro_valu, with ~waves_per_simd waves on every SIMD and eight
+    independent chains per lane; also the FMA rate of a lone wave per SIMD
+    with one dependent chain (the issue rate of a serial recurrence)."""
+    from selective_state_space_38_amd import _lib
+    lib = _lib.load_micro()
+    seed = torch.tensor([0.5, 0.25] + [0.5 + 0.06 * k for k in range(8)], dtype=torch.float32,
+                        device=dev)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def rate(kind, chains, wps):
+        blocks = COMPUTE_UNITS * wps
+        ms = _ms(lambda p: lib.ssm_micro_valu(kind, chains, blocks, iters,
+                                              ctypes.c_void_p(seed.data_ptr()),
+                                              ctypes.c_void_p(sink.data_ptr()), reps, p, st))
+        steps = blocks * 256 * iters * 16 * chains
+        return steps / (ms / 1e3) / 1e12
+
+    fma = rate(0, 8, waves_per_simd)
+    exp = rate(1, 8, waves_per_simd)
+    mix_steps = rate(2, 8, waves_per_simd)    # element-steps: 1 exp + 4 FMA each
+    lone = rate(0, 1, 1)
+    lone_ilp = rate(0, 8, 1)
+
+    def cycles(r):  # issue interval of one wave at the nominal clock (one wave per SIMD)
+        return 2.4e9 * COMPUTE_UNITS * 4 * 64 / (r * 1e12)
+
+    return {
+        "fma_T_per_s": fma,
+        "exp_T_per_s": exp,
+        "exp_to_fma_rate": exp / fma,
+        # slots an exp occupies, measured: 1 exp + 4 FMA per element-step
+        # take (1 / mix) seconds per T steps against 4 / fma for the FMAs
+        "exp_issue_slots_in_mix": (fma / mix_steps) - 4.0,
+        "fma_lone_wave_dependent_T_per_s": lone,
+        "fma_lone_wave_independent_T_per_s": lone_ilp,
+        "lone_wave_cycles_per_fma_at_2p4GHz": {"dependent": cycles(lone),
+                                               "independent": cycles(lone_ilp)},
+        "waves_per_simd": waves_per_simd, "chains_per_lane": 8,
+    }
+
+
+def probe_stream(torch, dev, nbytes=1 << 30, reps=5, sweep=False):
+    """Streaming HBM bandwidth (GB/s of HBM traffic) from ssm_micro_stream
+    over nbytes buffers (4x the Infinity Cache), 16-byte non-temporal
+    accesses; the best of a few (vectors in flight, workgroups) choices."""
+    from selective_state_space_38_amd import _lib
+    lib = _lib.load_micro()
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(2)
+    sink = torch.zeros(4, dtype=torch.uint8, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    # the quick set holds the best shapes of the full sweep on MI355X (small
+    # grids: 4-8 workgroups per CU, 1-2 vectors in flight; writes alone
+    # prefer many workgroups)
+    shapes = ([(u, k) for u in (1, 2, 4, 8) for k in (4, 8, 16, 32, 64)] if sweep
+              else [(1, 4), (2, 4), (1, 8), (2, 8), (1, 64)])
+    out = {}
+    for mode, name, factor in ((0, "read", 1), (1, "write", 1), (2, "copy", 2),
+                               (3, "update_in_place", 2)):
+        best = None
+        for unroll, per_cu in shapes:
+            blocks = COMPUTE_UNITS * per_cu
+            ms = _ms(lambda p: lib.ssm_micro_stream(
+                mode, unroll, blocks, ctypes.c_void_p(a.data_ptr()),
+                ctypes.c_void_p(b.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), reps, p,
+                st))
+            gbs = factor * nbytes / (ms / 1e3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, unroll, per_cu)
+        out[name] = {"GBps": best[0], "frac_of_8TBps": best[0] / HBM_PEAK_GBS,
+                     "vectors_in_flight": best[1], "workgroups_per_cu": best[2]}
+    out["buffer_bytes"] = nbytes
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def micro_bench(args, torch, dev):
+    """The ceiling probes alone, with the wider stream sweep: one JSON line."""
+    valu = {w: probe_valu(torch, dev, waves_per_simd=w) for w in (1, 2, 4, 8)}
+    stream = probe_stream(torch, dev, sweep=True)
+    print(json.dumps({"micro": True, "valu_by_waves_per_simd": valu, "stream": stream,
+                      "nominal_valu_peak_T_lane_slots_per_s": VALU_PEAK_TSLOTS,
+                      "hbm_peak_GBps": HBM_PEAK_GBS}), flush=True)
+
+
+# --------------------------------------------------------- per workload --
+
+def fwd_entry(w, ms_list, ceil, bbar="delta", traffic=None):
+    """Rates and roofline fractions of one forward workload from its launch
+    times (ms)."""
+    avg = float(np.mean(ms_list))
+    tokch = w.batch * w.seqlen * w.dim
+    nbytes = synth.algorithmic_bytes(w)
+    slots_per = valu_slots_per_token_channel(w.dstate, bbar)
+    alu = slots_per * tokch / (avg / 1e3) / 1e12
+    trans = transcendentals_per_token_channel(w.dstate) * tokch / (avg / 1e3) / 1e12
+    gbs = nbytes / (avg / 1e3) / 1e9
+    e = {
+        "shape": {"batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
+                  "io_dtype": w.dtype},
+        "tokens_channels_per_s": tokch / (avg / 1e3),
+        "avg_ms": avg, "median_ms": float(np.median(ms_list)), "min_ms": float(np.min(ms_list)),
+        "launches": len(ms_list),
+        "algorithmic_bytes": nbytes,
+        "hbm_GBps": gbs, "hbm_frac_of_8TBps": gbs / HBM_PEAK_GBS,
+        "alu": {"slots_per_token_channel": slots_per, "achieved": alu, "unit": ALU_UNIT,
+                "frac_of_nominal": alu / VALU_PEAK_TSLOTS,
+                "frac_of_measured_fma_rate": alu / ceil["fma_T_per_s"]},
+        "transcendentals": {"per_token_channel": transcendentals_per_token_channel(w.dstate),
+                            "achieved_T_per_s": trans,
+                            "frac_of_measured_exp_rate": trans / ceil["exp_T_per_s"]},
+    }
+    if traffic is not None:
+        e["counter_traffic_bytes"] = traffic
+        e["counter_traffic_over_algorithmic"] = traffic / nbytes
+    return e
+
+
+def _upload(torch, dev, a, dtype=None):
+    dtype = torch.float32 if dtype is None else dtype
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dtype)
+
+
+def time_forward(torch, dev, w, steps, warmup, bbar="delta"):
+    """Launch times (ms, HIP events on the launch stream) of the forward on
+    workload w; input sets rotate when one set could sit in the Infinity
+    Cache (the 130M layer's 405 MB), the 2.8B layer (1.35 GB) and the
+    million-token sequence (4.4 GB) stream from HBM anyway."""
+    from selective_state_space_38_amd import check_device_errors, selective_scan_fwd
+    act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    n_sets = 3 if synth.algorithmic_bytes(w) < 1 << 30 else 1
+    print(f"bench: generating {w.name} inputs ({n_sets} set(s))", file=sys.stderr, flush=True)
+    sets = []
+    x0 = None
+    for k in range(n_sets):
+        xs = synth.make(w, seed=None if k == 0 else w.seed + 1000 * k)
+        if k == 0:
+            x0 = xs
+        sets.append(tuple(_upload(torch, dev, xs[n], act) for n in ("u", "delta", "z", "B", "C")))
+    A, Dv, bias = (_upload(torch, dev, x0[n]) for n in ("A", "D", "dt_bias"))
+    out = torch.empty_like(sets[0][0])
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+    calls = [0]
+
+    def fwd():
+        su, sdt, sz, sB, sC = sets[calls[0] % n_sets]
+        calls[0] += 1
+        selective_scan_fwd(su, sdt, A, sB, sC, D=Dv, z=sz, delta_bias=bias, delta_softplus=True,
+                           return_last_state=True, out=out, last_state=last, bbar=bbar)
+
+    ms = _time_ms(torch, fwd, steps, warmup)
+    check_device_errors(dev)
+    del sets, out, last
+    torch.cuda.empty_cache()
+    return ms, n_sets
 
 
 def main():
@@ -514,6 +707,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.micro:
+        micro_bench(args, torch, dev)
+        return
     if args.l_sweep:
         l_sweep(args, torch, dev)
         return
@@ -526,6 +722,11 @@ def main():
     if args.block:
         block_bench(args, torch, dev)
         return
+
+    print("bench: measuring the ALU and HBM ceilings", file=sys.stderr, flush=True)
+    ceil = probe_valu(torch, dev)
+    stream = probe_stream(torch, dev)
+
     w = synth.WORKLOADS[args.workload]
     dw = synth.WORKLOADS["decode"]
     act = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -533,29 +734,16 @@ def main():
     print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
     x = synth.make(w)
     dec = synth.make(dw)
-
-    def up(a, dtype=torch.float32):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dtype)
-
-    # Input sets rotate when one set is small enough for the 256 MB Infinity
-    # Cache to keep a useful share of it between steps (the 130M layer's 405
-    # MB); the 2.8B layer (1.35 GB) and the million-token sequence (4.4 GB)
-    # stream from HBM anyway.
-    n_sets = 3 if synth.algorithmic_bytes(w) < 1 << 30 else 1
-    sets = []
-    for k in range(n_sets):
-        xs = x if k == 0 else synth.make(w, seed=w.seed + 1000 * k)
-        sets.append((up(xs["u"], act), up(xs["delta"], act), up(xs["z"], act),
-                     up(xs["B"], act), up(xs["C"], act)))
-    u = sets[0][0]
-    A, Dv, bias = up(x["A"]), up(x["D"]), up(x["dt_bias"])
+    u, dt_, z = (_upload(torch, dev, x[n], act) for n in ("u", "delta", "z"))
+    Bm, Cm = (_upload(torch, dev, x[n], act) for n in ("B", "C"))
+    A, Dv, bias = (_upload(torch, dev, x[n]) for n in ("A", "D", "dt_bias"))
     out = torch.empty_like(u)
     last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
     n_rot = 6  # 6 x 84 MB of decode state: twice the 256 MB Infinity Cache
-    states = [up(dec["state"]) for _ in range(n_rot)]
-    dx, ddt, dz = up(dec["u"], dact), up(dec["delta"], dact), up(dec["z"], dact)
-    dB, dC = up(dec["B"], dact), up(dec["C"], dact)
-    dA, dD, dbias = up(dec["A"]), up(dec["D"]), up(dec["dt_bias"])
+    states = [_upload(torch, dev, dec["state"]) for _ in range(n_rot)]
+    dx, ddt, dz = (_upload(torch, dev, dec[n], dact) for n in ("u", "delta", "z"))
+    dB, dC = (_upload(torch, dev, dec[n], dact) for n in ("B", "C"))
+    dA, dD, dbias = (_upload(torch, dev, dec[n]) for n in ("A", "D", "dt_bias"))
     dout = torch.empty_like(dx)
     torch.cuda.synchronize()
     if args.copy_calibration_mb > 0:
@@ -569,12 +757,8 @@ def main():
               file=sys.stderr, flush=True)
         del src, dst
 
-    fwd_calls = [0]
-
     def fwd():
-        su, sdt, sz, sB, sC = sets[fwd_calls[0] % n_sets]
-        fwd_calls[0] += 1
-        selective_scan_fwd(su, sdt, A, sB, sC, D=Dv, z=sz, delta_bias=bias, delta_softplus=True,
+        selective_scan_fwd(u, dt_, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, delta_softplus=True,
                            return_last_state=True, out=out, last_state=last, bbar=args.bbar)
 
     def decode(i):
@@ -605,23 +789,46 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    fwd_avg = float(np.mean(fwd_ms))
-    dec_avg = float(np.mean(dec_ms))
-    trans_rate = (transcendentals_per_token_channel(w.dstate) * w.batch * w.seqlen * w.dim
-                  / (fwd_avg / 1e3) / 1e12)
+    del u, dt_, z, Bm, Cm, out
+    torch.cuda.empty_cache()
 
-    tokch_fwd = w.batch * w.seqlen * w.dim
-    tokch_dec = 0 if args.no_decode else dw.batch * dw.dim
-    value = (tokch_fwd + tokch_dec) / (ms_per_step / 1e3)
-    fwd_bytes = synth.algorithmic_bytes(w)
-    dec_bytes = synth.algorithmic_bytes(dw)
-    slots = valu_slots_per_token_channel(w.dstate, args.bbar) * tokch_fwd
-    achieved_t = slots / (fwd_avg / 1e3) / 1e12
-    plan = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate, act)
+    traffic = measured_traffic(w.name) if args.bbar == "delta" else None
+    configs = {w.name: fwd_entry(w, fwd_ms, ceil, args.bbar, traffic)}
+    configs[w.name]["plan"] = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate, act)
+    if not args.no_decode:
+        dec_avg = float(np.mean(dec_ms))
+        dec_bytes = synth.algorithmic_bytes(dw)
+        dgbs = dec_bytes / (dec_avg / 1e3) / 1e9
+        configs["decode"] = {
+            "shape": {"batch": dw.batch, "dim": dw.dim, "dstate": dw.dstate,
+                      "io_dtype": dw.dtype, "state": "f32"},
+            "tokens_channels_per_s": dw.batch * dw.dim / (dec_avg / 1e3),
+            "avg_ms": dec_avg, "median_ms": float(np.median(dec_ms)),
+            "min_ms": float(np.min(dec_ms)), "launches": len(dec_ms),
+            "algorithmic_bytes": dec_bytes, "hbm_GBps": dgbs,
+            "hbm_frac_of_8TBps": dgbs / HBM_PEAK_GBS,
+            "frac_of_measured_update_in_place": dgbs / stream["update_in_place"]["GBps"],
+            "frac_of_measured_copy": dgbs / stream["copy"]["GBps"],
+            "state_sets_rotated": n_rot,
+        }
+    if not args.no_extra:
+        for name in ("seq1m", "mamba130m"):
+            if name == w.name:
+                continue
+            ew = synth.WORKLOADS[name]
+            ms_e, sets_e = time_forward(torch, dev, ew, args.extra_steps, args.warmup, args.bbar)
+            configs[name] = fwd_entry(ew, ms_e, ceil, args.bbar,
+                                      measured_traffic(name) if args.bbar == "delta" else None)
+            configs[name]["input_sets_rotated"] = sets_e
+            configs[name]["plan"] = fwd_plan(ew.batch, ew.seqlen, ew.dim, ew.dstate,
+                                             torch.bfloat16 if ew.dtype == "bf16"
+                                             else torch.float32)
 
+    head = configs[w.name]
+    fwd_avg = head["avg_ms"]
     line = {
         "metric": METRIC,
-        "value": value,
+        "value": head["tokens_channels_per_s"],
         "unit": "tokens·channels/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -630,8 +837,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": f"{w.dtype} io, f32 arithmetic",
         "data": "synthetic (seeded N(0,1) activations, S4D-real A, log-uniform dt bias)",
+        "hbm_GBps": head["hbm_GBps"],
+        "hbm_frac_of_peak": head["hbm_frac_of_8TBps"],
         "config": {
             "workload": (f"{w.name} forward (B={w.batch}, L={w.seqlen}, D={w.dim}, N={w.dstate}, "
                          f"{w.dtype} activations)"
@@ -640,44 +849,28 @@ def main():
                             f"{dw.dtype})")),
             "io_dtype": w.dtype,
             "bbar": args.bbar,
-            "forward_plan": plan,
-            "forward_input_sets": n_sets,
             "decode_state_sets": n_rot,
         },
         "roofline": {
             "bound": "alu",
-            "achieved": achieved_t,
-            "peak": VALU_PEAK_TOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved_t / VALU_PEAK_TOPS,
-            "traffic": measured_traffic(w.name) if args.bbar == "delta" else None,
+            "achieved": head["alu"]["achieved"],
+            "peak": VALU_PEAK_TSLOTS,
+            "unit": ALU_UNIT,
+            "frac": head["alu"]["frac_of_nominal"],
+            "traffic": traffic,
             "kernel": "scan_fwd_kernel",
-            "ops_per_unit": f"{valu_slots_per_token_channel(w.dstate, args.bbar)} fp32 VALU "
-                            "issue slots per token*channel",
-            "units_per_launch": tokch_fwd,
+            "ops_per_unit": (f"{valu_slots_per_token_channel(w.dstate, args.bbar)} fp32 VALU "
+                             "issue slots per token*channel (v_exp_f32 counted as 2)"),
+            "units_per_launch": w.batch * w.seqlen * w.dim,
             "avg_launch_ms": fwd_avg,
-            "median_launch_ms": float(np.median(fwd_ms)),
-            "min_launch_ms": float(np.min(fwd_ms)),
-            "transcendentals": {
-                "per_token_channel": transcendentals_per_token_channel(w.dstate),
-                "achieved_T_per_s": trans_rate,
-                "measured_v_exp_peak_T_per_s": EXP_PEAK_TPS,
-                "frac": trans_rate / EXP_PEAK_TPS,
-            },
+            "hbm": {"achieved": head["hbm_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": head["hbm_frac_of_8TBps"],
+                    "algorithmic_bytes_per_launch": head["algorithmic_bytes"]},
+            "transcendentals": head["transcendentals"],
         },
-        "hbm": {
-            "forward_GBps": fwd_bytes / (fwd_avg / 1e3) / 1e9,
-            "forward_frac_of_8TBps": fwd_bytes / (fwd_avg / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "forward_algorithmic_bytes": fwd_bytes,
-            "decode_GBps": (None if args.no_decode else
-                            dec_bytes / (dec_avg / 1e3) / 1e9),
-            "decode_frac_of_8TBps": (None if args.no_decode else
-                                     dec_bytes / (dec_avg / 1e3) / 1e9 / HBM_PEAK_GBS),
-            "decode_algorithmic_bytes": dec_bytes,
-            "decode_avg_launch_ms": None if args.no_decode else dec_avg,
-            "decode_median_launch_ms": None if args.no_decode else float(np.median(dec_ms)),
-            "decode_min_launch_ms": None if args.no_decode else float(np.min(dec_ms)),
-        },
+        "ceilings": {"valu": ceil, "stream": stream},
+        "configs": configs,
+        "step_tokens_channels_per_s": (w.batch * w.seqlen * w.dim) / (ms_per_step / 1e3),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

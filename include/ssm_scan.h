@@ -139,6 +139,9 @@ int selective_scan_fwd_ex(const void* u, const void* delta, const float* A,
  *   B, C        : [B][N] of dtype
  *   out         : [B][D] of dtype, written
  *   dims->seqlen must be 1.  `out` must not alias an input or `state`.
+ *   For dstate >= 4, `state` and A must be 16-byte aligned (SSM_EALIGN
+ *   otherwise); B and C are read as vectors when they are aligned to four
+ *   elements and element by element when not.
  */
 int selective_state_update(float* state, const void* x, const void* dt,
                            const float* A, const void* B, const void* C,

@@ -9,6 +9,9 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssm_scan.so")
+# the roofline ceiling probes (include/ssm_micro.h), used by the benchmark
+MICRO_LIB_PATH = os.path.join(HERE, "libssm_micro.so")
+EXPORTED_MICRO = ("ssm_micro_valu", "ssm_micro_stream")
 
 SSM_F32 = 0
 SSM_BF16 = 1
@@ -78,6 +81,29 @@ class MambaBlockDims(ctypes.Structure):
 
 
 _lib = None
+_micro = None
+
+
+def load_micro():
+    """Returns the loaded probe library, raising if it has not been built."""
+    global _micro
+    if _micro is not None:
+        return _micro
+    if not os.path.exists(MICRO_LIB_PATH):
+        raise RuntimeError(
+            f"{MICRO_LIB_PATH} not found: build it with "
+            "`python -m selective_state_space_38_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(MICRO_LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.ssm_micro_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                   vp, ctypes.c_int, ctypes.POINTER(ctypes.c_float), vp]
+    lib.ssm_micro_valu.restype = ctypes.c_int
+    lib.ssm_micro_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
+                                     ctypes.c_int64, vp, ctypes.c_int,
+                                     ctypes.POINTER(ctypes.c_float), vp]
+    lib.ssm_micro_stream.restype = ctypes.c_int
+    _micro = lib
+    return lib
 
 
 def load():

@@ -11,6 +11,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm_scan.so")
+# the roofline ceiling probes: a library of their own, not part of the scan's ABI
+MICRO_LIB = os.path.join(HERE, "libssm_micro.so")
+MICRO_SOURCE = "micro.hip"
 # (source, object name, extra flags): the forward is compiled once per
 # activation type so the two halves build in parallel
 SOURCES = [
@@ -74,12 +77,16 @@ def build(verbose=False):
         objs.append(obj)
         procs.append(_run([hipcc()] + compile_flags + extra +
                           ["-c", os.path.join(CSRC, src), "-o", obj], verbose))
+    micro_tmp = MICRO_LIB + ".tmp"
+    procs.append(_run([hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, MICRO_SOURCE), "-o",
+                                                 micro_tmp], verbose))
     for proc in procs:
         _check(proc, verbose)
     tmp = LIB + ".tmp"
     _check(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs +
                 ["-o", tmp] + LINK_LIBS, verbose), verbose)
     os.replace(tmp, LIB)
+    os.replace(micro_tmp, MICRO_LIB)
     return LIB
 
 

@@ -79,8 +79,11 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
   }
   const int force_seg = env_int("SSM_FORCE_SEGMENT", 0);
   if (force_seg > 0) seg_len = force_seg;
-  seg_len = div_up(seg_len, ssm::kChunk) * ssm::kChunk;
-  if (seg_len > d.seqlen) seg_len = div_up(d.seqlen, ssm::kChunk) * ssm::kChunk;
+  // segments are whole chunks of the kernel instance (16 steps from four
+  // state groups on, 32 below), so only a sequence's last segment can end in
+  // a partial chunk
+  seg_len = div_up(seg_len, chunk) * chunk;
+  if (seg_len > d.seqlen) seg_len = div_up(d.seqlen, chunk) * chunk;
   int64_t n_seg = div_up(d.seqlen, seg_len);
   if (n_seg == 1) lookback = 0;
   int64_t whole = n_seg == 1 ? chains : 0;
@@ -97,7 +100,7 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
     const int force_split = env_int("SSM_FORCE_SPLIT", -1);
     if (force_split >= 1 && K > 0 && M > 0) S = force_split;
     if (S > 1) {
-      const int64_t sl = div_up(div_up(d.seqlen, S), ssm::kChunk) * ssm::kChunk;
+      const int64_t sl = div_up(div_up(d.seqlen, S), chunk) * chunk;
       if (div_up(d.seqlen, sl) > 1) {
         seg_len = sl;
         n_seg = div_up(d.seqlen, sl);

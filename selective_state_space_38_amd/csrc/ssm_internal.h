@@ -65,8 +65,7 @@ struct FwdPtrs {
 // through LDS per iteration): 32 for one or two state groups, 16 from four
 // on, where two workgroups of 8 waves must fit a CU's LDS (the tiles and the
 // partial readouts of every group are double buffered).  Segments are a
-// multiple of the largest chunk.
-constexpr int kChunk = 32;
+// multiple of the instance's chunk.
 constexpr int chunk_for_groups(int groups) { return groups >= 4 ? 16 : 32; }
 constexpr int helper_waves(int /*groups*/) { return 4; }
 

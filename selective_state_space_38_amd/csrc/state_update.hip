@@ -24,8 +24,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // reduce the readout C . h with shuffles.  The state is streamed once, so it
 // is read and written with non-temporal hints.  (4 and 16 states per lane
 // measured slower: 16 makes the per-instruction accesses of a wave strided.)
+// VBC: B and C are aligned for the same vector loads (8 bytes per 4 bfloat16,
+// 16 per 4 float32); otherwise they are read element by element.
 constexpr int kDecodeStatesPerLane = 8;
-template <typename T, int N, bool ZOH>
+template <typename T, int N, bool ZOH, bool VBC>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ x, const T* __restrict__ dtp,
     const float* __restrict__ A, const T* __restrict__ Bm, const T* __restrict__ Cm,
@@ -68,7 +70,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     for (int v = 0; v < NV; ++v) {
       const float4 av = reinterpret_cast<const float4*>(ap)[v];
       a2[4 * v] = av.x; a2[4 * v + 1] = av.y; a2[4 * v + 2] = av.z; a2[4 * v + 3] = av.w;
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (!VBC) {
+#pragma unroll
+        for (int j = 4 * v; j < 4 * v + 4; ++j) {
+          bv[j] = to_f32(bp[j]);
+          cv[j] = to_f32(cp[j]);
+        }
+      } else if constexpr (sizeof(T) == 2) {
         const uint2 bw = reinterpret_cast<const uint2*>(bp)[v];
         const uint2 cw = reinterpret_cast<const uint2*>(cp)[v];
         bv[4 * v] = __uint_as_float(bw.x << 16); bv[4 * v + 1] = __uint_as_float(bw.x & 0xffff0000u);
@@ -129,16 +137,27 @@ static hipError_t launch_n(int n, float* state, const void* x, const void* dt, c
                            const void* B, const void* C, const float* D, const void* z,
                            const float* bias, int softplus, int zoh, void* out, int64_t batch,
                            int64_t dim, hipStream_t stream) {
+  // B and C rows start at b * N elements: vector loads need the base aligned
+  // to 4 elements (N >= 4 keeps every row start aligned with it)
+  const uintptr_t vec_bytes = 4 * sizeof(T);
+  const bool vbc = reinterpret_cast<uintptr_t>(B) % vec_bytes == 0 &&
+                   reinterpret_cast<uintptr_t>(C) % vec_bytes == 0;
   const int q = n < kDecodeStatesPerLane ? n : kDecodeStatesPerLane;
   const int64_t total = batch * dim * (n / q);
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
   const dim3 grid(static_cast<unsigned>(blocks));
-#define SSM_LAUNCH_SU_Z(NN, Z)                                                                  \
-  hipLaunchKernelGGL((state_update_kernel<T, NN, Z>), grid, dim3(threads), 0, stream, state,    \
+#define SSM_LAUNCH_SU_ZV(NN, Z, V)                                                              \
+  hipLaunchKernelGGL((state_update_kernel<T, NN, Z, V>), grid, dim3(threads), 0, stream, state, \
                      static_cast<const T*>(x), static_cast<const T*>(dt), A,                    \
                      static_cast<const T*>(B), static_cast<const T*>(C), D,                     \
                      static_cast<const T*>(z), bias, softplus, static_cast<T*>(out), batch, dim)
+#define SSM_LAUNCH_SU_Z(NN, Z)          \
+  if (vbc) {                            \
+    SSM_LAUNCH_SU_ZV(NN, Z, true);      \
+  } else {                              \
+    SSM_LAUNCH_SU_ZV(NN, Z, false);     \
+  }
 #define SSM_LAUNCH_SU(NN)         \
   if (zoh) {                      \
     SSM_LAUNCH_SU_Z(NN, true);    \
@@ -157,6 +176,7 @@ static hipError_t launch_n(int n, float* state, const void* x, const void* dt, c
   }
 #undef SSM_LAUNCH_SU
 #undef SSM_LAUNCH_SU_Z
+#undef SSM_LAUNCH_SU_ZV
   return hipGetLastError();
 }
 

@@ -1,0 +1,50 @@
+"""Host-only checks of the benchmark's bookkeeping (no GPU): the roofline
+arithmetic of a workload entry and the refusal of more than one GPU."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_slot_and_transcendental_counts():
+    # per state: mul, exp (2 slots), mul, fma, fma; per channel step 20
+    assert bench.valu_slots_per_token_channel(16) == 116
+    assert bench.valu_slots_per_token_channel(16, "zoh") == 276
+    assert bench.transcendentals_per_token_channel(16) == 21
+
+
+def test_forward_entry_fractions():
+    w = synth.WORKLOADS["mamba2p8b"]
+    ceil = {"fma_T_per_s": 35.0, "exp_T_per_s": 17.5}
+    e = bench.fwd_entry(w, [0.8, 0.8, 0.8], ceil, traffic=1.4e9)
+    tokch = 4 * 8192 * 5120
+    assert e["tokens_channels_per_s"] == pytest.approx(tokch / 0.8e-3)
+    nbytes = synth.algorithmic_bytes(w)
+    assert e["algorithmic_bytes"] == nbytes == 1345953792
+    assert e["hbm_frac_of_8TBps"] == pytest.approx(nbytes / 0.8e-3 / 8e12)
+    assert e["alu"]["frac_of_nominal"] == pytest.approx(
+        116 * tokch / 0.8e-3 / 1e12 / bench.VALU_PEAK_TSLOTS)
+    assert e["alu"]["unit"] == "T VALU lane-slots/s"
+    assert e["transcendentals"]["frac_of_measured_exp_rate"] == pytest.approx(
+        21 * tokch / 0.8e-3 / 1e12 / 17.5)
+    assert e["counter_traffic_over_algorithmic"] == pytest.approx(1.4e9 / nbytes)
+
+
+def test_nominal_valu_peak():
+    # 256 CUs x 4 SIMD16 x 16 lanes x 2.4 GHz
+    assert bench.VALU_PEAK_TSLOTS == pytest.approx(39.3216)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

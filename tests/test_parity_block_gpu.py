@@ -59,3 +59,13 @@ def test_block_2p8b_full_size_prefix():
     assert np.all(np.isfinite(got))
     ref = oracle.mamba_block_fwd(x_in[:, :32], w)
     check("block out", got[:, :32], ref, float(np.max(np.abs(ref))), TOL["bf16"])
+
+
+def test_block_2p8b_full_width_every_token():
+    """The 2.8B block's full width (d_model 2560, d_inner 5120, N 16, dt_rank
+    160, bfloat16) at L = 512, checked over every token of both rows."""
+    cfg = synth.BLOCKS["mamba2p8b"]
+    x_in, w = synth.make_block(**cfg, batch=2, seqlen=512, dtype="bf16")
+    got = _gpu_block(x_in, w, "bf16")
+    ref = oracle.mamba_block_fwd(x_in, w)
+    check("block out", got, ref, float(np.max(np.abs(ref))), TOL["bf16"])

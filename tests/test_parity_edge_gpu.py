@@ -1,0 +1,274 @@
+"""GPU parity at the method's edge cases and under repetition, through the C
+ABI, against the float64 oracle (tolerances in parity_util):
+
+* a large step resets the state onto the current input ("Mamba / MambaMini"
+  Q&A on how Delta acts on A; reading guide FAQ on Delta): softplus off,
+  dt = 1e4, A <= -0.1, so exp(Delta A) underflows to exactly 0 and
+  h_t = Delta B_t x_t, in every carry mode and in the decode step;
+* softplus far into saturation on both sides (reading guide, S6: Delta =
+  softplus(parameter + projection));
+* repeated launches of the decoupled look-back (segment carries rest on the
+  pair operator's associativity, "Mamba / MambaMini" Step 3): the
+  million-token sequence and 16-step segments, thirty times each, every run
+  checked against the oracle and the device error counter;
+* the plain selective_scan_fwd export, and decode B/C that are not aligned
+  for vector loads.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import (TOL, act_dtype, check, check_forward, env, gpu_available,
+                         gpu_forward, oracle_forward, sample_columns, to_dev)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+MODES = {
+    # carry mode -> planner overrides (None: the planner's own choice)
+    "whole": dict(SSM_FORCE_LOOKBACK=None, SSM_FORCE_SEGMENT=None),
+    "chained": dict(SSM_FORCE_LOOKBACK=0, SSM_FORCE_SEGMENT=64),
+    "lookback": dict(SSM_FORCE_LOOKBACK=1, SSM_FORCE_SEGMENT=64),
+}
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _wl(tag):
+    return "mamba130m" if tag == "f32" else "mamba2p8b"
+
+
+def _round(a, tag):
+    a = np.asarray(a, dtype=np.float32)
+    return synth.round_bf16(a) if tag == "bf16" else a
+
+
+# ------------------------------------------------------ large-Delta reset --
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
+def test_large_delta_resets_state(tag, mode):
+    x = synth.make(_wl(tag), batch=2, seqlen=600, dim=96, dstate=16, a_init="random")
+    x["A"] = np.minimum(x["A"], np.float32(-0.1))
+    x["delta"] = _round(np.full(x["delta"].shape, 1e4), tag)
+    x["dt_bias"] = np.zeros_like(x["dt_bias"])
+    h0 = np.random.default_rng(11).standard_normal((2, 96, 16)).astype(np.float32)
+    _log(f"large delta {tag} {mode}")
+    with env(**MODES[mode]):
+        got, st = gpu_forward(x, tag, softplus=False, h0=h0)
+    ref, ref_st = oracle_forward(x, softplus=False, h0=h0)
+    e1, e2, scale = check_forward(x, tag, got, st, ref, ref_st)
+    # the reset itself, from the pages' statement rather than the oracle: the
+    # final state is the last step's input term alone
+    delta = x["delta"][:, -1].astype(np.float64)                    # [B, D]
+    reset = (delta * x["u"][:, -1])[:, :, None] * x["B"][:, -1][:, None, :]
+    check("reset state", st, reset, scale, TOL[tag])
+    _log(f"  err/scale {e1 / scale:.2e} state {e2 / scale:.2e}")
+
+
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
+def test_decode_large_delta_resets_state(tag):
+    import dataclasses
+    w = dataclasses.replace(synth.WORKLOADS["decode"], dtype=tag)
+    x = synth.make(w, batch=8, dim=300, a_init="random")
+    x["A"] = np.minimum(x["A"], np.float32(-0.1))
+    x["delta"] = _round(np.full(x["delta"].shape, 1e4), tag)
+    x["dt_bias"] = np.zeros_like(x["dt_bias"])
+    from selective_state_space_38_amd import selective_state_update
+    act = act_dtype(tag)
+    st = to_dev(x["state"], torch.float32)
+    out = selective_state_update(st, to_dev(x["u"], act), to_dev(x["delta"], act),
+                                 to_dev(x["A"], torch.float32), to_dev(x["B"], act),
+                                 to_dev(x["C"], act), D=to_dev(x["D"], torch.float32),
+                                 z=to_dev(x["z"], act),
+                                 dt_bias=to_dev(x["dt_bias"], torch.float32), dt_softplus=False)
+    torch.cuda.synchronize()
+    got, gst = out.float().cpu().numpy(), st.cpu().numpy()
+    ref, ref_st = oracle.state_update(x["state"], x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                      x["D"], x["z"], x["dt_bias"], False)
+    scale = float(np.max(np.abs(ref)))
+    check("decode out", got, ref, scale, TOL[tag])
+    check("decode state", gst, ref_st, scale, TOL[tag])
+    reset = (x["delta"].astype(np.float64) * x["u"])[:, :, None] * x["B"][:, None, :]
+    check("decode reset", gst, reset, scale, TOL[tag])
+
+
+# ---------------------------------------------------- softplus saturation --
+
+@pytest.mark.parametrize("center", [-60, -40, -25, -20, -15, 15, 20, 25, 40, 60])
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
+def test_softplus_saturation(tag, center):
+    """s = dt + dt_bias around `center` (jittered across the |s| = 20 edge
+    where softplus(s) meets s and e^s).  On the negative side Delta ~ e^s is
+    tiny, so the skip term and the initial state are left out: the outputs
+    are then made of Delta-sized terms alone and their relative accuracy
+    tests Delta's."""
+    x = synth.make(_wl(tag), batch=2, seqlen=300, dim=80, dstate=16, a_init="random")
+    r = np.random.default_rng(1000 + center)
+    x["delta"] = _round(center + r.uniform(-0.75, 0.75, size=x["delta"].shape), tag)
+    x["dt_bias"] = r.uniform(-0.25, 0.25, size=x["dt_bias"].shape).astype(np.float32)
+    positive = center > 0
+    _log(f"softplus saturation {tag} s~{center}")
+    got, st = gpu_forward(x, tag, D=positive)
+    ref, ref_st = oracle_forward(x, D=positive)
+    e1, e2, scale = check_forward(x, tag, got, st, ref, ref_st)
+    assert scale > 0
+    _log(f"  scale {scale:.3e} err/scale {e1 / scale:.2e} state {e2 / scale:.2e}")
+
+
+# -------------------------------------------------------- look-back stress --
+
+def _device_inputs(x, tag):
+    act = act_dtype(tag)
+    return dict(u=to_dev(x["u"], act), delta=to_dev(x["delta"], act), z=to_dev(x["z"], act),
+                B=to_dev(x["B"], act), C=to_dev(x["C"], act),
+                A=to_dev(x["A"], torch.float32), D=to_dev(x["D"], torch.float32),
+                bias=to_dev(x["dt_bias"], torch.float32))
+
+
+def _run(g, out, last):
+    from selective_state_space_38_amd import selective_scan_fwd
+    selective_scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                       delta_bias=g["bias"], return_last_state=True, out=out, last_state=last)
+
+
+def test_lookback_stress_million_tokens():
+    """The million-token forward 30 times in one process: every run's sampled
+    columns against the oracle, every run's whole output against the first
+    run's (only the look-back's summation order may differ), and the device
+    error counter after every run."""
+    from selective_state_space_38_amd import check_device_errors, fwd_plan
+    w = synth.WORKLOADS["seq1m"]
+    plan = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate)
+    assert plan["lookback"] == 1 and plan["segments"] > 1, plan
+    x = synth.make(w)
+    g = _device_inputs(x, "f32")
+    cols = sample_columns(w.batch, w.dim, 10, seed=w.seed + 1)
+    _log(f"seq1m stress: plan {plan}; oracle on {len(cols)} columns")
+    ref, ref_st = oracle_forward(x, cols=cols)
+    scale = float(np.max(np.abs(ref)))
+    tol = TOL["f32"] * scale
+    bb = torch.tensor([b for b, _ in cols], device="cuda")
+    dd = torch.tensor([d for _, d in cols], device="cuda")
+    out = torch.empty_like(g["u"])
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device="cuda")
+    first = first_st = None
+    check_device_errors()
+    for rep in range(30):
+        _run(g, out, last)
+        check_device_errors()   # synchronises; raises if a carry wait timed out
+        g_out = out[bb, :, dd].double().cpu().numpy()
+        g_st = last[bb, dd].double().cpu().numpy()
+        check(f"rep {rep} out", g_out, ref, scale, TOL["f32"])
+        check(f"rep {rep} state", g_st, ref_st, scale, TOL["f32"])
+        if first is None:
+            first, first_st = out.clone(), last.clone()
+        else:
+            d1 = float((out - first).abs().max())
+            d2 = float((last - first_st).abs().max())
+            assert d1 <= tol and d2 <= tol, (rep, d1, d2, tol)
+        if rep % 10 == 0:
+            _log(f"  rep {rep} ok")
+
+
+@pytest.mark.parametrize("lookback", [1, 0])
+def test_short_segment_stress(lookback):
+    """16-step segments (the kernel's own chunk at N = 16): 256 segments per
+    channel block, the look-back walking up to 255 predecessors in windows,
+    or the chained hand-off through 255 waits; 30 runs, each against the
+    oracle in full and the error counter."""
+    from selective_state_space_38_amd import check_device_errors, fwd_plan
+    bsz, L, dim = 1, 4096, 256
+    x = synth.make("mamba130m", batch=bsz, seqlen=L, dim=dim, dstate=16, a_init="random")
+    ref, ref_st = oracle_forward(x)
+    scale = float(np.max(np.abs(ref)))
+    g = _device_inputs(x, "f32")
+    out = torch.empty_like(g["u"])
+    last = torch.empty((bsz, dim, 16), dtype=torch.float32, device="cuda")
+    check_device_errors()
+    with env(SSM_FORCE_LOOKBACK=lookback, SSM_FORCE_SEGMENT=16):
+        plan = fwd_plan(bsz, L, dim, 16)
+        assert plan["segment_len"] == 16 and plan["segments"] == 256, plan
+        assert plan["lookback"] == lookback, plan
+        _log(f"short-segment stress lookback={lookback}: plan {plan}")
+        for rep in range(30):
+            _run(g, out, last)
+            check_device_errors()
+            check(f"rep {rep} out", out.double().cpu().numpy(), ref, scale, TOL["f32"])
+            check(f"rep {rep} state", last.double().cpu().numpy(), ref_st, scale, TOL["f32"])
+
+
+# ------------------------------------------------------ plain entry point --
+
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
+def test_plain_selective_scan_fwd_export(tag):
+    """selective_scan_fwd (no h0 argument) called through ctypes: the oracle's
+    outputs, and bit for bit those of selective_scan_fwd_h0 with h0 = NULL."""
+    from selective_state_space_38_amd import _lib
+    lib = _lib.load()
+    x = synth.make(_wl(tag), batch=2, seqlen=333, dim=100, dstate=16, a_init="random")
+    g = _device_inputs(x, tag)
+    outs = []
+    for fn in ("plain", "h0"):
+        out = torch.empty_like(g["u"])
+        last = torch.empty((2, 100, 16), dtype=torch.float32, device="cuda")
+        dims = _lib.SsmDims(2, 333, 100, 16, _lib.SSM_BF16 if tag == "bf16" else _lib.SSM_F32)
+        p = [ctypes.c_void_p(g[k].data_ptr()) for k in ("u", "delta", "A", "B", "C", "D", "z",
+                                                        "bias")]
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if fn == "plain":
+            rc = lib.selective_scan_fwd(*p, 1, ctypes.c_void_p(out.data_ptr()),
+                                        ctypes.c_void_p(last.data_ptr()), ctypes.byref(dims),
+                                        stream)
+        else:
+            rc = lib.selective_scan_fwd_h0(*p, 1, None, ctypes.c_void_p(out.data_ptr()),
+                                           ctypes.c_void_p(last.data_ptr()),
+                                           ctypes.byref(dims), stream)
+        assert rc == 0, _lib.status_string(rc)
+        torch.cuda.synchronize()
+        outs.append((out.float().cpu().numpy(), last.cpu().numpy()))
+    ref, ref_st = oracle_forward(x)
+    check_forward(x, tag, outs[0][0], outs[0][1], ref, ref_st)
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------- decode with unaligned B and C --
+
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
+def test_decode_unaligned_b_c(tag):
+    """B and C as views one dword past an aligned start: 4-byte aligned (as the
+    ABI requires) but not aligned for the kernel's vector loads, which then
+    read them element by element."""
+    import dataclasses
+    from selective_state_space_38_amd import selective_state_update
+    w = dataclasses.replace(synth.WORKLOADS["decode"], dtype=tag)
+    x = synth.make(w, batch=6, dim=200, a_init="random")
+    act = act_dtype(tag)
+    shift = 4 // torch.tensor([], dtype=act).element_size()   # elements in one dword
+
+    def offset_view(a):
+        flat = torch.zeros(a.size + 64, dtype=act, device="cuda")
+        v = flat[shift:shift + a.size].view(a.shape)
+        v.copy_(torch.from_numpy(np.ascontiguousarray(a)).to(device="cuda", dtype=act))
+        assert v.data_ptr() % 4 == 0 and v.data_ptr() % (4 * v.element_size()) != 0
+        return v
+
+    st = to_dev(x["state"], torch.float32)
+    out = selective_state_update(st, to_dev(x["u"], act), to_dev(x["delta"], act),
+                                 to_dev(x["A"], torch.float32), offset_view(x["B"]),
+                                 offset_view(x["C"]), D=to_dev(x["D"], torch.float32),
+                                 z=to_dev(x["z"], act),
+                                 dt_bias=to_dev(x["dt_bias"], torch.float32))
+    torch.cuda.synchronize()
+    ref, ref_st = oracle.state_update(x["state"], x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                      x["D"], x["z"], x["dt_bias"])
+    scale = float(np.max(np.abs(ref)))
+    check("decode out", out.float().cpu().numpy(), ref, scale, TOL[tag])
+    check("decode state", st.cpu().numpy(), ref_st, scale, TOL[tag])

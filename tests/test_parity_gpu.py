@@ -87,10 +87,13 @@ def test_nullable_arguments(tag, drop):
 def test_segment_carry_modes(tag, lookback, seg):
     """Many short segments exercise the chained hand-off and the decoupled
     look-back (aggregates, walks over several predecessors)."""
+    from selective_state_space_38_amd import fwd_plan
     wl = "mamba130m" if tag == "f32" else "mamba2p8b"
     x = _case(wl, batch=2, seqlen=1000, dim=96, dstate=16, a_init="random")
     _log(f"modes {tag} lookback={lookback} seg={seg}")
     with env(SSM_FORCE_LOOKBACK=lookback, SSM_FORCE_SEGMENT=seg):
+        plan = fwd_plan(2, 1000, 96, 16, act_dtype(tag))
+        assert plan["segment_len"] == seg and plan["lookback"] == lookback, plan
         got, st = gpu_forward(x, tag)
     ref, ref_st = oracle_forward(x)
     check_forward(x, tag, got, st, ref, ref_st)
