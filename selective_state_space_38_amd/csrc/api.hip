@@ -166,7 +166,8 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   plan_forward(*dims, &plan);
   const int64_t cblk = div_up(dims->dim, 64);
   const int64_t chains = dims->batch * cblk;
-  const int64_t recs = chains * plan.segments;
+  // carry records of the split chains (whole chains need none)
+  const int64_t recs = (chains - plan.whole_chains) * plan.segments;
   if (recs * plan.state_groups > (1LL << 30) || plan.workgroups > (1LL << 31) - 1)
     return SSM_EINVAL;
 
@@ -183,18 +184,18 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const int64_t total = off_inc + inc_bytes + aggb_bytes + aggs_bytes;
 
   if (env_int("SSM_TEST_FAIL_ALLOC", 0) == 1) return SSM_ENOMEM;
-  char* scratch = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void**>(&scratch), static_cast<size_t>(total), st) !=
+  char* buf = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&buf), static_cast<size_t>(total), st) !=
           hipSuccess ||
-      !scratch)
+      !buf)
     return SSM_ENOMEM;
 
   ssm::FwdScratch sc;
-  sc.ticket = reinterpret_cast<int*>(scratch);
+  sc.ticket = reinterpret_cast<int*>(buf);
   sc.status = sc.ticket + 1;
-  sc.inc = reinterpret_cast<float*>(scratch + off_inc);
-  sc.agg_b = reinterpret_cast<float*>(scratch + off_inc + inc_bytes);
-  sc.agg_s = reinterpret_cast<float*>(scratch + off_inc + inc_bytes + aggb_bytes);
+  sc.inc = reinterpret_cast<float*>(buf + off_inc);
+  sc.agg_b = reinterpret_cast<float*>(buf + off_inc + inc_bytes);
+  sc.agg_s = reinterpret_cast<float*>(buf + off_inc + inc_bytes + aggb_bytes);
   sc.spin_limit = env_int("SSM_TEST_SPIN_LIMIT", kDefaultSpinLimit);
   sc.ckpt = ckpt;
   sc.ysave = ckpt ? reinterpret_cast<float*>(reinterpret_cast<char*>(ckpt) + ckpt_y_offset(dims))
@@ -246,7 +247,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
                                              sh, plan.workgroups, st);
     if (el != hipSuccess) rc = SSM_ELAUNCH;
   }
-  if (hipFreeAsync(scratch, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
+  if (hipFreeAsync(buf, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
   return rc;
 }
 

@@ -172,7 +172,10 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
   const int64_t t_end = (t_begin + seg_len_c < L) ? t_begin + seg_len_c : L;
   const int n_chunks = static_cast<int>((t_end - t_begin + TC - 1) / TC);
   const int64_t row0 = static_cast<int64_t>(b) * L;  // row of (b, t=0)
-  const int rec = chain * sh.n_seg + seg;
+  // carry records exist for split chains only: rec0 is this chain's first
+  // (whole chains never publish or read one)
+  const int rec0 = whole ? 0 : (chain - sh.n_full) * sh.n_seg;
+  const int rec = rec0 + seg;
   // Barrier-separated iterations of a pass after its prologue: one per chunk,
   // plus one for the last chunk's outputs, rounded up to even (see the
   // helpers' loop); both roles run exactly this many.
@@ -617,7 +620,6 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     float acc_b[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc_b[g] = 0.0f;
-    const int rec0 = chain * sh.n_seg;
     constexpr int kWin = 8;
     int j = rec - 1;
     int spins = 0;

@@ -14,8 +14,9 @@ namespace ssm {
 constexpr int kBwdChunk = 8;
 
 // Carry records exchanged between sequence segments of one channel block.
-// A record is indexed by rec = chain * n_seg + seg, and split per state group
-// (one wave per group), so every wave publishes and consumes its own part.
+// Only split chains (chain >= n_full) have records: a record is indexed by
+// rec = (chain - n_full) * n_seg + seg, and split per state group (one wave
+// per group), so every wave publishes and consumes its own part.
 struct FwdScratch {
   int* ticket;       // [1] work-order counter (zeroed before launch)
   int* status;       // [recs][groups] 0 empty, 1 aggregate, 2 inclusive
