@@ -70,7 +70,9 @@ typedef enum {
   SSM_EALIGN = -3,   /* a pointer is not 4-byte aligned */
   SSM_ENOMEM = -4,   /* scratch allocation failed */
   SSM_ELAUNCH = -5,  /* the HIP runtime rejected a launch */
-  SSM_ETIMEOUT = -6  /* a carry wait exceeded its bound (see ssm_check_device_errors) */
+  SSM_ETIMEOUT = -6, /* a carry wait exceeded its bound (see ssm_check_device_errors) */
+  SSM_ESCRATCH = -7  /* selective_scan_fwd_noalloc: the call needs more carry scratch than
+                        its static array holds */
 } ssm_status;
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -116,6 +118,32 @@ int selective_scan_fwd_h0(const void* u, const void* delta, const float* A,
                           const void* z, const float* dt_bias, int softplus,
                           const float* h0, void* out, float* last_state,
                           const ssm_dims* dims, void* stream);
+
+/*
+ * As selective_scan_fwd_h0, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The call allocates and frees nothing (no hipMalloc, hipFree or
+ * allocating library routine): its carry scratch (the work-order ticket,
+ * status words and segment carry records) lives in a static device array of
+ * 32 MiB that each GPU the library runs on holds until the process ends.
+ * The first call on a device looks up that device's copy of the array; the
+ * array's words that must start at zero are cleared by a fill kernel on
+ * `stream` at every call.
+ *   - A call whose launch plan needs more than 32 MiB of carry scratch
+ *     returns SSM_ESCRATCH before any HIP call (plans with few segment
+ *     carries need almost none: the 2.8B-shaped layer ~2.4 MB, the
+ *     million-token sequence ~4.5 MB at d_state 16).
+ *   - Every call on one GPU shares that GPU's array and the array keeps the
+ *     last call's contents: calls that overlap on one GPU (different
+ *     streams or host threads without ordering between them) race on it and
+ *     give wrong results.  Calls ordered on one stream are safe.
+ * Arguments, layouts, results and the other errors as selective_scan_fwd_h0.
+ */
+int selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A,
+                               const void* B, const void* C, const float* D,
+                               const void* z, const float* dt_bias, int softplus,
+                               const float* h0, void* out, float* last_state,
+                               const ssm_dims* dims, void* stream);
 
 /*
  * As selective_scan_fwd_h0 with the input discretisation `bbar` (an

@@ -22,6 +22,7 @@ SSM_BBAR_ZOH = 1
 EXPORTED = (
     "selective_scan_fwd",
     "selective_scan_fwd_h0",
+    "selective_scan_fwd_noalloc",
     "selective_scan_fwd_ex",
     "selective_scan_bwd",
     "selective_scan_fwd_train",
@@ -124,6 +125,8 @@ def load():
     lib.selective_scan_fwd_h0.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                           vp, vp, vp, dims_p, vp]
     lib.selective_scan_fwd_h0.restype = ctypes.c_int
+    lib.selective_scan_fwd_noalloc.argtypes = lib.selective_scan_fwd_h0.argtypes
+    lib.selective_scan_fwd_noalloc.restype = ctypes.c_int
     lib.selective_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                           vp, ctypes.c_int, vp, vp, dims_p, vp]
     lib.selective_scan_fwd_ex.restype = ctypes.c_int

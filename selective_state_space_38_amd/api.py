@@ -72,7 +72,7 @@ def ckpt_buffer(u, dstate):
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                        delta_softplus=True, return_last_state=False, h0=None,
-                       out=None, last_state=None, bbar="delta", ckpt=None):
+                       out=None, last_state=None, bbar="delta", ckpt=None, no_alloc=False):
     """Selective-scan forward on the GPU.
 
     u, delta, z: [batch, L, dim]; B, C: [batch, L, dstate] (float32 or
@@ -81,11 +81,16 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return_last_state, the float32 final state [batch, dim, dstate].
     bbar: "delta" (Bbar = Delta*B) or "zoh" (exact zero-order hold,
     (exp(Delta A) - 1)/A * B).  ckpt: a buffer from ckpt_buffer() to keep the
-    backward's checkpoints (training mode; Delta*B only).
+    backward's checkpoints (training mode; Delta*B only).  no_alloc: use the
+    entry point that allocates nothing (selective_scan_fwd_noalloc: its carry
+    scratch is a static per-device array, so overlapping calls on one GPU
+    race; Delta*B only, no checkpoints).
     """
     code = _bbar_code(bbar)
     if ckpt is not None and code != _lib.SSM_BBAR_DELTA:
         raise ValueError("checkpoints are kept for the Delta*B input only")
+    if no_alloc and (ckpt is not None or code != _lib.SSM_BBAR_DELTA):
+        raise ValueError("no_alloc covers the Delta*B forward without checkpoints only")
     if u.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {u.dtype}")
     bsz, L, dim = u.shape
@@ -120,6 +125,11 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                 _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                 _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(out),
                 _ptr(last_state), _ptr(ckpt), ctypes.byref(dims), _stream(dev))
+        elif no_alloc:
+            rc = lib.selective_scan_fwd_noalloc(
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(out),
+                _ptr(last_state), ctypes.byref(dims), _stream(dev))
         elif code == _lib.SSM_BBAR_DELTA:
             rc = lib.selective_scan_fwd_h0(
                 _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),

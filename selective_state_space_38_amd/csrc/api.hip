@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/ssm_scan.h"
@@ -13,6 +15,35 @@ namespace {
 
 constexpr int kDefaultSpinLimit = 1 << 24;
 constexpr int64_t kComputeUnits = 256;  // MI355X (gfx950)
+
+// Scratch of the allocation-free forward (selective_scan_fwd_noalloc): the
+// ticket, status words and carry records of one call, in an array that every
+// device the library runs on holds (its own copy, at its own address) until
+// the process ends.  In host code `scratch` is only a stand-in for the
+// symbol: its device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and only that address is passed to
+// kernels.  Calls on one device share the array, so calls that overlap on a
+// device race on it.
+constexpr int64_t kStaticScratchBytes = int64_t{32} << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// This device's address of `scratch` (set-up on the device's first call).
+int static_scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSM_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSM_ELAUNCH;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return SSM_OK;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -148,7 +179,7 @@ int64_t ckpt_y_offset(const ssm_dims* dims) { return div_up(ckpt_state_bytes(dim
 int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
              const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
              int bbar, void* out, float* last_state, float* ckpt, const ssm_dims* dims,
-             void* stream, bool no_out = false) {
+             void* stream, bool no_out = false, bool no_alloc = false) {
   int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
   if (bbar != SSM_BBAR_DELTA && bbar != SSM_BBAR_ZOH) return SSM_EINVAL;
@@ -183,12 +214,21 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const int64_t aggs_bytes = plan.lookback ? up256(recs * plan.state_groups * 64 * 4) : 0;
   const int64_t total = off_inc + inc_bytes + aggb_bytes + aggs_bytes;
 
-  if (env_int("SSM_TEST_FAIL_ALLOC", 0) == 1) return SSM_ENOMEM;
   char* buf = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void**>(&buf), static_cast<size_t>(total), st) !=
-          hipSuccess ||
-      !buf)
-    return SSM_ENOMEM;
+  if (no_alloc) {
+    // the static array: nothing is allocated or freed by this call
+    if (total > kStaticScratchBytes) return SSM_ESCRATCH;
+    void* addr = nullptr;
+    rc = static_scratch_address(&addr);
+    if (rc != SSM_OK) return rc;
+    buf = static_cast<char*>(addr);
+  } else {
+    if (env_int("SSM_TEST_FAIL_ALLOC", 0) == 1) return SSM_ENOMEM;
+    if (hipMallocAsync(reinterpret_cast<void**>(&buf), static_cast<size_t>(total), st) !=
+            hipSuccess ||
+        !buf)
+      return SSM_ENOMEM;
+  }
 
   ssm::FwdScratch sc;
   sc.ticket = reinterpret_cast<int*>(buf);
@@ -247,7 +287,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
                                              sh, plan.workgroups, st);
     if (el != hipSuccess) rc = SSM_ELAUNCH;
   }
-  if (hipFreeAsync(buf, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
+  if (!no_alloc && hipFreeAsync(buf, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
   return rc;
 }
 
@@ -609,6 +649,14 @@ int selective_scan_fwd_h0(const void* u, const void* delta, const float* A, cons
                   last_state, nullptr, dims, stream);
 }
 
+int selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A,
+                               const void* B, const void* C, const float* D, const void* z,
+                               const float* dt_bias, int softplus, const float* h0, void* out,
+                               float* last_state, const ssm_dims* dims, void* stream) {
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, SSM_BBAR_DELTA, out,
+                  last_state, nullptr, dims, stream, /*no_out=*/false, /*no_alloc=*/true);
+}
+
 int selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
                           const void* C, const float* D, const void* z, const float* dt_bias,
                           int softplus, const float* h0, int bbar, void* out,
@@ -699,6 +747,9 @@ const char* ssm_status_string(int status) {
     case SSM_ENOMEM: return "SSM_ENOMEM: scratch allocation failed";
     case SSM_ELAUNCH: return "SSM_ELAUNCH: kernel launch failed";
     case SSM_ETIMEOUT: return "SSM_ETIMEOUT: a segment carry wait hit its bound";
+    case SSM_ESCRATCH:
+      return "SSM_ESCRATCH: the call needs more carry scratch than the allocation-free "
+             "entry point's static array holds (32 MiB)";
     default: return "SSM_UNKNOWN: unknown status code";
   }
 }

@@ -64,7 +64,7 @@ def test_probe_validation():
 
 
 def test_status_strings():
-    for rc in (0, -1, -2, -3, -4, -5, -6):
+    for rc in (0, -1, -2, -3, -4, -5, -6, -7):
         s = _lib.status_string(rc)
         assert s.startswith("SSM_")
     assert "UNKNOWN" in _lib.status_string(12345)
@@ -254,3 +254,25 @@ def test_training_pair_validation():
                                      P[5], None, None, P[6], P[7], P[8], P[9], P[10], None,
                                      None, None, None, ctypes.byref(d), None)
     assert rc == SSM_EINVAL            # ckpt is required
+
+
+def _fwd_noalloc(dims):
+    lib = _lib.load()
+    return lib.selective_scan_fwd_noalloc(P[0], P[1], P[2], P[3], P[4], None, None, None, 1,
+                                          None, P[5], None, ctypes.byref(dims), None)
+
+
+def test_noalloc_validates_like_the_allocating_forward():
+    assert _fwd_noalloc(_dims(L=0)) == SSM_EINVAL
+    assert _fwd_noalloc(_dims(dtype=3)) == SSM_EDTYPE
+    assert _fwd_noalloc(_dims(n=5)) == SSM_EINVAL
+
+
+def test_noalloc_rejects_plans_beyond_its_static_scratch(monkeypatch):
+    """16-step look-back segments over 65536 steps and 4 channel blocks need
+    16384 carry records (~150 MB): refused on the host with SSM_ESCRATCH,
+    before any HIP call."""
+    monkeypatch.setenv("SSM_FORCE_LOOKBACK", "1")
+    monkeypatch.setenv("SSM_FORCE_SEGMENT", "16")
+    assert _fwd_noalloc(_dims(b=1, L=65536, d=256, n=16)) == -7
+    assert "SSM_ESCRATCH" in _lib.status_string(-7)
