@@ -311,6 +311,7 @@ int state_update_impl(float* state, const void* x, const void* dt, const float* 
   if (ssm::launch_state_update(dims->dtype, static_cast<int>(dims->dstate), state, x, dt, A, B,
                                C, D, z, dt_bias, softplus ? 1 : 0, bbar == SSM_BBAR_ZOH ? 1 : 0,
                                out, dims->batch, dims->dim,
+                               env_int("SSM_FORCE_DECODE_ROWS", 0),
                                static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSM_ELAUNCH;
   return SSM_OK;

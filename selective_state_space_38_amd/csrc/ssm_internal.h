@@ -89,12 +89,14 @@ SSM_DECLARE_FWD(fwd_f32)
 SSM_DECLARE_FWD(fwd_bf16)
 #undef SSM_DECLARE_FWD
 
+// rows_override > 0 fixes the batch rows each workgroup walks (tuning);
+// otherwise one row per workgroup.
 hipError_t launch_state_update(int dtype, int dstate, float* state,
                                const void* x, const void* dt, const float* A,
                                const void* B, const void* C, const float* D,
                                const void* z, const float* dt_bias,
                                int softplus, int zoh, void* out, int64_t batch,
-                               int64_t dim, hipStream_t stream);
+                               int64_t dim, int rows_override, hipStream_t stream);
 
 // Backward: inputs, outputs and scratch of one call.  Activations and their
 // gradients (u, delta, z, dout, du, ddelta, dz, B, C, dB, dC) are of the call's

@@ -8,9 +8,9 @@
 // guide's Method, (exp(Delta A) - 1) / A * B * x.
 //
 // The step is a pure read-modify-write stream over the float32 state, so it
-// is laid out for HBM (see the kernel comment).  The shuffle partners of a
-// lane are always in range: total = B*D*LPC is a multiple of LPC, which
-// divides 64.
+// is laid out for HBM (see the kernel comment).  The exchange partners of a
+// lane are always in range: a channel's LPC lanes are aligned neighbours
+// within one wave (LPC divides 64).
 
 #include "ssm_device.h"
 #include "ssm_internal.h"
@@ -19,116 +19,178 @@ namespace ssm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// One lane owns Q = min(N, 8) consecutive states of one channel (two 16-byte
-// vector loads and stores), the N/Q lanes of a channel are neighbours and
-// reduce the readout C . h with shuffles.  The state is streamed once, so it
-// is read and written with non-temporal hints.  (4 and 16 states per lane
-// measured slower: 16 makes the per-instruction accesses of a wave strided.)
-// VBC: B and C are aligned for the same vector loads (8 bytes per 4 bfloat16,
-// 16 per 4 float32); otherwise they are read element by element.
-constexpr int kDecodeStatesPerLane = 8;
+// Layout.  For N >= 4 a lane holds G = 2 vectors of Q = 4 consecutive
+// states; a channel's N states are spread over LPC = N/4 neighbouring lanes,
+// which reduce the readout C . h with DPP exchanges.  Vector g of lane l is
+// vector g*64 + l of the wave's run of 2*64 vectors, so each state load or
+// store instruction of the wave covers one dense 1 KB run (every 64-byte line
+// fully used by one instruction), and the two vectors are independent work in
+// flight.  The lane's two vectors belong to two channels of the wave's
+// 128/LPC.  A workgroup (four waves) owns 512/LPC consecutive channels of
+// one batch row (the launcher can give it a run of rows; a lane then keeps
+// its channels' A, scaled by log2 e, dt_bias and D for all of them).  The
+// state is read once and written once (non-temporal).  Many short
+// workgroups hide the state's memory latency better than longer ones.  For
+// N < 4 a lane holds one channel's N states.
+// VBC: B and C are aligned for vector loads (8 bytes per 4 bfloat16, 16 per 4
+// float32); otherwise they are read element by element.
+// (Measured variants that did not pay at the 256 x 5120 x 16 step: four
+// vectors per lane, 36-38 us; the two vectors as one channel in two rows,
+// 35 us; one lane per channel with its N states as 8-state halves, whose
+// 16-byte accesses half-fill every line per instruction, 41-44 us; more than
+// one row per workgroup, slower from 4 rows on.)
+template <int N>
+struct DecodeShape {
+  static constexpr int Q = N < 4 ? N : 4;        // states per vector
+  static constexpr int LPC = N / Q;              // lanes per channel: 1, 2, 4, 8, 16
+  static constexpr int G = N < 4 ? 1 : 2;        // vectors (channel groups) per lane
+  static constexpr int CPW = G * 64 / LPC;       // channels per wave
+  static constexpr int CPB = 4 * CPW;            // channels per workgroup of 256
+};
+
 template <typename T, int N, bool ZOH, bool VBC>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ x, const T* __restrict__ dtp,
     const float* __restrict__ A, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ Dv, const T* __restrict__ zp,
     const float* __restrict__ bias, int softplus, T* __restrict__ out,
-    int64_t batch, int64_t dim) {
-  constexpr int Q = N < kDecodeStatesPerLane ? N : kDecodeStatesPerLane;
-  constexpr int LPC = N / Q;               // lanes per channel
-  constexpr int NV = Q >= 4 ? Q / 4 : 0;   // 16-byte vectors per lane
-  const int64_t total = batch * dim * LPC;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t ic = i < total ? i : total - 1;
-  const int64_t bd = ic / LPC;
-  const int q = static_cast<int>(ic - bd * LPC);
-  const int64_t b = bd / dim;
-  const int64_t d = bd - b * dim;
-
-  float h[Q];
-  float* hp = state + bd * N + q * Q;
-  if constexpr (NV > 0) {
+    int64_t batch, int64_t dim, int rows_per_block) {
+  using S = DecodeShape<N>;
+  constexpr int Q = S::Q, LPC = S::LPC, G = S::G;
+  constexpr bool kVec = Q == 4;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int wave = static_cast<int>(threadIdx.x) >> 6;
+  const int q = lane % LPC;                      // which Q states of the channel
+  const int64_t c_wave = static_cast<int64_t>(blockIdx.x) * S::CPB + wave * S::CPW;
+  int64_t dch[G];
+  bool dvalid[G];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const f32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp) + v);
-      h[4 * v] = hv.x; h[4 * v + 1] = hv.y; h[4 * v + 2] = hv.z; h[4 * v + 3] = hv.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < Q; ++j) h[j] = __builtin_nontemporal_load(hp + j);
+  for (int g = 0; g < G; ++g) {
+    const int64_t dr = c_wave + g * (64 / LPC) + lane / LPC;
+    dvalid[g] = dr < dim;
+    dch[g] = dvalid[g] ? dr : dim - 1;           // tail lanes compute, never store
   }
-  const float s = to_f32(dtp[bd]) + (bias ? bias[d] : 0.0f);
-  const float dl = softplus ? softplus_f32(s) : s;
-  const float xv = to_f32(x[bd]);
-  const float du = dl * xv;
-  const float* ap = A + d * N + q * Q;
-  const T* bp = Bm + b * N + q * Q;
-  const T* cp = Cm + b * N + q * Q;
-  float a2[Q], bv[Q], cv[Q];
-  if constexpr (NV > 0) {
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * rows_per_block;
+  const int64_t b1 = b0 + rows_per_block < batch ? b0 + rows_per_block : batch;
+
+  // the channels' constants
+  float a2[G][Q], ia[G][Q], bs[G], dd[G];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const float4 av = reinterpret_cast<const float4*>(ap)[v];
-      a2[4 * v] = av.x; a2[4 * v + 1] = av.y; a2[4 * v + 2] = av.z; a2[4 * v + 3] = av.w;
-      if constexpr (!VBC) {
+  for (int g = 0; g < G; ++g) {
+    const float* ap = A + dch[g] * N + q * Q;
+    float av[Q];
+    if constexpr (kVec) {
+      const float4 w4 = *reinterpret_cast<const float4*>(ap);
+      av[0] = w4.x; av[1] = w4.y; av[2] = w4.z; av[3] = w4.w;
+    } else {
 #pragma unroll
-        for (int j = 4 * v; j < 4 * v + 4; ++j) {
-          bv[j] = to_f32(bp[j]);
-          cv[j] = to_f32(cp[j]);
-        }
-      } else if constexpr (sizeof(T) == 2) {
-        const uint2 bw = reinterpret_cast<const uint2*>(bp)[v];
-        const uint2 cw = reinterpret_cast<const uint2*>(cp)[v];
-        bv[4 * v] = __uint_as_float(bw.x << 16); bv[4 * v + 1] = __uint_as_float(bw.x & 0xffff0000u);
-        bv[4 * v + 2] = __uint_as_float(bw.y << 16); bv[4 * v + 3] = __uint_as_float(bw.y & 0xffff0000u);
-        cv[4 * v] = __uint_as_float(cw.x << 16); cv[4 * v + 1] = __uint_as_float(cw.x & 0xffff0000u);
-        cv[4 * v + 2] = __uint_as_float(cw.y << 16); cv[4 * v + 3] = __uint_as_float(cw.y & 0xffff0000u);
-      } else {
-        const float4 bw = reinterpret_cast<const float4*>(bp)[v];
-        const float4 cw = reinterpret_cast<const float4*>(cp)[v];
-        bv[4 * v] = bw.x; bv[4 * v + 1] = bw.y; bv[4 * v + 2] = bw.z; bv[4 * v + 3] = bw.w;
-        cv[4 * v] = cw.x; cv[4 * v + 1] = cw.y; cv[4 * v + 2] = cw.z; cv[4 * v + 3] = cw.w;
-      }
+      for (int j = 0; j < Q; ++j) av[j] = ap[j];
     }
-  } else {
 #pragma unroll
     for (int j = 0; j < Q; ++j) {
-      a2[j] = ap[j];
-      bv[j] = to_f32(bp[j]);
-      cv[j] = to_f32(cp[j]);
+      a2[g][j] = av[j] * kLog2e;
+      ia[g][j] = ZOH ? 1.0f / av[j] : 0.0f;
     }
+    bs[g] = bias ? bias[dch[g]] : 0.0f;
+    dd[g] = Dv ? Dv[dch[g]] : 0.0f;
   }
-  float y = 0.0f;
-#pragma unroll
-  for (int j = 0; j < Q; ++j) {
-    const float x2 = dl * (a2[j] * kLog2e);
-    const float a = exp2_hw(x2);
-    if constexpr (ZOH) {
-      h[j] = fmaf(a, h[j], zoh_coef(x2, a, dl, 1.0f / a2[j]) * (xv * bv[j]));
-    } else {
-      h[j] = fmaf(a, h[j], du * bv[j]);
-    }
-    y = fmaf(cv[j], h[j], y);
-  }
-  if (i < total) {
-    if constexpr (NV > 0) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const f32x4 hv = {h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
-        __builtin_nontemporal_store(hv, reinterpret_cast<f32x4*>(hp) + v);
+
+  for (int64_t b = b0; b < b1; ++b) {
+    // B and C of the row (the same Q states for every channel group)
+    const T* bp = Bm + b * N + q * Q;
+    const T* cp = Cm + b * N + q * Q;
+    float bv[Q], cv[Q];
+    if constexpr (kVec && VBC) {
+      if constexpr (sizeof(T) == 2) {
+        const uint2 bw = *reinterpret_cast<const uint2*>(bp);
+        const uint2 cw = *reinterpret_cast<const uint2*>(cp);
+        bv[0] = __uint_as_float(bw.x << 16); bv[1] = __uint_as_float(bw.x & 0xffff0000u);
+        bv[2] = __uint_as_float(bw.y << 16); bv[3] = __uint_as_float(bw.y & 0xffff0000u);
+        cv[0] = __uint_as_float(cw.x << 16); cv[1] = __uint_as_float(cw.x & 0xffff0000u);
+        cv[2] = __uint_as_float(cw.y << 16); cv[3] = __uint_as_float(cw.y & 0xffff0000u);
+      } else {
+        const float4 bw = *reinterpret_cast<const float4*>(bp);
+        const float4 cw = *reinterpret_cast<const float4*>(cp);
+        bv[0] = bw.x; bv[1] = bw.y; bv[2] = bw.z; bv[3] = bw.w;
+        cv[0] = cw.x; cv[1] = cw.y; cv[2] = cw.z; cv[3] = cw.w;
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < Q; ++j) __builtin_nontemporal_store(h[j], hp + j);
+      for (int j = 0; j < Q; ++j) {
+        bv[j] = to_f32(bp[j]);
+        cv[j] = to_f32(cp[j]);
+      }
     }
-  }
-  // reduce the partial readouts of the channel's LPC neighbouring lanes
+    float h[G][Q];
+    float* hp[G];
 #pragma unroll
-  for (int off = 1; off < LPC; off <<= 1) y += __shfl_xor(y, off, 64);
-  if (i < total && q == 0) {
-    y += (Dv ? Dv[d] : 0.0f) * xv;
-    if (zp) y = silu_gate(y, to_f32(zp[bd]));
-    store_act(out, bd, y);
+    for (int g = 0; g < G; ++g) {
+      hp[g] = state + (b * dim + dch[g]) * N + q * Q;
+      if constexpr (kVec) {
+        const f32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp[g]));
+        h[g][0] = hv.x; h[g][1] = hv.y; h[g][2] = hv.z; h[g][3] = hv.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < Q; ++j) h[g][j] = __builtin_nontemporal_load(hp[g] + j);
+      }
+    }
+    float xv[G], y[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t bd = b * dim + dch[g];
+      const float s = to_f32(dtp[bd]) + bs[g];
+      const float dl = softplus ? softplus_f32(s) : s;
+      xv[g] = to_f32(x[bd]);
+      const float du = dl * xv[g];
+      float yy = 0.0f;
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+        const float x2 = dl * a2[g][j];
+        const float a = exp2_hw(x2);
+        if constexpr (ZOH) {
+          h[g][j] = fmaf(a, h[g][j], zoh_coef(x2, a, dl, ia[g][j]) * (xv[g] * bv[j]));
+        } else {
+          h[g][j] = fmaf(a, h[g][j], du * bv[j]);
+        }
+        yy = fmaf(cv[j], h[g][j], yy);
+      }
+      y[g] = yy;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (dvalid[g]) {
+        if constexpr (kVec) {
+          const f32x4 hv = {h[g][0], h[g][1], h[g][2], h[g][3]};
+          __builtin_nontemporal_store(hv, reinterpret_cast<f32x4*>(hp[g]));
+        } else {
+#pragma unroll
+          for (int j = 0; j < Q; ++j) __builtin_nontemporal_store(h[g][j], hp[g] + j);
+        }
+      }
+    }
+    // the partial readouts of each channel's LPC neighbouring lanes (every
+    // lane of the wave takes part: the row loop is uniform over the workgroup)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float v = y[g];
+      if constexpr (LPC == 2) {
+        v = pair_sum(v);
+      } else if constexpr (LPC >= 4) {
+        v = quad_sum(v);
+        if constexpr (LPC >= 8) v += __shfl_xor(v, 4, 64);
+        if constexpr (LPC >= 16) v += __shfl_xor(v, 8, 64);
+      }
+      y[g] = v;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (dvalid[g] && q == 0) {
+        const int64_t bd = b * dim + dch[g];
+        float v = y[g] + dd[g] * xv[g];
+        if (zp) v = silu_gate(v, to_f32(zp[bd]));
+        store_act(out, bd, v);
+      }
+    }
   }
 }
 
@@ -136,22 +198,34 @@ template <typename T>
 static hipError_t launch_n(int n, float* state, const void* x, const void* dt, const float* A,
                            const void* B, const void* C, const float* D, const void* z,
                            const float* bias, int softplus, int zoh, void* out, int64_t batch,
-                           int64_t dim, hipStream_t stream) {
+                           int64_t dim, int decode_rows_override, hipStream_t stream) {
   // B and C rows start at b * N elements: vector loads need the base aligned
   // to 4 elements (N >= 4 keeps every row start aligned with it)
   const uintptr_t vec_bytes = 4 * sizeof(T);
   const bool vbc = reinterpret_cast<uintptr_t>(B) % vec_bytes == 0 &&
                    reinterpret_cast<uintptr_t>(C) % vec_bytes == 0;
-  const int q = n < kDecodeStatesPerLane ? n : kDecodeStatesPerLane;
-  const int64_t total = batch * dim * (n / q);
+  const int q = n < 4 ? n : 4;                          // states per vector
+  const int64_t cpb = 4 * (n < 4 ? 1 : 2) * 64 / (n / q);  // channels per workgroup
+  const int64_t cblocks = (dim + cpb - 1) / cpb;
+  // rows per workgroup: one (many short workgroups hide the state's latency
+  // best: 1 row measured faster than 2, 4, 8 and 16 at the 256 x 5120 x 16
+  // decode step), more only where the grid height would pass its limit
+  int64_t rows = 1;
+  if (decode_rows_override > 0) rows = decode_rows_override;
+  if (rows < 1) rows = 1;
+  if (rows > batch) rows = batch;
+  const int64_t min_rows = (batch + 65534) / 65535;
+  if (rows < min_rows) rows = min_rows;
+  const int64_t rblocks = (batch + rows - 1) / rows;
   const int threads = 256;
-  const int64_t blocks = (total + threads - 1) / threads;
-  const dim3 grid(static_cast<unsigned>(blocks));
+  const dim3 grid(static_cast<unsigned>(cblocks), static_cast<unsigned>(rblocks));
+  const int rows_per_block = static_cast<int>(rows);
 #define SSM_LAUNCH_SU_ZV(NN, Z, V)                                                              \
   hipLaunchKernelGGL((state_update_kernel<T, NN, Z, V>), grid, dim3(threads), 0, stream, state, \
                      static_cast<const T*>(x), static_cast<const T*>(dt), A,                    \
                      static_cast<const T*>(B), static_cast<const T*>(C), D,                     \
-                     static_cast<const T*>(z), bias, softplus, static_cast<T*>(out), batch, dim)
+                     static_cast<const T*>(z), bias, softplus, static_cast<T*>(out), batch, dim, \
+                     rows_per_block)
 #define SSM_LAUNCH_SU_Z(NN, Z)          \
   if (vbc) {                            \
     SSM_LAUNCH_SU_ZV(NN, Z, true);      \
@@ -184,12 +258,12 @@ hipError_t launch_state_update(int dtype, int dstate, float* state, const void* 
                                const void* dt, const float* A, const void* B, const void* C,
                                const float* D, const void* z, const float* dt_bias,
                                int softplus, int zoh, void* out, int64_t batch, int64_t dim,
-                               hipStream_t stream) {
+                               int rows_override, hipStream_t stream) {
   if (dtype == 0)
     return launch_n<float>(dstate, state, x, dt, A, B, C, D, z, dt_bias, softplus, zoh, out,
-                           batch, dim, stream);
+                           batch, dim, rows_override, stream);
   return launch_n<bf16_t>(dstate, state, x, dt, A, B, C, D, z, dt_bias, softplus, zoh, out,
-                          batch, dim, stream);
+                          batch, dim, rows_override, stream);
 }
 
 }  // namespace ssm
