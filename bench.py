@@ -27,6 +27,7 @@ import argparse
 import ctypes
 import json
 import os
+import re
 import sys
 import time
 
@@ -117,6 +118,15 @@ def parse():
     p.add_argument("--l-sweep", action="store_true",
                    help="instead of the step: time the forward alone over L = 2^10 .. 2^20 "
                         "at B=1, D=256, N=16, float32 (one JSON line per L)")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="host only: read the rocprofv3 --pmc CSVs of a FETCH_SIZE run and a "
+                        "WRITE_SIZE run of this benchmark, calibrate them against the copy "
+                        "probe's known bytes and write profiles/scan_fwd_traffic_<workload>.json "
+                        "per forward workload (and the decode's); prints a markdown table")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="host only: per-dispatch durations from a rocprofv3 --kernel-trace run "
+                        "of this benchmark, grouped by kernel and grid (so workloads that share "
+                        "a kernel instance stay apart); prints a markdown table")
     p.add_argument("--micro", action="store_true",
                    help="instead of the step: the ceiling probes alone (VALU rates at 1-8 "
                         "waves per SIMD, the full streaming sweep); one JSON line")
@@ -136,7 +146,8 @@ def traffic_file(workload):
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_38_amd", "csrc", f)
-                  for f in ("scan_fwd.hip", "ssm_device.h", "ssm_internal.h", "api.hip")]
+                  for f in ("scan_fwd.hip", "state_update.hip", "ssm_device.h", "ssm_internal.h",
+                            "api.hip")]
 
 
 def kernel_source_digest():
@@ -693,8 +704,147 @@ def time_forward(torch, dev, w, steps, warmup, bbar="delta"):
     return ms, n_sets
 
 
+# ------------------------------------------------- counter summaries --
+
+def _counter_rows(directory):
+    """(kernel name, grid size, counter, value) of every dispatch in the
+    rocprofv3 counter-collection CSVs under directory."""
+    import csv
+    rows = []
+    for dirpath, _, files in os.walk(directory):
+        for f in sorted(files):
+            if not f.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(dirpath, f), newline="") as fh:
+                for r in csv.DictReader(fh):
+                    rows.append((r["Kernel_Name"], int(r["Grid_Size"]), r["Counter_Name"],
+                                 float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
+    summed over the device's channels), each scaled by what the same counter
+    read for the copy probe's 1 GiB copy (2^30 bytes read and written)."""
+    from selective_state_space_38_amd import fwd_plan
+    fetch = _counter_rows(fetch_dir)
+    write = _counter_rows(write_dir)
+    copy_bytes = 1 << 30
+
+    def per_kernel(rows, counter):
+        out = {}
+        for name, grid, cname, val in rows:
+            if cname != counter:
+                continue
+            out.setdefault((name, grid), []).append(val)
+        return out
+
+    fk, wk = per_kernel(fetch, "FETCH_SIZE"), per_kernel(write, "WRITE_SIZE")
+
+    def copy_probe(d):
+        vals = [v for (n, g), vs in d.items() if "stream_probe<2," in n for v in vs]
+        return float(np.median(vals)) if vals else None
+
+    cf, cw = copy_probe(fk), copy_probe(wk)
+    if not cf or not cw:
+        raise SystemExit("no copy-probe dispatches (stream_probe<2, ...>) in the counter CSVs")
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    digest = kernel_source_digest()
+    table = ["| kernel (workload) | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated bytes | "
+             "algorithmic bytes | ratio |", "|---|---|---|---|---|---|"]
+
+    def entry(name_key, grid, w, label):
+        fv = [v for (n, g), vs in fk.items() if name_key in n and g == grid for v in vs]
+        wv = [v for (n, g), vs in wk.items() if name_key in n and g == grid for v in vs]
+        if not fv or not wv:
+            return None
+        kname = next(n for (n, g) in fk if name_key in n and g == grid)
+        fb = float(np.mean(fv)) * 1024.0 * f_scale
+        wb = float(np.mean(wv)) * 1024.0 * w_scale
+        alg = synth.algorithmic_bytes(w)
+        m = re.match(r"(.*?>)\(", kname)
+        short = m.group(1) if m else kname.split("(")[0]
+        table.append(f"| `{short}` ({label}) | {np.mean(fv):,.0f} | "
+                     f"{np.mean(wv):,.0f} | {fb + wb:,.0f} | {alg:,} | {(fb + wb) / alg:.3f} |")
+        return {"kernel": kname, "grid_size": grid,
+                "counters_KiB_per_dispatch": {"FETCH_SIZE": fv, "WRITE_SIZE": wv},
+                "hbm_fetch_bytes_per_launch": fb, "hbm_write_bytes_per_launch": wb,
+                "hbm_bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": alg,
+                "traffic_over_algorithmic": (fb + wb) / alg}
+
+    calib = {"probe": "ssm_micro_stream copy of 1 GiB (2^30 bytes read and written)",
+             "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw, "fetch_scale": f_scale,
+             "write_scale": w_scale}
+    for name in ("mamba2p8b", "seq1m", "mamba130m"):
+        w = synth.WORKLOADS[name]
+        import torch
+        plan = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate,
+                        torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+        threads = 64 * (plan["state_groups"] + 4)
+        ns = "fwd_bf16::scan_fwd_kernel" if w.dtype == "bf16" else "fwd_f32::scan_fwd_kernel"
+        e = entry(ns, plan["workgroups"] * threads, w, name)
+        if e is None:
+            continue
+        e.update({"workload": name, "kernel_source_sha256": digest, "copy_calibration": calib})
+        if name == "mamba2p8b":
+            dw = synth.WORKLOADS["decode"]
+            grids = sorted({g for (n, g) in fk if "state_update_kernel" in n})
+            d = entry("state_update_kernel", grids[0], dw, "decode") if grids else None
+            if d:
+                e["decode"] = d
+        with open(traffic_file(name), "w") as fh:
+            json.dump(e, fh, indent=1)
+    print("\n".join(table))
+    print(f"\ncalibration: copy probe read FETCH_SIZE = {cf:,.0f} KiB and WRITE_SIZE = "
+          f"{cw:,.0f} KiB for 2^30 bytes each way: fetch x {f_scale:.4f}, write x {w_scale:.4f}")
+
+
+def summarize_trace(directory):
+    """Average, median and minimum duration per (kernel, grid size) from the
+    kernel-trace CSVs under directory, with the forward workloads and the
+    decode named by the grid their launch plans give."""
+    import csv
+    from selective_state_space_38_amd import fwd_plan
+    groups = {}
+    for dirpath, _, files in os.walk(directory):
+        for f in sorted(files):
+            if not f.endswith("kernel_trace.csv"):
+                continue
+            with open(os.path.join(dirpath, f), newline="") as fh:
+                for r in csv.DictReader(fh):
+                    grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                    dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                    groups.setdefault((r["Kernel_Name"], grid), []).append(dur)
+    import torch
+    names = {}
+    for name in ("mamba2p8b", "seq1m", "mamba130m"):
+        w = synth.WORKLOADS[name]
+        plan = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate,
+                        torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+        ns = "fwd_bf16::" if w.dtype == "bf16" else "fwd_f32::"
+        names[(ns, plan["workgroups"] * 64 * (plan["state_groups"] + 4))] = name
+    print("| kernel | grid (threads) | workload | launches | avg us | median us | min us |")
+    print("|---|---|---|---|---|---|---|")
+    for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        label = next((n for (ns, gg), n in names.items() if ns in k and gg == g
+                      and "scan_fwd_kernel" in k), "")
+        if "state_update_kernel" in k:
+            label = "decode"
+        m = re.match(r"(.*?>)\(", k)
+        short = m.group(1) if m else k.split("(")[0]
+        print(f"| `{short}` | {g:,} | {label} | {len(v)} | {np.mean(v):.1f} | "
+              f"{np.median(v):.1f} | {np.min(v):.1f} |")
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this path runs on one GPU "
               "(no collectives, no sharding); run with --gpus 1", file=sys.stderr)
