@@ -946,6 +946,15 @@ def main():
     configs = {w.name: fwd_entry(w, fwd_ms, ceil, args.bbar, traffic)}
     configs[w.name]["plan"] = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate, act)
     if not args.no_decode:
+        # the decode in its own loop as well (inside the step it follows the
+        # forward, whose output is still draining from the caches)
+        rot = [0]
+
+        def decode_alone():
+            decode(rot[0])
+            rot[0] += 1
+
+        dec_alone = _time_ms(torch, decode_alone, args.steps, args.warmup)
         dec_avg = float(np.mean(dec_ms))
         dec_bytes = synth.algorithmic_bytes(dw)
         dgbs = dec_bytes / (dec_avg / 1e3) / 1e9
@@ -960,6 +969,17 @@ def main():
             "frac_of_measured_update_in_place": dgbs / stream["update_in_place"]["GBps"],
             "frac_of_measured_copy": dgbs / stream["copy"]["GBps"],
             "state_sets_rotated": n_rot,
+            "timing": "inside the step, right after the forward",
+        }
+        da = float(np.mean(dec_alone))
+        dagbs = dec_bytes / (da / 1e3) / 1e9
+        configs["decode"]["alone"] = {
+            "avg_ms": da, "median_ms": float(np.median(dec_alone)),
+            "min_ms": float(np.min(dec_alone)), "launches": len(dec_alone),
+            "hbm_GBps": dagbs, "hbm_frac_of_8TBps": dagbs / HBM_PEAK_GBS,
+            "frac_of_measured_update_in_place": dagbs / stream["update_in_place"]["GBps"],
+            "frac_of_measured_copy": dagbs / stream["copy"]["GBps"],
+            "timing": "back-to-back decode steps, state sets rotated",
         }
     if not args.no_extra:
         for name in ("seq1m", "mamba130m"):
