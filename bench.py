@@ -610,14 +610,34 @@ def probe_stream(torch, dev, nbytes=1 << 30, reps=5, sweep=False):
             blocks = COMPUTE_UNITS * per_cu
             ms = _ms(lambda p: lib.ssm_micro_stream(
                 mode, unroll, blocks, ctypes.c_void_p(a.data_ptr()),
-                ctypes.c_void_p(b.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), reps, p,
-                st))
+                ctypes.c_void_p(b.data_ptr()), nbytes, 1, ctypes.c_void_p(sink.data_ptr()), reps,
+                p, st))
             gbs = factor * nbytes / (ms / 1e3) / 1e9
             if best is None or gbs > best[0]:
                 best = (gbs, unroll, per_cu)
         out[name] = {"GBps": best[0], "frac_of_8TBps": best[0] / HBM_PEAK_GBS,
                      "vectors_in_flight": best[1], "workgroups_per_cu": best[2]}
     out["buffer_bytes"] = nbytes
+    # the decode step's own access pattern and size: an in-place update of
+    # one decode state (256 x 5120 x 16 float32, 84 MB), rotated over six
+    # slices so the Infinity Cache cannot hold the working set
+    dw = synth.WORKLOADS["decode"]
+    sbytes = 4 * dw.batch * dw.dim * dw.dstate
+    slices = 6
+    if slices * sbytes <= nbytes:
+        best = None
+        for unroll, per_cu in shapes:
+            blocks = COMPUTE_UNITS * per_cu
+            ms = _ms(lambda p: lib.ssm_micro_stream(
+                3, unroll, blocks, None, ctypes.c_void_p(b.data_ptr()), sbytes, slices,
+                ctypes.c_void_p(sink.data_ptr()), 3 * slices, p, st))
+            gbs = 2 * sbytes / (ms / 1e3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, unroll, per_cu)
+        out["update_in_place_decode_size"] = {
+            "GBps": best[0], "frac_of_8TBps": best[0] / HBM_PEAK_GBS,
+            "vectors_in_flight": best[1], "workgroups_per_cu": best[2],
+            "bytes_per_launch": 2 * sbytes, "slices_rotated": slices}
     del a, b
     torch.cuda.empty_cache()
     return out
@@ -968,6 +988,8 @@ def main():
             "hbm_frac_of_8TBps": dgbs / HBM_PEAK_GBS,
             "frac_of_measured_update_in_place": dgbs / stream["update_in_place"]["GBps"],
             "frac_of_measured_copy": dgbs / stream["copy"]["GBps"],
+            "frac_of_measured_update_in_place_decode_size":
+                dgbs / stream["update_in_place_decode_size"]["GBps"],
             "state_sets_rotated": n_rot,
             "timing": "inside the step, right after the forward",
         }
@@ -979,6 +1001,8 @@ def main():
             "hbm_GBps": dagbs, "hbm_frac_of_8TBps": dagbs / HBM_PEAK_GBS,
             "frac_of_measured_update_in_place": dagbs / stream["update_in_place"]["GBps"],
             "frac_of_measured_copy": dagbs / stream["copy"]["GBps"],
+            "frac_of_measured_update_in_place_decode_size":
+                dagbs / stream["update_in_place_decode_size"]["GBps"],
             "timing": "back-to-back decode steps, state sets rotated",
         }
     if not args.no_extra:

@@ -57,7 +57,10 @@ int ssm_micro_valu(int kind, int chains, int blocks, int iters, const float* see
 
 /*
  * HBM streaming probe over `bytes` (a multiple of 16; both buffers 16-byte
- * aligned and at least `bytes` long).
+ * aligned and at least slices * bytes long).  Launch i (the warm-up is launch
+ * 0) works on slice i mod `slices` of the buffers, so a working set smaller
+ * than the Infinity Cache can still be streamed from HBM (slices * bytes
+ * well above 256 MB).
  *   mode   : 0 read src; 1 write dst; 2 copy src -> dst; 3 dst += 1 per
  *            32-bit word, in place (src unused, may be NULL for 1 and 3)
  *   unroll : 1, 2, 4 or 8 vectors in flight per thread
@@ -66,7 +69,8 @@ int ssm_micro_valu(int kind, int chains, int blocks, int iters, const float* see
  * HBM bytes per launch: bytes (read, write) or 2 * bytes (copy, update).
  */
 int ssm_micro_stream(int mode, int unroll, int blocks, const void* src, void* dst,
-                     int64_t bytes, void* sink, int reps, float* ms_out, void* stream);
+                     int64_t bytes, int slices, void* sink, int reps, float* ms_out,
+                     void* stream);
 
 #ifdef __cplusplus
 }

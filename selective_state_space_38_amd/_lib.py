@@ -100,7 +100,7 @@ def load_micro():
                                    vp, ctypes.c_int, ctypes.POINTER(ctypes.c_float), vp]
     lib.ssm_micro_valu.restype = ctypes.c_int
     lib.ssm_micro_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
-                                     ctypes.c_int64, vp, ctypes.c_int,
+                                     ctypes.c_int64, ctypes.c_int, vp, ctypes.c_int,
                                      ctypes.POINTER(ctypes.c_float), vp]
     lib.ssm_micro_stream.restype = ctypes.c_int
     _micro = lib

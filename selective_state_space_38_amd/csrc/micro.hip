@@ -162,21 +162,25 @@ int ssm_micro_valu(int kind, int chains, int blocks, int iters, const float* see
 }
 
 int ssm_micro_stream(int mode, int unroll, int blocks, const void* src, void* dst,
-                     int64_t bytes, void* sink, int reps, float* ms_out, void* stream) {
+                     int64_t bytes, int slices, void* sink, int reps, float* ms_out,
+                     void* stream) {
   if (mode < 0 || mode > 3 || (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) ||
-      blocks <= 0 || bytes <= 0 || bytes % 16 != 0 || reps <= 0 || !dst || !sink || !ms_out ||
-      ((mode == 0 || mode == 2) && !src))
+      blocks <= 0 || bytes <= 0 || bytes % 16 != 0 || slices <= 0 || reps <= 0 || !dst ||
+      !sink || !ms_out || ((mode == 0 || mode == 2) && !src))
     return SSM_MICRO_EINVAL;
   if (reinterpret_cast<uintptr_t>(dst) % 16 != 0 ||
       (src && reinterpret_cast<uintptr_t>(src) % 16 != 0))
     return SSM_MICRO_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t n_vec = bytes / 16;
-  const u32x4* s = static_cast<const u32x4*>(src);
-  u32x4* d = static_cast<u32x4*>(dst);
   uint32_t* k = static_cast<uint32_t*>(sink);
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  int launch_no = 0;
   auto launch = [&]() {
+    // launch i works on slice i mod slices of the buffers
+    const int64_t off = static_cast<int64_t>(launch_no++ % slices) * n_vec;
+    const u32x4* s = src ? static_cast<const u32x4*>(src) + off : nullptr;
+    u32x4* d = static_cast<u32x4*>(dst) + off;
 #define SSM_STREAM(M, U) \
   hipLaunchKernelGGL((stream_probe<M, U>), grid, block, 0, st, s, d, n_vec, k)
 #define SSM_STREAM_U(M)                  \

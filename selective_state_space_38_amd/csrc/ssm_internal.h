@@ -89,8 +89,8 @@ SSM_DECLARE_FWD(fwd_f32)
 SSM_DECLARE_FWD(fwd_bf16)
 #undef SSM_DECLARE_FWD
 
-// rows_override > 0 fixes the batch rows each workgroup walks (tuning);
-// otherwise one row per workgroup.
+// rows_override (1, 2, 4 or 8) fixes the batch rows each workgroup walks
+// (tuning); otherwise one row per workgroup.
 hipError_t launch_state_update(int dtype, int dstate, float* state,
                                const void* x, const void* dt, const float* A,
                                const void* B, const void* C, const float* D,

@@ -26,19 +26,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // store instruction of the wave covers one dense 1 KB run (every 64-byte line
 // fully used by one instruction), and the two vectors are independent work in
 // flight.  The lane's two vectors belong to two channels of the wave's
-// 128/LPC.  A workgroup (four waves) owns 512/LPC consecutive channels of
-// one batch row (the launcher can give it a run of rows; a lane then keeps
-// its channels' A, scaled by log2 e, dt_bias and D for all of them).  The
-// state is read once and written once (non-temporal).  Many short
-// workgroups hide the state's memory latency better than longer ones.  For
-// N < 4 a lane holds one channel's N states.
+// 128/LPC.  A workgroup (four waves) owns 512/LPC consecutive channels of a
+// run of R batch rows (a lane keeps its channels' A, scaled by log2 e,
+// dt_bias and D for all of them).  The state is read once and written once
+// (non-temporal).  For N < 4 a lane holds one channel's N states.
 // VBC: B and C are aligned for vector loads (8 bytes per 4 bfloat16, 16 per 4
 // float32); otherwise they are read element by element.
 // (Measured variants that did not pay at the 256 x 5120 x 16 step: four
 // vectors per lane, 36-38 us; the two vectors as one channel in two rows,
 // 35 us; one lane per channel with its N states as 8-state halves, whose
-// 16-byte accesses half-fill every line per instruction, 41-44 us; more than
-// one row per workgroup, slower from 4 rows on.)
+// 16-byte accesses half-fill every line per instruction, 41-44 us.)
+// batch rows per workgroup (software-pipelined, see the kernel); 1, 2, 4
+// or 8 are instantiated.  At the 256 x 5120 x 16 step, 1 and 2 rows measured
+// 33.7-35 us and 4 or 8 rows 36 us: many short workgroups hide the state's
+// latency at least as well as prefetching inside longer ones.
+constexpr int kDecodeRows = 1;
+
 template <int N>
 struct DecodeShape {
   static constexpr int Q = N < 4 ? N : 4;        // states per vector
@@ -48,20 +51,24 @@ struct DecodeShape {
   static constexpr int CPB = 4 * CPW;            // channels per workgroup of 256
 };
 
-template <typename T, int N, bool ZOH, bool VBC>
+template <typename T, int N, bool ZOH, bool VBC, int R>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ x, const T* __restrict__ dtp,
     const float* __restrict__ A, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ Dv, const T* __restrict__ zp,
     const float* __restrict__ bias, int softplus, T* __restrict__ out,
-    int64_t batch, int64_t dim, int rows_per_block) {
+    int64_t batch, int64_t dim, int64_t n_cblk) {
   using S = DecodeShape<N>;
   constexpr int Q = S::Q, LPC = S::LPC, G = S::G;
   constexpr bool kVec = Q == 4;
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int wave = static_cast<int>(threadIdx.x) >> 6;
   const int q = lane % LPC;                      // which Q states of the channel
-  const int64_t c_wave = static_cast<int64_t>(blockIdx.x) * S::CPB + wave * S::CPW;
+  // workgroup -> (run of R batch rows, block of channels); channel blocks
+  // vary fastest, so neighbouring workgroups stream neighbouring state
+  const int64_t cb = static_cast<int64_t>(blockIdx.x) % n_cblk;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) / n_cblk * R;
+  const int64_t c_wave = cb * S::CPB + wave * S::CPW;
   int64_t dch[G];
   bool dvalid[G];
 #pragma unroll
@@ -70,8 +77,6 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     dvalid[g] = dr < dim;
     dch[g] = dvalid[g] ? dr : dim - 1;           // tail lanes compute, never store
   }
-  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * rows_per_block;
-  const int64_t b1 = b0 + rows_per_block < batch ? b0 + rows_per_block : batch;
 
   // the channels' constants
   float a2[G][Q], ia[G][Q], bs[G], dd[G];
@@ -95,81 +100,94 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     dd[g] = Dv ? Dv[dch[g]] : 0.0f;
   }
 
-  for (int64_t b = b0; b < b1; ++b) {
-    // B and C of the row (the same Q states for every channel group)
+  // One row's inputs.  Row r + 1's loads are issued before row r is computed
+  // and stored (two register sets, fully unrolled over the R rows), so a
+  // row's memory latency overlaps the previous row's work.  Rows past the
+  // batch re-read the last row and store nothing.
+  struct RowIn {
+    float h[G][Q];
+    float bv[Q], cv[Q];
+    float dt[G], xv[G], zv[G];
+  };
+  auto load_row = [&](int r, RowIn& in) {
+    const int64_t b = b0 + r < batch ? b0 + r : batch - 1;
     const T* bp = Bm + b * N + q * Q;
     const T* cp = Cm + b * N + q * Q;
-    float bv[Q], cv[Q];
     if constexpr (kVec && VBC) {
       if constexpr (sizeof(T) == 2) {
         const uint2 bw = *reinterpret_cast<const uint2*>(bp);
         const uint2 cw = *reinterpret_cast<const uint2*>(cp);
-        bv[0] = __uint_as_float(bw.x << 16); bv[1] = __uint_as_float(bw.x & 0xffff0000u);
-        bv[2] = __uint_as_float(bw.y << 16); bv[3] = __uint_as_float(bw.y & 0xffff0000u);
-        cv[0] = __uint_as_float(cw.x << 16); cv[1] = __uint_as_float(cw.x & 0xffff0000u);
-        cv[2] = __uint_as_float(cw.y << 16); cv[3] = __uint_as_float(cw.y & 0xffff0000u);
+        in.bv[0] = __uint_as_float(bw.x << 16); in.bv[1] = __uint_as_float(bw.x & 0xffff0000u);
+        in.bv[2] = __uint_as_float(bw.y << 16); in.bv[3] = __uint_as_float(bw.y & 0xffff0000u);
+        in.cv[0] = __uint_as_float(cw.x << 16); in.cv[1] = __uint_as_float(cw.x & 0xffff0000u);
+        in.cv[2] = __uint_as_float(cw.y << 16); in.cv[3] = __uint_as_float(cw.y & 0xffff0000u);
       } else {
         const float4 bw = *reinterpret_cast<const float4*>(bp);
         const float4 cw = *reinterpret_cast<const float4*>(cp);
-        bv[0] = bw.x; bv[1] = bw.y; bv[2] = bw.z; bv[3] = bw.w;
-        cv[0] = cw.x; cv[1] = cw.y; cv[2] = cw.z; cv[3] = cw.w;
+        in.bv[0] = bw.x; in.bv[1] = bw.y; in.bv[2] = bw.z; in.bv[3] = bw.w;
+        in.cv[0] = cw.x; in.cv[1] = cw.y; in.cv[2] = cw.z; in.cv[3] = cw.w;
       }
     } else {
 #pragma unroll
       for (int j = 0; j < Q; ++j) {
-        bv[j] = to_f32(bp[j]);
-        cv[j] = to_f32(cp[j]);
+        in.bv[j] = to_f32(bp[j]);
+        in.cv[j] = to_f32(cp[j]);
       }
     }
-    float h[G][Q];
-    float* hp[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      hp[g] = state + (b * dim + dch[g]) * N + q * Q;
+      const float* hp = state + (b * dim + dch[g]) * N + q * Q;
       if constexpr (kVec) {
-        const f32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp[g]));
-        h[g][0] = hv.x; h[g][1] = hv.y; h[g][2] = hv.z; h[g][3] = hv.w;
+        const f32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(hp));
+        in.h[g][0] = hv.x; in.h[g][1] = hv.y; in.h[g][2] = hv.z; in.h[g][3] = hv.w;
       } else {
 #pragma unroll
-        for (int j = 0; j < Q; ++j) h[g][j] = __builtin_nontemporal_load(hp[g] + j);
+        for (int j = 0; j < Q; ++j) in.h[g][j] = __builtin_nontemporal_load(hp + j);
       }
+      const int64_t bd = b * dim + dch[g];
+      in.dt[g] = to_f32(dtp[bd]);
+      in.xv[g] = to_f32(x[bd]);
+      in.zv[g] = zp ? to_f32(zp[bd]) : 0.0f;
     }
-    float xv[G], y[G];
+  };
+  auto finish_row = [&](int r, RowIn& in) {
+    const int64_t b = b0 + r;
+    const bool live = b < batch;
+    float y[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int64_t bd = b * dim + dch[g];
-      const float s = to_f32(dtp[bd]) + bs[g];
+      const float s = in.dt[g] + bs[g];
       const float dl = softplus ? softplus_f32(s) : s;
-      xv[g] = to_f32(x[bd]);
-      const float du = dl * xv[g];
+      const float du = dl * in.xv[g];
       float yy = 0.0f;
 #pragma unroll
       for (int j = 0; j < Q; ++j) {
         const float x2 = dl * a2[g][j];
         const float a = exp2_hw(x2);
         if constexpr (ZOH) {
-          h[g][j] = fmaf(a, h[g][j], zoh_coef(x2, a, dl, ia[g][j]) * (xv[g] * bv[j]));
+          in.h[g][j] = fmaf(a, in.h[g][j], zoh_coef(x2, a, dl, ia[g][j]) * (in.xv[g] * in.bv[j]));
         } else {
-          h[g][j] = fmaf(a, h[g][j], du * bv[j]);
+          in.h[g][j] = fmaf(a, in.h[g][j], du * in.bv[j]);
         }
-        yy = fmaf(cv[j], h[g][j], yy);
+        yy = fmaf(in.cv[j], in.h[g][j], yy);
       }
       y[g] = yy;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      if (dvalid[g]) {
+      if (dvalid[g] && live) {
+        float* hp = state + (b * dim + dch[g]) * N + q * Q;
         if constexpr (kVec) {
-          const f32x4 hv = {h[g][0], h[g][1], h[g][2], h[g][3]};
-          __builtin_nontemporal_store(hv, reinterpret_cast<f32x4*>(hp[g]));
+          const f32x4 hv = {in.h[g][0], in.h[g][1], in.h[g][2], in.h[g][3]};
+          __builtin_nontemporal_store(hv, reinterpret_cast<f32x4*>(hp));
         } else {
 #pragma unroll
-          for (int j = 0; j < Q; ++j) __builtin_nontemporal_store(h[g][j], hp[g] + j);
+          for (int j = 0; j < Q; ++j) __builtin_nontemporal_store(in.h[g][j], hp + j);
         }
       }
     }
     // the partial readouts of each channel's LPC neighbouring lanes (every
-    // lane of the wave takes part: the row loop is uniform over the workgroup)
+    // lane of the wave takes part: the rows are uniform over the workgroup)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float v = y[g];
@@ -184,13 +202,20 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      if (dvalid[g] && q == 0) {
-        const int64_t bd = b * dim + dch[g];
-        float v = y[g] + dd[g] * xv[g];
-        if (zp) v = silu_gate(v, to_f32(zp[bd]));
-        store_act(out, bd, v);
+      if (dvalid[g] && live && q == 0) {
+        float v = y[g] + dd[g] * in.xv[g];
+        if (zp) v = silu_gate(v, in.zv[g]);
+        store_act(out, b * dim + dch[g], v);
       }
     }
+  };
+
+  RowIn in[2];
+  load_row(0, in[0]);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r + 1 < R) load_row(r + 1, in[(r + 1) & 1]);
+    finish_row(r, in[r & 1]);
   }
 }
 
@@ -207,25 +232,24 @@ static hipError_t launch_n(int n, float* state, const void* x, const void* dt, c
   const int q = n < 4 ? n : 4;                          // states per vector
   const int64_t cpb = 4 * (n < 4 ? 1 : 2) * 64 / (n / q);  // channels per workgroup
   const int64_t cblocks = (dim + cpb - 1) / cpb;
-  // rows per workgroup: one (many short workgroups hide the state's latency
-  // best: 1 row measured faster than 2, 4, 8 and 16 at the 256 x 5120 x 16
-  // decode step), more only where the grid height would pass its limit
-  int64_t rows = 1;
-  if (decode_rows_override > 0) rows = decode_rows_override;
-  if (rows < 1) rows = 1;
-  if (rows > batch) rows = batch;
-  const int64_t min_rows = (batch + 65534) / 65535;
-  if (rows < min_rows) rows = min_rows;
-  const int64_t rblocks = (batch + rows - 1) / rows;
-  const int threads = 256;
-  const dim3 grid(static_cast<unsigned>(cblocks), static_cast<unsigned>(rblocks));
-  const int rows_per_block = static_cast<int>(rows);
-#define SSM_LAUNCH_SU_ZV(NN, Z, V)                                                              \
-  hipLaunchKernelGGL((state_update_kernel<T, NN, Z, V>), grid, dim3(threads), 0, stream, state, \
+  const int rows = (decode_rows_override == 1 || decode_rows_override == 2 ||
+                    decode_rows_override == 8) ? decode_rows_override : kDecodeRows;
+  const int64_t blocks = cblocks * ((batch + rows - 1) / rows);
+  if (blocks > (int64_t{1} << 31) - 1) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+#define SSM_LAUNCH_SU_ZVR(NN, Z, V, RR)                                                         \
+  hipLaunchKernelGGL((state_update_kernel<T, NN, Z, V, RR>), grid, block, 0, stream, state,    \
                      static_cast<const T*>(x), static_cast<const T*>(dt), A,                    \
                      static_cast<const T*>(B), static_cast<const T*>(C), D,                     \
                      static_cast<const T*>(z), bias, softplus, static_cast<T*>(out), batch, dim, \
-                     rows_per_block)
+                     cblocks)
+#define SSM_LAUNCH_SU_ZV(NN, Z, V)            \
+  switch (rows) {                             \
+    case 1: SSM_LAUNCH_SU_ZVR(NN, Z, V, 1); break; \
+    case 2: SSM_LAUNCH_SU_ZVR(NN, Z, V, 2); break; \
+    case 8: SSM_LAUNCH_SU_ZVR(NN, Z, V, 8); break; \
+    default: SSM_LAUNCH_SU_ZVR(NN, Z, V, 4); break; \
+  }
 #define SSM_LAUNCH_SU_Z(NN, Z)          \
   if (vbc) {                            \
     SSM_LAUNCH_SU_ZV(NN, Z, true);      \
@@ -251,6 +275,7 @@ static hipError_t launch_n(int n, float* state, const void* x, const void* dt, c
 #undef SSM_LAUNCH_SU
 #undef SSM_LAUNCH_SU_Z
 #undef SSM_LAUNCH_SU_ZV
+#undef SSM_LAUNCH_SU_ZVR
   return hipGetLastError();
 }
 

@@ -53,13 +53,15 @@ def test_probe_validation():
     # bad selectors and sizes are rejected before any HIP call
     assert lib.ssm_micro_valu(3, 8, 256, 1, P[0], P[1], 1, ctypes.byref(ms), None) == -1
     assert lib.ssm_micro_valu(0, 4, 256, 1, P[0], P[1], 1, ctypes.byref(ms), None) == -1
-    assert lib.ssm_micro_stream(4, 4, 256, P[0], P[1], 1 << 20, P[2], 1, ctypes.byref(ms),
+    assert lib.ssm_micro_stream(4, 4, 256, P[0], P[1], 1 << 20, 1, P[2], 1, ctypes.byref(ms),
                                 None) == -1
-    assert lib.ssm_micro_stream(2, 3, 256, P[0], P[1], 1 << 20, P[2], 1, ctypes.byref(ms),
+    assert lib.ssm_micro_stream(2, 3, 256, P[0], P[1], 1 << 20, 1, P[2], 1, ctypes.byref(ms),
                                 None) == -1
-    assert lib.ssm_micro_stream(2, 4, 256, P[0], P[1], 1000, P[2], 1, ctypes.byref(ms),
+    assert lib.ssm_micro_stream(2, 4, 256, P[0], P[1], 1000, 1, P[2], 1, ctypes.byref(ms),
                                 None) == -1
-    assert lib.ssm_micro_stream(2, 4, 256, None, P[1], 1 << 20, P[2], 1, ctypes.byref(ms),
+    assert lib.ssm_micro_stream(2, 4, 256, None, P[1], 1 << 20, 1, P[2], 1, ctypes.byref(ms),
+                                None) == -1
+    assert lib.ssm_micro_stream(3, 4, 256, None, P[1], 1 << 20, 0, P[2], 1, ctypes.byref(ms),
                                 None) == -1
 
 
