@@ -8,7 +8,10 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libssm_scan.so")
+# SSM_SCAN_LIB names another build of the same library (the host-sanitized
+# build that the CPU tests run the argument checks against); unset, the in-tree
+# library is loaded
+LIB_PATH = os.environ.get("SSM_SCAN_LIB") or os.path.join(HERE, "libssm_scan.so")
 # the roofline ceiling probes (include/ssm_micro.h), used by the benchmark
 MICRO_LIB_PATH = os.path.join(HERE, "libssm_micro.so")
 EXPORTED_MICRO = ("ssm_micro_valu", "ssm_micro_stream")

@@ -43,6 +43,16 @@ HIPCC_FLAGS = [
 LINK_LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 
 
+# The host-sanitized build: AddressSanitizer and UndefinedBehaviorSanitizer on
+# the host code only (argument checks, planning, workspace arithmetic); the
+# device code is compiled as in the product build.  Loaded with the ASan
+# runtime preloaded, for the CPU tests of the argument checks.
+SANITIZED_DIR = os.path.join(HERE, "_build", "asan")
+SANITIZED_LIB = os.path.join(SANITIZED_DIR, "libssm_scan.so")
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
 def hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
         if cand and (os.path.isabs(cand) and os.path.exists(cand) or not os.path.isabs(cand)):
@@ -88,6 +98,45 @@ def build(verbose=False):
     os.replace(tmp, LIB)
     os.replace(micro_tmp, MICRO_LIB)
     return LIB
+
+
+def asan_runtime():
+    """Path of the compiler's shared ASan runtime (to preload), or None."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin",
+                         "clang")
+    for cand in (clang, "/opt/rocm/lib/llvm/bin/clang"):
+        if os.path.exists(cand):
+            out = subprocess.run([cand, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                                 capture_output=True, text=True).stdout.strip()
+            if os.path.isabs(out) and os.path.exists(out):
+                return out
+    return None
+
+
+def build_host_sanitized(verbose=False):
+    """Builds the host-sanitized library into SANITIZED_DIR unless it is newer
+    than every source; returns its path."""
+    include = os.path.join(os.path.dirname(HERE), "include")
+    srcs = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + \
+        [os.path.join(include, f) for f in os.listdir(include)]
+    if os.path.exists(SANITIZED_LIB) and \
+            os.path.getmtime(SANITIZED_LIB) > max(os.path.getmtime(f) for f in srcs):
+        return SANITIZED_LIB
+    os.makedirs(SANITIZED_DIR, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"] + SANITIZE_HOST
+    objs, procs = [], []
+    for src, name, extra in SOURCES:
+        obj = os.path.join(SANITIZED_DIR, name + ".o")
+        objs.append(obj)
+        procs.append(_run([hipcc()] + compile_flags + extra +
+                          ["-c", os.path.join(CSRC, src), "-o", obj], verbose))
+    for proc in procs:
+        _check(proc, verbose)
+    tmp = SANITIZED_LIB + ".tmp"
+    _check(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + SANITIZE_HOST + objs +
+                ["-o", tmp] + LINK_LIBS, verbose), verbose)
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
 
 
 if __name__ == "__main__":
