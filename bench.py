@@ -424,8 +424,16 @@ def block_bench(args, torch, dev):
     print(f"bench: generating {w.name} block weights", file=sys.stderr, flush=True)
     x_np, wt_np = synth.make_block(**cfg, batch=w.batch, seqlen=w.seqlen, dtype=w.dtype)
     f32 = ("conv_w", "conv_b", "dt_bias", "A", "D")
-    wt = {k: torch.from_numpy(v).to(device=dev, dtype=torch.float32 if k in f32 else act)
+    # the generator's projection weights are [in][out]; the library takes a
+    # linear layer's [out][in], with x_dt, x_B, x_C the row blocks of one
+    # x_proj weight as in a model
+    proj = ("in_x", "in_z", "x_dt", "x_B", "x_C", "dt", "out")
+    wt = {k: torch.from_numpy(np.ascontiguousarray(v.T) if k in proj else v).to(
+              device=dev, dtype=torch.float32 if k in f32 else act)
           for k, v in wt_np.items()}
+    r_, n_ = wt["x_dt"].shape[0], wt["x_B"].shape[0]
+    x_proj = torch.cat([wt["x_dt"], wt["x_B"], wt["x_C"]], dim=0).contiguous()
+    wt["x_dt"], wt["x_B"], wt["x_C"] = x_proj[:r_], x_proj[r_:r_ + n_], x_proj[r_ + n_:]
     x = torch.from_numpy(x_np).to(device=dev, dtype=act)
     out = torch.empty_like(x)
     M = w.batch * w.seqlen

@@ -49,7 +49,9 @@
  *   - Entry points that need scratch (carries between sequence segments,
  *     checkpoints, partial sums, the block's intermediates) allocate it
  *     stream-ordered (hipMallocAsync) and free it on the same stream;
- *     failure returns SSM_ENOMEM.  The only other state is a per-device count
+ *     failure returns SSM_ENOMEM.  A forward whose launch plan runs every
+ *     (batch row, channel block) as one whole chain needs none and
+ *     allocates nothing.  The only other state is a per-device count
  *     of timed-out carry waits (read by ssm_check_device_errors) and, for
  *     mamba_block_fwd, one hipBLASLt handle per host thread and device, so
  *     calls on different streams or host threads may run concurrently.
@@ -259,20 +261,25 @@ int causal_conv1d_update(float* state, const void* x, const float* weight,
  * MambaMini" Q&A: d_inner = expand * d_model, the Conv before the SSM, B and
  * C from a linear layer, Delta from a low-rank pair of linear layers).
  * Matrices are row-major [rows][cols]; "dtype" is the block's dims->dtype.
+ * A projection's weight is stored [out][in], the layout of a PyTorch linear
+ * layer's weight: y = x W^T.  x_dt, x_B and x_C are the row blocks of one
+ * [dt_rank + 2 d_state][d_inner] x_proj weight; when they lie back to back
+ * in that order the block reads them in place, otherwise it copies them
+ * into its scratch.
  */
 typedef struct {
-  const void* in_x;      /* [d_model][d_inner] dtype: x = x_in in_x            */
-  const void* in_z;      /* [d_model][d_inner] dtype: z = x_in in_z (gate)     */
+  const void* in_x;      /* [d_inner][d_model] dtype: x = x_in in_x^T          */
+  const void* in_z;      /* [d_inner][d_model] dtype: z = x_in in_z^T (gate)   */
   const float* conv_w;   /* [d_inner][conv_width] float32                      */
   const float* conv_b;   /* [d_inner] float32 (nullable)                       */
-  const void* x_dt;      /* [d_inner][dt_rank] dtype: dt_low = u x_dt          */
-  const void* x_B;       /* [d_inner][d_state] dtype: B = u x_B                */
-  const void* x_C;       /* [d_inner][d_state] dtype: C = u x_C                */
-  const void* dt;        /* [dt_rank][d_inner] dtype: dt = dt_low dt           */
+  const void* x_dt;      /* [dt_rank][d_inner] dtype: dt_low = u x_dt^T        */
+  const void* x_B;       /* [d_state][d_inner] dtype: B = u x_B^T              */
+  const void* x_C;       /* [d_state][d_inner] dtype: C = u x_C^T              */
+  const void* dt;        /* [d_inner][dt_rank] dtype: dt = dt_low dt^T         */
   const float* dt_bias;  /* [d_inner] float32 (nullable)                       */
   const float* A;        /* [d_inner][d_state] float32                         */
   const float* D;        /* [d_inner] float32 (nullable)                       */
-  const void* out;       /* [d_inner][d_model] dtype: out = y out              */
+  const void* out;       /* [d_model][d_inner] dtype: out = y out^T            */
 } mamba_block_weights;
 
 typedef struct {
@@ -284,18 +291,20 @@ typedef struct {
 
 /*
  * Forward of one Mamba block:
- *   x, z  = x_in in_x, x_in in_z                      (hipBLASLt GEMMs)
+ *   x, z  = x_in in_x^T, x_in in_z^T                  (hipBLASLt GEMMs)
  *   u     = SiLU(causal_conv1d(x) + conv_b)            (causal_conv1d_fwd)
- *   dt_low, B, C = u x_dt, u x_B, u x_C;  dt = dt_low dt   (GEMMs; the three
- *           projections of u run as one GEMM against [x_dt | x_B | x_C])
+ *   dt_low, B, C = u x_dt^T, u x_B^T, u x_C^T;  dt = dt_low dt^T  (GEMMs; the
+ *           three projections of u run as one GEMM against the stacked
+ *           [x_dt; x_B; x_C])
  *   y     = selective scan of u with Delta = softplus(dt + dt_bias), gated
  *           by SiLU(z)                                 (selective_scan_fwd)
- *   out   = y out                                      (GEMM)
+ *   out   = y out^T                                    (GEMM)
  *   x_in, out : [batch][seqlen][d_model] of dtype; out must not alias x_in.
  * GEMMs accumulate in float32; intermediates are stored in dtype.  Scratch
  * for the intermediates (about (5 d_inner + dt_rank + 4 d_state) * batch *
- * seqlen elements of dtype, plus a d_inner x (dt_rank + 2 d_state) copy of
- * the x_proj weights) is allocated stream-ordered and freed on the stream.  Normalisation and the residual connection are the caller's.
+ * seqlen elements of dtype, plus a copy of the stacked x_proj weights
+ * unless they are already back to back) is allocated stream-ordered and
+ * freed on the stream.  Normalisation and the residual connection are the caller's.
  * Returns an ssm_status (SSM_ELAUNCH if a GEMM fails).
  */
 int mamba_block_fwd(const void* x_in, const mamba_block_weights* weights, void* out,

@@ -325,8 +325,9 @@ def mamba_block_fwd(x_in, weights, out=None):
     + SiLU and the gated selective scan in this library's kernels).
 
     x_in: [batch, L, d_model] (float32 or bfloat16).  ``weights``: dict with
-    in_x, in_z [d_model, d_inner], x_dt [d_inner, r], x_B, x_C
-    [d_inner, N], dt [r, d_inner], out [d_inner, d_model] in x_in's dtype,
+    the projection weights in the layout of a linear layer's weight,
+    [out, in]: in_x, in_z [d_inner, d_model], x_dt [r, d_inner], x_B, x_C
+    [N, d_inner], dt [d_inner, r], out [d_model, d_inner] in x_in's dtype;
     and conv_w [d_inner, K], A [d_inner, N], optional conv_b, dt_bias, D
     [d_inner] in float32.  Returns out [batch, L, d_model].
     """
@@ -335,14 +336,14 @@ def mamba_block_fwd(x_in, weights, out=None):
     bsz, L, dm = x_in.shape
     dev = x_in.device
     act = x_in.dtype
-    di = weights["in_x"].shape[1]
+    di = weights["in_x"].shape[0]
     n = weights["A"].shape[1]
-    r = weights["x_dt"].shape[1]
+    r = weights["x_dt"].shape[0]
     k = weights["conv_w"].shape[1]
-    shapes = dict(in_x=((dm, di), act), in_z=((dm, di), act), conv_w=((di, k), torch.float32),
-                  conv_b=((di,), torch.float32), x_dt=((di, r), act), x_B=((di, n), act),
-                  x_C=((di, n), act), dt=((r, di), act), dt_bias=((di,), torch.float32),
-                  A=((di, n), torch.float32), D=((di,), torch.float32), out=((di, dm), act))
+    shapes = dict(in_x=((di, dm), act), in_z=((di, dm), act), conv_w=((di, k), torch.float32),
+                  conv_b=((di,), torch.float32), x_dt=((r, di), act), x_B=((n, di), act),
+                  x_C=((n, di), act), dt=((di, r), act), dt_bias=((di,), torch.float32),
+                  A=((di, n), torch.float32), D=((di,), torch.float32), out=((dm, di), act))
     _check(x_in, "x_in", act, (bsz, L, dm), dev)
     for name, (shp, dt_) in shapes.items():
         if weights.get(name) is None and name not in ("conv_b", "dt_bias", "D"):

@@ -214,8 +214,13 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const int64_t aggs_bytes = plan.lookback ? up256(recs * plan.state_groups * 64 * 4) : 0;
   const int64_t total = off_inc + inc_bytes + aggb_bytes + aggs_bytes;
 
+  // a plan of whole chains only takes no ticket and publishes no carry: no
+  // scratch, no clearing launch
+  const bool need_scratch = plan.whole_chains < chains;
   char* buf = nullptr;
-  if (no_alloc) {
+  if (!need_scratch) {
+    // nothing to allocate
+  } else if (no_alloc) {
     // the static array: nothing is allocated or freed by this call
     if (total > kStaticScratchBytes) return SSM_ESCRATCH;
     void* addr = nullptr;
@@ -231,11 +236,12 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   }
 
   ssm::FwdScratch sc;
-  sc.ticket = reinterpret_cast<int*>(buf);
-  sc.status = sc.ticket + 1;
-  sc.inc = reinterpret_cast<float*>(buf + off_inc);
-  sc.agg_b = reinterpret_cast<float*>(buf + off_inc + inc_bytes);
-  sc.agg_s = reinterpret_cast<float*>(buf + off_inc + inc_bytes + aggb_bytes);
+  sc.ticket = need_scratch ? reinterpret_cast<int*>(buf) : nullptr;
+  sc.status = need_scratch ? sc.ticket + 1 : nullptr;
+  sc.inc = need_scratch ? reinterpret_cast<float*>(buf + off_inc) : nullptr;
+  sc.agg_b = need_scratch ? reinterpret_cast<float*>(buf + off_inc + inc_bytes) : nullptr;
+  sc.agg_s =
+      need_scratch ? reinterpret_cast<float*>(buf + off_inc + inc_bytes + aggb_bytes) : nullptr;
   sc.spin_limit = env_int("SSM_TEST_SPIN_LIMIT", kDefaultSpinLimit);
   sc.ckpt = ckpt;
   sc.ysave = ckpt ? reinterpret_cast<float*>(reinterpret_cast<char*>(ckpt) + ckpt_y_offset(dims))
@@ -276,9 +282,11 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
 
   rc = SSM_OK;
   const bool f32 = dims->dtype == SSM_F32;
-  const hipError_t ez = f32 ? ssm::fwd_f32::launch_fill_zero(sc.ticket, n_int, st)
-                            : ssm::fwd_bf16::launch_fill_zero(sc.ticket, n_int, st);
-  if (ez != hipSuccess) rc = SSM_ELAUNCH;
+  if (need_scratch) {
+    const hipError_t ez = f32 ? ssm::fwd_f32::launch_fill_zero(sc.ticket, n_int, st)
+                              : ssm::fwd_bf16::launch_fill_zero(sc.ticket, n_int, st);
+    if (ez != hipSuccess) rc = SSM_ELAUNCH;
+  }
   if (rc == SSM_OK) {
     const hipError_t el =
         f32 ? ssm::fwd_f32::launch_scan_fwd(plan.state_groups, plan.states_per_group, p, sc, sh,
@@ -287,7 +295,8 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
                                              sh, plan.workgroups, st);
     if (el != hipSuccess) rc = SSM_ELAUNCH;
   }
-  if (!no_alloc && hipFreeAsync(buf, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
+  if (need_scratch && !no_alloc && hipFreeAsync(buf, st) != hipSuccess && rc == SSM_OK)
+    rc = SSM_ELAUNCH;
   return rc;
 }
 
@@ -560,14 +569,19 @@ int block_impl(const void* x_in, const mamba_block_weights* w, void* out,
   const int64_t esz = bd->dtype == SSM_BF16 ? 2 : 4;
   auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
   // u feeds three projections (the low-rank dt, B, C): one GEMM against the
-  // side-by-side weights [x_dt | x_B | x_C] reads u once (each projection is
-  // HBM-bound on u); B and C are then copied out as the scan's contiguous
-  // [rows][N] operands
+  // stacked weights [x_dt; x_B; x_C] ([dt_rank + 2 d_state][d_inner]) reads u
+  // once (each projection is HBM-bound on u); B and C are then copied out as
+  // the scan's contiguous [rows][N] operands.  The stack is the caller's
+  // memory when the three weights already lie back to back (the rows of one
+  // x_proj weight), else a copy.
   const int64_t nx = r + 2 * n;
+  const char* wx_dt = static_cast<const char*>(w->x_dt);
+  const bool stacked = static_cast<const char*>(w->x_B) == wx_dt + r * di * esz &&
+                       static_cast<const char*>(w->x_C) == wx_dt + (r + n) * di * esz;
   const int64_t b_act = up256(M * di * esz);
   const int64_t b_xo = up256(M * nx * esz);
   const int64_t b_bc = up256(M * n * esz);
-  const int64_t b_wx = up256(di * nx * esz);
+  const int64_t b_wx = stacked ? 0 : up256(di * nx * esz);
   const int64_t total = 5 * b_act + b_xo + 2 * b_bc + b_wx;  // x, z, u, dt, y; x_proj; B, C
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (env_int("SSM_TEST_FAIL_ALLOC", 0) == 1) return SSM_ENOMEM;
@@ -584,24 +598,31 @@ int block_impl(const void* x_in, const mamba_block_weights* w, void* out,
   char* xo = y + b_act;
   char* Bm = xo + b_xo;
   char* Cm = Bm + b_bc;
-  char* wx = Cm + b_bc;
+  char* wx_copy = Cm + b_bc;
   const int dtype = bd->dtype;
 
   int rc = SSM_OK;
-  auto gemm = [&](int64_t rows, int64_t cols, int64_t inner, const void* a, const void* wt,
-                  void* c) {
+  // C[rows][cols] = a[rows][inner] (leading dimension lda) times the [cols][inner]
+  // weight transposed
+  auto gemm = [&](int64_t rows, int64_t cols, int64_t inner, const void* a, int64_t lda,
+                  const void* wt, void* c) {
     if (rc == SSM_OK &&
-        ssm::gemm_rowmajor(dtype, rows, cols, inner, a, inner, wt, cols, c, cols, st) !=
+        ssm::gemm_linear(dtype, rows, cols, inner, a, lda, wt, inner, c, cols, st) !=
             hipSuccess)
       rc = SSM_ELAUNCH;
   };
-  gemm(M, di, dm, x_in, w->in_x, x);
-  gemm(M, di, dm, x_in, w->in_z, z);
+  gemm(M, di, dm, x_in, dm, w->in_x, x);
+  gemm(M, di, dm, x_in, dm, w->in_z, z);
   if (rc == SSM_OK) {
     ssm_dims cd{bd->batch, bd->seqlen, di, 1, dtype};
     rc = conv_fwd_impl(x, w->conv_w, w->conv_b, nullptr, bd->conv_width, 1, u, nullptr, &cd,
                        stream);
   }
+  auto copy = [&](void* dst, const void* src, int64_t bytes) {
+    if (rc == SSM_OK && hipMemcpyAsync(dst, src, static_cast<size_t>(bytes),
+                                       hipMemcpyDeviceToDevice, st) != hipSuccess)
+      rc = SSM_ELAUNCH;
+  };
   auto copy2d = [&](void* dst, int64_t dpitch, const void* src, int64_t spitch, int64_t width,
                     int64_t height) {
     if (rc == SSM_OK &&
@@ -610,22 +631,24 @@ int block_impl(const void* x_in, const mamba_block_weights* w, void* out,
                          hipMemcpyDeviceToDevice, st) != hipSuccess)
       rc = SSM_ELAUNCH;
   };
-  copy2d(wx, nx * esz, w->x_dt, r * esz, r * esz, di);
-  copy2d(wx + r * esz, nx * esz, w->x_B, n * esz, n * esz, di);
-  copy2d(wx + (r + n) * esz, nx * esz, w->x_C, n * esz, n * esz, di);
-  gemm(M, nx, di, u, wx, xo);
+  const void* wx = w->x_dt;
+  if (!stacked) {
+    copy(wx_copy, w->x_dt, r * di * esz);
+    copy(wx_copy + r * di * esz, w->x_B, n * di * esz);
+    copy(wx_copy + (r + n) * di * esz, w->x_C, n * di * esz);
+    wx = wx_copy;
+  }
+  gemm(M, nx, di, u, di, wx, xo);
   copy2d(Bm, n * esz, xo + r * esz, nx * esz, n * esz, M);
   copy2d(Cm, n * esz, xo + (r + n) * esz, nx * esz, n * esz, M);
-  // dt = dt_low W_dt with dt_low the first r columns of the x_proj output
-  if (rc == SSM_OK && ssm::gemm_rowmajor(dtype, M, di, r, xo, nx, w->dt, di, dt, di, st) !=
-                          hipSuccess)
-    rc = SSM_ELAUNCH;
+  // dt = dt_low dt^T with dt_low the first r columns of the x_proj output
+  gemm(M, di, r, xo, nx, w->dt, dt);
   if (rc == SSM_OK) {
     ssm_dims sd{bd->batch, bd->seqlen, di, n, dtype};
     rc = fwd_impl(u, dt, w->A, Bm, Cm, w->D, z, w->dt_bias, 1, nullptr, SSM_BBAR_DELTA, y,
                   nullptr, nullptr, &sd, stream);
   }
-  gemm(M, dm, di, y, w->out, out);
+  gemm(M, dm, di, y, di, w->out, out);
   if (hipFreeAsync(ws, st) != hipSuccess && rc == SSM_OK) rc = SSM_ELAUNCH;
   return rc;
 }

@@ -112,7 +112,7 @@ int time_launches(F launch, int reps, hipStream_t st, float* ms_out) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (hipEventCreate(&e0) != hipSuccess) return SSM_MICRO_ERUNTIME;
   if (hipEventCreate(&e1) != hipSuccess) {
-    hipEventDestroy(e0);
+    (void)hipEventDestroy(e0);
     return SSM_MICRO_ERUNTIME;
   }
   int rc = SSM_MICRO_OK;
@@ -128,8 +128,8 @@ int time_launches(F launch, int reps, hipStream_t st, float* ms_out) {
                              hipEventSynchronize(e1) != hipSuccess ||
                              hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
     rc = SSM_MICRO_ERUNTIME;
-  hipEventDestroy(e0);
-  hipEventDestroy(e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
   if (rc == SSM_MICRO_OK) *ms_out = ms / static_cast<float>(reps);
   return rc;
 }

@@ -128,8 +128,12 @@ def test_fwd_rejects_aliasing():
 
 
 def test_fwd_allocation_failure_is_reported(monkeypatch):
+    # four 16-step look-back segments: a plan with carry records, so scratch
+    # is allocated (a plan of whole chains allocates nothing)
     monkeypatch.setenv("SSM_TEST_FAIL_ALLOC", "1")
-    assert _fwd(_dims()) == SSM_ENOMEM
+    monkeypatch.setenv("SSM_FORCE_LOOKBACK", "1")
+    monkeypatch.setenv("SSM_FORCE_SEGMENT", "16")
+    assert _fwd(_dims(L=64)) == SSM_ENOMEM
 
 
 def test_update_rejects_seqlen_not_one():
