@@ -360,7 +360,8 @@ int ssm_check_device_errors(void* stream);
  * Launch plan the forward would use for `dims` (host only, no GPU call):
  * state_groups = waves sharing one block of 64 channels, each holding
  * states_per_group of the N states of every channel; segments = sequence
- * segments of segment_len steps; lookback = 1 if segments exchange partial
+ * segments: the first of first_segment_len steps, the others of segment_len
+ * steps (the last may be shorter); lookback = 1 if segments exchange partial
  * aggregates (decoupled look-back), 0 if each waits for its predecessor's
  * final state; chunk = steps staged through LDS at a time; workgroups = the
  * launch's grid; whole_chains = how many (batch row, channel block) chains run
@@ -376,6 +377,7 @@ typedef struct {
   int32_t chunk;
   int64_t workgroups;
   int32_t whole_chains;
+  int32_t first_segment_len;
 } ssm_fwd_plan;
 
 int ssm_fwd_plan_for(const ssm_dims* dims, ssm_fwd_plan* plan);

@@ -62,6 +62,7 @@ class SsmFwdPlan(ctypes.Structure):
         ("chunk", ctypes.c_int32),
         ("workgroups", ctypes.c_int64),
         ("whole_chains", ctypes.c_int32),
+        ("first_segment_len", ctypes.c_int32),
     ]
 
 

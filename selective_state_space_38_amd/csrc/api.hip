@@ -118,6 +118,7 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
   int64_t n_seg = div_up(d.seqlen, seg_len);
   if (n_seg == 1) lookback = 0;
   int64_t whole = n_seg == 1 ? chains : 0;
+  int64_t first_len = seg_len;
 
   // Whole chains beyond a multiple of the CU count would double up on some
   // CUs while the rest idle for the second half.  Those M chains are split
@@ -134,10 +135,25 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
       const int64_t sl = div_up(div_up(d.seqlen, S), chunk) * chunk;
       if (div_up(d.seqlen, sl) > 1) {
         seg_len = sl;
+        first_len = sl;
         n_seg = div_up(d.seqlen, sl);
         whole = K;
         lookback = 1;
       }
+    }
+  }
+  // A split chain's first segment starts from the initial state and skips
+  // the aggregate pass, but its successors' look-back ends only at its final
+  // state, published when its output pass ends.  SSM_FORCE_FIRST_SEGMENT
+  // sets its length (steps, rounded to the chunk); the other segments then
+  // share the rest of the sequence evenly, their count not growing.
+  const int force_first = env_int("SSM_FORCE_FIRST_SEGMENT", 0);
+  if (n_seg > 1 && force_first > 0) {
+    const int64_t fl = div_up(force_first, chunk) * chunk;
+    if (fl < d.seqlen) {
+      first_len = fl;
+      seg_len = div_up(div_up(d.seqlen - fl, n_seg - 1), chunk) * chunk;
+      n_seg = 1 + div_up(d.seqlen - fl, seg_len);
     }
   }
 
@@ -149,6 +165,7 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
   p->chunk = chunk;
   p->workgroups = whole + (chains - whole) * n_seg;
   p->whole_chains = static_cast<int32_t>(whole);
+  p->first_segment_len = static_cast<int32_t>(first_len);
 }
 
 int check_dims(const ssm_dims* dims) {
@@ -255,6 +272,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.n_full = plan.whole_chains;
   sh.n_seg = plan.segments;
   sh.seg_len = plan.segment_len;
+  sh.seg0_len = plan.first_segment_len;
   sh.softplus = softplus ? 1 : 0;
   sh.lookback = plan.lookback;
   sh.has_bias = dt_bias != nullptr;

@@ -167,9 +167,11 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
   const bool dvalid = d < dim;
   const int64_t dc = dvalid ? d : dim - 1;      // tail lanes read a valid channel, never store
 
-  const int64_t seg_len_c = whole ? L : sh.seg_len;
-  const int64_t t_begin = static_cast<int64_t>(seg) * seg_len_c;
-  const int64_t t_end = (t_begin + seg_len_c < L) ? t_begin + seg_len_c : L;
+  // a split chain's first segment has its own length; the others follow it
+  const int64_t t_begin =
+      (whole || seg == 0) ? 0 : sh.seg0_len + static_cast<int64_t>(seg - 1) * sh.seg_len;
+  const int64_t t_stop = whole ? L : t_begin + (seg == 0 ? sh.seg0_len : sh.seg_len);
+  const int64_t t_end = t_stop < L ? t_stop : L;
   const int n_chunks = static_cast<int>((t_end - t_begin + TC - 1) / TC);
   const int64_t row0 = static_cast<int64_t>(b) * L;  // row of (b, t=0)
   // carry records exist for split chains only: rec0 is this chain's first

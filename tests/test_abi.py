@@ -180,6 +180,25 @@ def test_forced_segments_are_whole_chunks_of_the_instance(monkeypatch):
         assert plan.segments == -(-4096 // want)
 
 
+def test_first_segment_override(monkeypatch):
+    """The first segment takes the forced length (rounded to the chunk); the
+    others share the rest evenly without adding segments."""
+    lib = _lib.load()
+    plan = _lib.SsmFwdPlan()
+    monkeypatch.setenv("SSM_FORCE_LOOKBACK", "1")
+    monkeypatch.setenv("SSM_FORCE_SEGMENT", "96")
+    L = 1000
+    base_segments = -(-L // 96)
+    for first, want in ((0, 96), (32, 32), (40, 48), (160, 160), (5000, 96)):
+        monkeypatch.setenv("SSM_FORCE_FIRST_SEGMENT", str(first))
+        assert lib.ssm_fwd_plan_for(ctypes.byref(_dims(b=2, L=L, d=96)), ctypes.byref(plan)) == 0
+        assert plan.first_segment_len == want, (first, plan.first_segment_len)
+        f, s = plan.first_segment_len, plan.segment_len
+        assert s % plan.chunk == 0 and plan.segments <= base_segments
+        assert f + (plan.segments - 2) * s < L <= f + (plan.segments - 1) * s
+        assert plan.workgroups == 2 * 2 * plan.segments
+
+
 def test_plan_covers_every_supported_state_size():
     lib = _lib.load()
     plan = _lib.SsmFwdPlan()

@@ -99,6 +99,27 @@ def test_segment_carry_modes(tag, lookback, seg):
     check_forward(x, tag, got, st, ref, ref_st)
 
 
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
+@pytest.mark.parametrize("lookback,seg,first", [(1, 96, 32), (1, 96, 160), (0, 64, 16),
+                                                (1, 16, 48)])
+def test_first_segment_length(tag, lookback, seg, first):
+    """A first segment shorter or longer than the others: every segment's
+    bounds and carry records follow from the two lengths."""
+    from selective_state_space_38_amd import fwd_plan
+    wl = "mamba130m" if tag == "f32" else "mamba2p8b"
+    L = 1000
+    x = _case(wl, batch=2, seqlen=L, dim=96, dstate=16, a_init="random")
+    _log(f"first segment {tag} lookback={lookback} seg={seg} first={first}")
+    with env(SSM_FORCE_LOOKBACK=lookback, SSM_FORCE_SEGMENT=seg, SSM_FORCE_FIRST_SEGMENT=first):
+        plan = fwd_plan(2, L, 96, 16, act_dtype(tag))
+        s_ = plan["segment_len"]
+        assert plan["first_segment_len"] == first and plan["segments"] > 2, plan
+        assert first + (plan["segments"] - 2) * s_ < L <= first + (plan["segments"] - 1) * s_
+        got, st = gpu_forward(x, tag)
+    ref, ref_st = oracle_forward(x)
+    check_forward(x, tag, got, st, ref, ref_st)
+
+
 @pytest.mark.parametrize("groups_per", [1, 2, 4, 8])
 def test_state_group_layouts(groups_per):
     """Every instantiated split of 16 states over waves gives the same answer."""
@@ -187,13 +208,16 @@ def test_carry_wait_bound_reports_timeout():
 @pytest.mark.parametrize("split", [None, 2, 8])
 def test_whole_and_split_chains(split):
     """More chains than CUs: 256 chains run whole and the rest are split into
-    look-back segments (the planner's choice, or a forced split count)."""
+    look-back segments (the planner's choice, or a forced split count; with a
+    forced split of 8 the first segment is also given its own length)."""
     from selective_state_space_38_amd import fwd_plan
     x = _case("mamba130m", batch=1, seqlen=600, dim=64 * 300, dstate=16, a_init="random")
-    with env(SSM_FORCE_SPLIT=split):
+    first = 96 if split == 8 else 0
+    with env(SSM_FORCE_SPLIT=split, SSM_FORCE_FIRST_SEGMENT=first):
         plan = fwd_plan(1, 600, 64 * 300, 16)
         got, st = gpu_forward(x, "f32")
     assert plan["whole_chains"] == 256 and plan["segments"] > 1, plan
+    assert plan["first_segment_len"] == (first or plan["segment_len"]), plan
     _log(f"mixed plan {plan}")
     # columns of whole chains, of split chains and the block edges
     cols = [(0, d) for d in (0, 63, 64, 16383, 16384, 16385, 17000, 19199)]
