@@ -95,7 +95,10 @@ def _upd(dims, *, state=P[0], x=P[1], dt=P[2], A=P[3], B=P[4], C=P[5], out=P[6])
 
 @pytest.mark.parametrize("field,value", [("batch", 0), ("seqlen", 0), ("dim", 0),
                                          ("dstate", 0), ("dstate", 3), ("dstate", 128),
-                                         ("batch", -1)])
+                                         ("batch", -1),
+                                         # beyond the 32-bit launch arithmetic
+                                         ("dim", (1 << 24) + 1), ("seqlen", 1 << 31),
+                                         ("batch", (1 << 30) + 1)])
 def test_fwd_rejects_bad_dims(field, value):
     d = _dims()
     setattr(d, field, value)

@@ -11,6 +11,7 @@ ABI, against the float64 oracle (tolerances in parity_util):
   pair operator's associativity, "Mamba / MambaMini" Step 3): the
   million-token sequence and 16-step segments, thirty times each, every run
   checked against the oracle and the device error counter;
+* the largest channel count the library accepts (2^24);
 * the plain selective_scan_fwd export, and decode B/C that are not aligned
   for vector loads.
 """
@@ -203,6 +204,28 @@ def test_short_segment_stress(lookback):
             check_device_errors()
             check(f"rep {rep} out", out.double().cpu().numpy(), ref, scale, TOL["f32"])
             check(f"rep {rep} state", last.double().cpu().numpy(), ref_st, scale, TOL["f32"])
+
+
+# ------------------------------------------------- maximum channel count --
+
+def test_maximum_channel_count():
+    """dim at the library's limit, 2^24 channels (one batch row, float32): the
+    helpers address a chunk's rows with 32-bit byte offsets, here up to 15
+    rows x 2^24 channels x 4 bytes; 17 steps are one full chunk and a ragged
+    one.  Sampled columns against the oracle, and every output finite."""
+    D = 1 << 24
+    _log("maximum channel count: generating inputs")
+    x = synth.make("mamba130m", batch=1, seqlen=17, dim=D, dstate=16, a_init="random")
+    _log("maximum channel count: forward")
+    got, st = gpu_forward(x, "f32")
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(st))
+    cols = sorted(set(sample_columns(1, D, 12, seed=24)) | {(0, D - 64), (0, D - 65)})
+    ref, ref_st = oracle_forward(x, cols=cols)
+    g_out = np.stack([got[b, :, d] for b, d in cols])
+    g_st = np.stack([st[b, d] for b, d in cols])
+    scale = float(np.max(np.abs(ref)))
+    check("out", g_out, ref, scale, TOL["f32"])
+    check("last_state", g_st, ref_st, scale, TOL["f32"])
 
 
 # ------------------------------------------------------ plain entry point --
