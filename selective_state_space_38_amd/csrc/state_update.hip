@@ -39,7 +39,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // batch rows per workgroup (software-pipelined, see the kernel); 1, 2, 4
 // or 8 are instantiated.  At the 256 x 5120 x 16 step, 1 and 2 rows measured
 // 33.7-35 us and 4 or 8 rows 36 us: many short workgroups hide the state's
-// latency at least as well as prefetching inside longer ones.
+// latency at least as well as prefetching inside longer ones.  (A persistent
+// grid-stride form, 1024 workgroups each prefetching its next tile, measured
+// 36.7 us: its registers halve the waves a SIMD holds.)
 constexpr int kDecodeRows = 1;
 
 template <int N>
@@ -233,7 +235,9 @@ static hipError_t launch_n(int n, float* state, const void* x, const void* dt, c
   const int64_t cpb = 4 * (n < 4 ? 1 : 2) * 64 / (n / q);  // channels per workgroup
   const int64_t cblocks = (dim + cpb - 1) / cpb;
   const int rows = (decode_rows_override == 1 || decode_rows_override == 2 ||
-                    decode_rows_override == 8) ? decode_rows_override : kDecodeRows;
+                    decode_rows_override == 4 || decode_rows_override == 8)
+                       ? decode_rows_override
+                       : kDecodeRows;
   const int64_t blocks = cblocks * ((batch + rows - 1) / rows);
   if (blocks > (int64_t{1} << 31) - 1) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
@@ -245,10 +249,10 @@ static hipError_t launch_n(int n, float* state, const void* x, const void* dt, c
                      cblocks)
 #define SSM_LAUNCH_SU_ZV(NN, Z, V)            \
   switch (rows) {                             \
-    case 1: SSM_LAUNCH_SU_ZVR(NN, Z, V, 1); break; \
     case 2: SSM_LAUNCH_SU_ZVR(NN, Z, V, 2); break; \
+    case 4: SSM_LAUNCH_SU_ZVR(NN, Z, V, 4); break; \
     case 8: SSM_LAUNCH_SU_ZVR(NN, Z, V, 8); break; \
-    default: SSM_LAUNCH_SU_ZVR(NN, Z, V, 4); break; \
+    default: SSM_LAUNCH_SU_ZVR(NN, Z, V, 1); break; \
   }
 #define SSM_LAUNCH_SU_Z(NN, Z)          \
   if (vbc) {                            \
