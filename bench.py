@@ -10,9 +10,13 @@ HBM; decode states rotate over six buffers (504 MB) so the 256 MB Infinity
 Cache cannot hold them between steps.
 
 Prints one JSON line.  `value` is the forward's tokens*channels per second
-(B*L*D over the forward kernel's own time; the decode's rate is reported
-separately); `ms_per_step` is the wall time of a whole step.  Beside the
-timed step the same run measures:
+(B*L*D over the forward's average launch time, measured over a timed region
+of back-to-back launches with one HIP event pair on the launch stream; the
+decode's rate is reported separately); `ms_per_step` is the wall time of a
+whole step over the K timed steps (`gpu_ms_per_step` the same from HIP
+events).  Per-launch medians and minima come from a second pass with an event
+pair around every launch (those events add a few microseconds to each).
+Beside the timed step the same run measures:
   * the ceilings the fractions are taken against (libssm_micro probes: fp32
     FMA and v_exp_f32 rates, streaming HBM bandwidth);
   * the million-token and 130M-shaped forwards (their own timing loops, not
@@ -398,6 +402,7 @@ def conv_bench(args, torch, dev):
 
 
 def _time_ms(torch, fn, steps, warmup):
+    """Per-call launch times (ms): an event pair around every call."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -408,6 +413,22 @@ def _time_ms(torch, fn, steps, warmup):
         e[1].record()
     torch.cuda.synchronize()
     return [e[0].elapsed_time(e[1]) for e in ev]
+
+
+def _time_region_ms(torch, fn, steps, warmup):
+    """Average launch time (ms) over a timed region: one event pair around
+    `steps` back-to-back calls (no event between them; an event recorded
+    between every two calls adds its own few microseconds to each)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def block_bench(args, torch, dev):
@@ -662,10 +683,12 @@ def micro_bench(args, torch, dev):
 
 # --------------------------------------------------------- per workload --
 
-def fwd_entry(w, ms_list, ceil, bbar="delta", traffic=None):
-    """Rates and roofline fractions of one forward workload from its launch
-    times (ms)."""
-    avg = float(np.mean(ms_list))
+def fwd_entry(w, ms_list, ceil, bbar="delta", traffic=None, region_avg=None):
+    """Rates and roofline fractions of one forward workload.  avg_ms is the
+    average over a timed region of back-to-back launches when region_avg is
+    given (else the mean of the per-call times); median and min are of the
+    per-call times."""
+    avg = float(region_avg) if region_avg is not None else float(np.mean(ms_list))
     tokch = w.batch * w.seqlen * w.dim
     nbytes = synth.algorithmic_bytes(w)
     slots_per = valu_slots_per_token_channel(w.dstate, bbar)
@@ -677,7 +700,11 @@ def fwd_entry(w, ms_list, ceil, bbar="delta", traffic=None):
                   "io_dtype": w.dtype},
         "tokens_channels_per_s": tokch / (avg / 1e3),
         "avg_ms": avg, "median_ms": float(np.median(ms_list)), "min_ms": float(np.min(ms_list)),
+        "per_call_avg_ms": float(np.mean(ms_list)),
         "launches": len(ms_list),
+        "timing": ("avg_ms over a region of back-to-back launches (one HIP event pair); "
+                   "median, min and per_call_avg from an event pair around every launch"
+                   if region_avg is not None else "event pair around every launch"),
         "algorithmic_bytes": nbytes,
         "hbm_GBps": gbs, "hbm_frac_of_8TBps": gbs / HBM_PEAK_GBS,
         "alu": {"slots_per_token_channel": slots_per, "achieved": alu, "unit": ALU_UNIT,
@@ -726,10 +753,11 @@ def time_forward(torch, dev, w, steps, warmup, bbar="delta"):
                            return_last_state=True, out=out, last_state=last, bbar=bbar)
 
     ms = _time_ms(torch, fwd, steps, warmup)
+    region = _time_region_ms(torch, fwd, steps, warmup)
     check_device_errors(dev)
     del sets, out, last
     torch.cuda.empty_cache()
-    return ms, n_sets
+    return ms, n_sets, region
 
 
 # ------------------------------------------------- counter summaries --
@@ -951,27 +979,44 @@ def main():
     check_device_errors(dev)
     print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed steps: K whole steps back to back, bracketed by synchronize,
+    # with one event pair around them (no event between the launches)
     torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    s0.record()
+    for i in range(args.steps):
+        fwd()
+        if not args.no_decode:
+            decode(i)
+    s1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    check_device_errors(dev)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gpu_ms_per_step = s0.elapsed_time(s1) / args.steps
+    # the same steps again with an event pair around every launch, for the
+    # per-launch distribution and the forward / decode split inside a step
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record()
         fwd()
         ev[i][1].record()
         if not args.no_decode:
-            decode(i)
+            decode(args.steps + i)
         ev[i][2].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     check_device_errors(dev)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
     fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    # the forward alone over a timed region: its average launch time
+    fwd_region = _time_region_ms(torch, fwd, args.steps, 1)
+    check_device_errors(dev)
     del u, dt_, z, Bm, Cm, out
     torch.cuda.empty_cache()
 
     traffic = measured_traffic(w.name) if args.bbar == "delta" else None
-    configs = {w.name: fwd_entry(w, fwd_ms, ceil, args.bbar, traffic)}
+    configs = {w.name: fwd_entry(w, fwd_ms, ceil, args.bbar, traffic, region_avg=fwd_region)}
     configs[w.name]["plan"] = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate, act)
     if not args.no_decode:
         # the decode in its own loop as well (inside the step it follows the
@@ -983,6 +1028,7 @@ def main():
             rot[0] += 1
 
         dec_alone = _time_ms(torch, decode_alone, args.steps, args.warmup)
+        dec_alone_region = _time_region_ms(torch, decode_alone, args.steps, 1)
         dec_avg = float(np.mean(dec_ms))
         dec_bytes = synth.algorithmic_bytes(dw)
         dgbs = dec_bytes / (dec_avg / 1e3) / 1e9
@@ -999,28 +1045,34 @@ def main():
             "frac_of_measured_update_in_place_decode_size":
                 dgbs / stream["update_in_place_decode_size"]["GBps"],
             "state_sets_rotated": n_rot,
-            "timing": "inside the step, right after the forward",
+            "timing": "inside the step, right after the forward (event pair around every "
+                      "launch)",
         }
-        da = float(np.mean(dec_alone))
+        da = float(dec_alone_region)
         dagbs = dec_bytes / (da / 1e3) / 1e9
         configs["decode"]["alone"] = {
             "avg_ms": da, "median_ms": float(np.median(dec_alone)),
             "min_ms": float(np.min(dec_alone)), "launches": len(dec_alone),
+            "per_call_avg_ms": float(np.mean(dec_alone)),
             "hbm_GBps": dagbs, "hbm_frac_of_8TBps": dagbs / HBM_PEAK_GBS,
             "frac_of_measured_update_in_place": dagbs / stream["update_in_place"]["GBps"],
             "frac_of_measured_copy": dagbs / stream["copy"]["GBps"],
             "frac_of_measured_update_in_place_decode_size":
                 dagbs / stream["update_in_place_decode_size"]["GBps"],
-            "timing": "back-to-back decode steps, state sets rotated",
+            "timing": ("back-to-back decode steps, state sets rotated; avg_ms over a "
+                       "region of back-to-back launches (one HIP event pair), median and min "
+                       "from an event pair around every launch"),
         }
     if not args.no_extra:
         for name in ("seq1m", "mamba130m"):
             if name == w.name:
                 continue
             ew = synth.WORKLOADS[name]
-            ms_e, sets_e = time_forward(torch, dev, ew, args.extra_steps, args.warmup, args.bbar)
+            ms_e, sets_e, region_e = time_forward(torch, dev, ew, args.extra_steps, args.warmup,
+                                                  args.bbar)
             configs[name] = fwd_entry(ew, ms_e, ceil, args.bbar,
-                                      measured_traffic(name) if args.bbar == "delta" else None)
+                                      measured_traffic(name) if args.bbar == "delta" else None,
+                                      region_avg=region_e)
             configs[name]["input_sets_rotated"] = sets_e
             configs[name]["plan"] = fwd_plan(ew.batch, ew.seqlen, ew.dim, ew.dstate,
                                              torch.bfloat16 if ew.dtype == "bf16"
@@ -1036,6 +1088,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "gpu_ms_per_step": gpu_ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

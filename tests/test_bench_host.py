@@ -38,6 +38,16 @@ def test_forward_entry_fractions():
     assert e["counter_traffic_over_algorithmic"] == pytest.approx(1.4e9 / nbytes)
 
 
+def test_forward_entry_takes_the_region_average():
+    w = synth.WORKLOADS["seq1m"]
+    ceil = {"fma_T_per_s": 35.0, "exp_T_per_s": 17.5}
+    e = bench.fwd_entry(w, [2.1, 2.0, 2.3], ceil, region_avg=1.95)
+    tokch = w.batch * w.seqlen * w.dim
+    assert e["avg_ms"] == 1.95 and e["tokens_channels_per_s"] == pytest.approx(tokch / 1.95e-3)
+    assert e["per_call_avg_ms"] == pytest.approx(2.1333333) and e["median_ms"] == 2.1
+    assert e["min_ms"] == 2.0 and "region" in e["timing"]
+
+
 def test_nominal_valu_peak():
     # 256 CUs x 4 SIMD16 x 16 lanes x 2.4 GHz
     assert bench.VALU_PEAK_TSLOTS == pytest.approx(39.3216)
