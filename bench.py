@@ -253,7 +253,7 @@ def bwd_bench(args, torch, dev):
     if args.train:
         fwd_train()
         torch.cuda.synchronize()
-        fwd_ms = _time_ms(torch, fwd_train, args.steps, args.warmup)
+        fwd_ms = _time_region_ms(torch, fwd_train, args.steps, args.warmup)
 
     def bwd():
         return selective_scan_bwd(u, dt, A, Bm, Cm, dout, D=Dv, z=z, delta_bias=bias, ckpt=ck)
@@ -262,16 +262,11 @@ def bwd_bench(args, torch, dev):
         bwd()
     torch.cuda.synchronize()
     check_device_errors(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for e in ev:
-        e[0].record()
-        bwd()
-        e[1].record()
-    torch.cuda.synchronize()
+    avg = _time_region_ms(torch, bwd, args.steps, 0)
     t1 = time.perf_counter()
-    ms = [e[0].elapsed_time(e[1]) for e in ev]
-    avg = float(np.mean(ms))
+    ms = _time_ms(torch, bwd, args.steps, 0)
+    check_device_errors(dev)
     tokch = w.batch * w.seqlen * w.dim
     slots = bwd_valu_slots_per_token_channel(w.dstate) * tokch
     achieved = slots / (avg / 1e3) / 1e12
@@ -297,10 +292,11 @@ def bwd_bench(args, torch, dev):
                             "slots per token*channel",
             "units_per_launch": tokch, "avg_launch_ms": avg,
             "median_launch_ms": float(np.median(ms)), "min_launch_ms": float(np.min(ms)),
+            "timing": "average over a region of back-to-back launches; median and min per launch",
         },
         "hbm": {"algorithmic_bytes": nbytes, "GBps": nbytes / (avg / 1e3) / 1e9,
                 "frac_of_8TBps": nbytes / (avg / 1e3) / 1e9 / HBM_PEAK_GBS},
-        "training_forward_ms": float(np.mean(fwd_ms)) if args.train else None,
+        "training_forward_ms": fwd_ms if args.train else None,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -356,16 +352,10 @@ def conv_bench(args, torch, dev):
     for _ in range(args.warmup):
         conv()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for ee in ev:
-        ee[0].record()
-        conv()
-        ee[1].record()
-    torch.cuda.synchronize()
+    avg = _time_region_ms(torch, conv, args.steps, 0)
     t1 = time.perf_counter()
-    ms = [ee[0].elapsed_time(ee[1]) for ee in ev]
-    avg = float(np.mean(ms))
+    ms = _time_ms(torch, conv, args.steps, 0)
     tokch = w.batch * w.seqlen * w.dim
     nbytes = 2 * e * tokch + 4 * (k * w.dim + w.dim) + 4 * w.batch * w.dim * (k - 1)
     gbps = nbytes / (avg / 1e3) / 1e9
@@ -383,7 +373,9 @@ def conv_bench(args, torch, dev):
                      "frac": gbps / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "conv1d_fwd_kernel", "bytes_per_launch": nbytes,
                      "avg_launch_ms": avg, "median_launch_ms": float(np.median(ms)),
-                     "min_launch_ms": float(np.min(ms))},
+                     "min_launch_ms": float(np.min(ms)),
+                     "timing": ("average over a region of back-to-back launches; median and "
+                                "min per launch")},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -460,19 +452,23 @@ def block_bench(args, torch, dev):
     M = w.batch * w.seqlen
     dm, di, n, r = cfg["d_model"], cfg["d_inner"], cfg["d_state"], cfg["dt_rank"]
     ms_block = _time_ms(torch, lambda: mamba_block_fwd(x, wt, out=out), args.steps, args.warmup)
+    reg_block = _time_region_ms(torch, lambda: mamba_block_fwd(x, wt, out=out), args.steps, 0)
     # the block's own conv1d and scan, alone on the same shapes
     xi = torch.randn(w.batch, w.seqlen, di, device=dev).to(act)
     u = torch.empty_like(xi)
-    ms_conv = _time_ms(torch, lambda: causal_conv1d_fwd(xi, wt["conv_w"], wt["conv_b"], out=u),
-                       args.steps, args.warmup)
+    conv_call = lambda: causal_conv1d_fwd(xi, wt["conv_w"], wt["conv_b"], out=u)  # noqa: E731
+    reg_conv = _time_region_ms(torch, conv_call, args.steps, args.warmup)
     dt = torch.randn(w.batch, w.seqlen, di, device=dev).to(act)
     Bm = torch.randn(w.batch, w.seqlen, n, device=dev).to(act)
     Cm = torch.randn(w.batch, w.seqlen, n, device=dev).to(act)
     y = torch.empty_like(xi)
-    ms_scan = _time_ms(torch, lambda: selective_scan_fwd(u, dt, wt["A"], Bm, Cm, D=wt["D"], z=xi,
-                                                         delta_bias=wt["dt_bias"], out=y),
-                       args.steps, args.warmup)
-    tb, tc, ts = (float(np.mean(v)) for v in (ms_block, ms_conv, ms_scan))
+    reg_scan = _time_region_ms(torch, lambda: selective_scan_fwd(u, dt, wt["A"], Bm, Cm,
+                                                                  D=wt["D"], z=xi,
+                                                                  delta_bias=wt["dt_bias"], out=y),
+                               args.steps, args.warmup)
+    # averages over timed regions of back-to-back launches; the block's
+    # median and min from an event pair around every call
+    tb, tc, ts = reg_block, reg_conv, reg_scan
     gemm_flops = 2 * M * (dm * 2 * di + di * (r + 2 * n) + r * di + di * dm)
     t_gemm = max(tb - tc - ts, 1e-6)
     gemm_tflops = gemm_flops / (t_gemm / 1e3) / 1e12
