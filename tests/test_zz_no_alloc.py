@@ -74,9 +74,16 @@ def test_noalloc_matches_the_allocating_forward_on_consecutive_calls():
 
 
 def test_noalloc_whole_and_split_and_chained_plans():
+    from selective_state_space_38_amd import fwd_plan
     # 300 chains: 256 whole, the rest split into look-back segments
     x = synth.make("mamba130m", batch=1, seqlen=600, dim=64 * 300, a_init="random")
     _compare(x, "f32", None, "whole + split")
+    # whole chains only (600 chains, no carry records: the call touches no
+    # scratch at all)
+    p = fwd_plan(2, 300, 64 * 300, 16, torch.bfloat16)
+    assert p["whole_chains"] == 600 and p["segments"] == 1, p
+    w = synth.make("mamba2p8b", batch=2, seqlen=300, dim=64 * 300, a_init="random")
+    _compare(w, "bf16", None, "whole chains only")
     # chained 64-step segments
     y = synth.make("mamba130m", batch=2, seqlen=1000, dim=96, a_init="random")
     with env(SSM_FORCE_LOOKBACK=0, SSM_FORCE_SEGMENT=64):
