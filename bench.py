@@ -20,7 +20,7 @@ Beside the timed step the same run measures:
   * the ceilings the fractions are taken against (libssm_micro probes: fp32
     FMA and v_exp_f32 rates, streaming HBM bandwidth);
   * the million-token and 130M-shaped forwards (their own timing loops, not
-    part of the step), so every north-star configuration has a number;
+    part of the step), so every benchmarked configuration has a number;
 and reports per configuration the HBM fraction of 8 TB/s (the metric), the
 VALU fraction (lane-slots/s) and the transcendental fraction.  `roofline`
 describes the 2.8B forward kernel; `cpu_baseline` times the float64 oracle on
