@@ -532,8 +532,9 @@ int conv_fwd_impl(const void* x, const float* weight, const float* bias, const f
   sh.seqlen = dims->seqlen;
   sh.dim = dims->dim;
   sh.silu = silu ? 1 : 0;
-  const int64_t ept = dims->dtype == SSM_BF16 ? 8 : 4;  // one 16-byte vector of channels
-  sh.vec_io = (dims->dim % ept == 0 && aligned(x, 16) && aligned(out, 16)) ? 1 : 0;
+  // runs of 4 channels, one vector of 16 (float32) or 8 (bfloat16) bytes
+  const uintptr_t run_bytes = dims->dtype == SSM_BF16 ? 8 : 16;
+  sh.vec_io = (dims->dim % 4 == 0 && aligned(x, run_bytes) && aligned(out, run_bytes)) ? 1 : 0;
   if (ssm::launch_conv1d_fwd(dims->dtype, width, p, sh, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return SSM_ELAUNCH;

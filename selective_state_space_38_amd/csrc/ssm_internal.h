@@ -186,16 +186,11 @@ struct ConvShape {
   int64_t batch;
   int64_t seqlen;
   int64_t dim;
-  int64_t runs;             // channel runs of one vector (set by the launcher)
-  int64_t tiles;            // time tiles of kConvTile steps (set by the launcher)
+  int64_t runs;             // runs of 4 channels (set by the launcher)
+  int64_t tiles;            // time tiles of the activation type's tile length (launcher)
   int32_t silu;
-  int32_t vec_io;           // rows of x / out may be moved in aligned 16-byte runs
+  int32_t vec_io;           // rows of x / out may be moved in aligned 4-channel runs
 };
-
-// Time steps per thread of the conv forward (the halo of K-1 rows is read
-// once more per tile, mostly from L2).  32 measured best against 64, 128 and
-// 256 at both the 2.8B (bf16) and 130M (f32) activation shapes.
-constexpr int kConvTile = 32;
 
 hipError_t launch_conv1d_fwd(int dtype, int width, const ConvPtrs& p, const ConvShape& sh,
                              hipStream_t stream);
