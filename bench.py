@@ -16,6 +16,9 @@ decode's rate is reported separately); `ms_per_step` is the wall time of a
 whole step over the K timed steps (`gpu_ms_per_step` the same from HIP
 events).  Per-launch medians and minima come from a second pass with an event
 pair around every launch (those events add a few microseconds to each).
+From idle the GPU's clocks ramp over some tens of milliseconds of sustained
+load, so every timed loop is preceded by at least 100 ms of untimed launches
+of the same work (then the W warm-up steps).
 Beside the timed step the same run measures:
   * the ceilings the fractions are taken against (libssm_micro probes: fp32
     FMA and v_exp_f32 rates, streaming HBM bandwidth);
@@ -393,8 +396,32 @@ def conv_bench(args, torch, dev):
     print(json.dumps(line), flush=True)
 
 
-def _time_ms(torch, fn, steps, warmup):
+# From idle the GPU takes some tens of milliseconds of sustained load to reach
+# its working clocks (measured: the 2.8B forward's first launches ~900 us,
+# settling at ~700 us after ~40 launches, ~30 ms; the same again after a
+# two-second pause).  Every timed loop below is therefore preceded by at least
+# WARM_MS of untimed launches of the same work, then its warm-up steps.
+WARM_MS = 100.0
+
+
+def _warm_gpu(torch, fn, min_ms=WARM_MS):
+    """Untimed calls of fn, in batches of ~5 ms of GPU work, until min_ms of
+    wall time has passed."""
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-6)
+    batch = max(1, int(5e-3 / one))
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+
+
+def _time_ms(torch, fn, steps, warmup, warm=True):
     """Per-call launch times (ms): an event pair around every call."""
+    if warm:
+        _warm_gpu(torch, fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -407,10 +434,12 @@ def _time_ms(torch, fn, steps, warmup):
     return [e[0].elapsed_time(e[1]) for e in ev]
 
 
-def _time_region_ms(torch, fn, steps, warmup):
+def _time_region_ms(torch, fn, steps, warmup, warm=True):
     """Average launch time (ms) over a timed region: one event pair around
     `steps` back-to-back calls (no event between them; an event recorded
     between every two calls adds its own few microseconds to each)."""
+    if warm:
+        _warm_gpu(torch, fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -588,6 +617,9 @@ def probe_valu(torch, dev, waves_per_simd=4, iters=256, reps=5):
         steps = blocks * 256 * iters * 16 * chains
         return steps / (ms / 1e3) / 1e12
 
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < WARM_MS:   # the clocks' ramp, untimed
+        rate(2, 8, waves_per_simd)
     fma = rate(0, 8, waves_per_simd)
     exp = rate(1, 8, waves_per_simd)
     mix_steps = rate(2, 8, waves_per_simd)    # element-steps: 1 exp + 4 FMA each
@@ -627,6 +659,11 @@ def probe_stream(torch, dev, nbytes=1 << 30, reps=5, sweep=False):
     # prefer many workgroups)
     shapes = ([(u, k) for u in (1, 2, 4, 8) for k in (4, 8, 16, 32, 64)] if sweep
               else [(1, 4), (2, 4), (1, 8), (2, 8), (1, 64)])
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < WARM_MS:   # the clocks' ramp, untimed
+        _ms(lambda p: lib.ssm_micro_stream(2, 1, COMPUTE_UNITS * 4, ctypes.c_void_p(a.data_ptr()),
+                                           ctypes.c_void_p(b.data_ptr()), nbytes, 1,
+                                           ctypes.c_void_p(sink.data_ptr()), 2, p, st))
     out = {}
     for mode, name, factor in ((0, "read", 1), (1, "write", 1), (2, "copy", 2),
                                (3, "update_in_place", 2)):
@@ -967,6 +1004,15 @@ def main():
         selective_state_update(states[i % n_rot], dx, ddt, dA, dB, dC, D=dD, z=dz,
                                dt_bias=dbias, dt_softplus=True, out=dout, bbar=args.bbar)
 
+    warm_i = [0]
+
+    def warm_step():
+        fwd()
+        if not args.no_decode:
+            decode(warm_i[0])
+        warm_i[0] += 1
+
+    _warm_gpu(torch, warm_step)   # the clocks' ramp (untimed), then the W warm-up steps
     for i in range(args.warmup):
         fwd()
         if not args.no_decode:
