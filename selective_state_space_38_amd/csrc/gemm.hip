@@ -3,8 +3,8 @@
 // the MFMA units).  A projection's weight is stored [out][in] (the layout of a
 // PyTorch linear layer), so both operands are contiguous along the reduction
 // dimension, the layout hipBLASLt's kernels run fastest on these shapes
-// (2.8B layer, bfloat16: in_proj 609 -> 569 us, out_proj 581 -> 540 us against
-// [in][out] weights).  One hipBLASLt handle per host thread and device,
+// (2.8B layer, bfloat16, each alone with the clocks warm: in_proj 619 -> 562
+// us, out_proj 603 -> 561 us against [in][out] weights).  One hipBLASLt handle per host thread and device,
 // created on first use and destroyed when the thread exits, so concurrent
 // callers on different threads never share state.  Each distinct problem
 // (shape, leading dimensions, type) keeps its descriptors and the algorithm
@@ -88,10 +88,11 @@ bool build_problem(hipblasLtHandle_t h, int dtype, int64_t M, int64_t N, int64_t
   if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return false;
   // The heuristic is asked with a workspace allowance: its ranking then
   // differs, and on these shapes the first candidate that needs no workspace
-  // is faster than the first candidate of a search without one (2.8B layer,
-  // bfloat16: in_proj 720 -> 569 us, out_proj 552 -> 540 us; 130M layer,
-  // float32: in_proj 322 -> 271 us).  Only candidates without workspace are
-  // taken, so no call allocates.
+  // is as fast or faster than the first candidate of a search without one
+  // (each alone, clocks warm: 2.8B layer, bfloat16, in_proj 593 -> 562 us,
+  // out_proj 557 -> 561 us, x_proj 75 -> 69 us, dt_proj 91 -> 88 us; 130M
+  // layer, float32, in_proj 303 -> 271 us).  Only candidates without
+  // workspace are taken, so no call allocates.
   const uint64_t allowance = uint64_t{64} << 20;
   hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
                                         &allowance, sizeof(allowance));
