@@ -856,8 +856,12 @@ def summarize_counters(fetch_dir, write_dir):
         short = m.group(1) if m else kname.split("(")[0]
         table.append(f"| `{short}` ({label}) | {np.mean(fv):,.0f} | "
                      f"{np.mean(wv):,.0f} | {fb + wb:,.0f} | {alg:,} | {(fb + wb) / alg:.3f} |")
+        def stats(v):
+            return {"dispatches": len(v), "mean": float(np.mean(v)), "min": float(np.min(v)),
+                    "max": float(np.max(v))}
+
         return {"kernel": kname, "grid_size": grid,
-                "counters_KiB_per_dispatch": {"FETCH_SIZE": fv, "WRITE_SIZE": wv},
+                "counters_KiB_per_dispatch": {"FETCH_SIZE": stats(fv), "WRITE_SIZE": stats(wv)},
                 "hbm_fetch_bytes_per_launch": fb, "hbm_write_bytes_per_launch": wb,
                 "hbm_bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": alg,
                 "traffic_over_algorithmic": (fb + wb) / alg}
