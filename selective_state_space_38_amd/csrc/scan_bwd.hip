@@ -513,7 +513,8 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
       }
       if constexpr (!kRed2) lds_barrier();  // the helpers have read the previous sums
       // the adjoint, last step first; step t - 1's LDS operands are read
-      // while step t computes (scheduling barriers keep the reads early)
+      // while step t computes (scheduling barriers keep the reads early:
+      // without them the training-pair backward measured 6% slower)
       float qdl[2], qdu[2], qdy[2], qB[2][G], qC[2][G];
       auto read_step = [&](int t) {
         const int q = t & 1;
