@@ -874,7 +874,7 @@ def summarize_counters(fetch_dir, write_dir):
         import torch
         plan = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate,
                         torch.bfloat16 if w.dtype == "bf16" else torch.float32)
-        threads = 64 * (plan["state_groups"] + 4)
+        threads = 64 * (plan["state_groups"] + plan["helper_waves"])
         ns = "fwd_bf16::scan_fwd_kernel" if w.dtype == "bf16" else "fwd_f32::scan_fwd_kernel"
         e = entry(ns, plan["workgroups"] * threads, w, name)
         if e is None:
@@ -916,7 +916,7 @@ def summarize_trace(directory):
         plan = fwd_plan(w.batch, w.seqlen, w.dim, w.dstate,
                         torch.bfloat16 if w.dtype == "bf16" else torch.float32)
         ns = "fwd_bf16::" if w.dtype == "bf16" else "fwd_f32::"
-        names[(ns, plan["workgroups"] * 64 * (plan["state_groups"] + 4))] = name
+        names[(ns, plan["workgroups"] * 64 * (plan["state_groups"] + plan["helper_waves"]))] = name
     print("| kernel | grid (threads) | workload | launches | avg us | median us | min us |")
     print("|---|---|---|---|---|---|---|")
     for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):

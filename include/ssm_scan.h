@@ -365,7 +365,10 @@ int ssm_check_device_errors(void* stream);
  * aggregates (decoupled look-back), 0 if each waits for its predecessor's
  * final state; chunk = steps staged through LDS at a time; workgroups = the
  * launch's grid; whole_chains = how many (batch row, channel block) chains run
- * the whole sequence in one workgroup (the others are split into `segments`).
+ * the whole sequence in one workgroup (the others are split into `segments`);
+ * helper_waves = waves per workgroup that stage the inputs and finish the
+ * outputs beside the state_groups scan waves (a workgroup has
+ * 64 * (state_groups + helper_waves) threads).
  * Returns SSM_OK or a validation error.
  */
 typedef struct {
@@ -378,6 +381,7 @@ typedef struct {
   int64_t workgroups;
   int32_t whole_chains;
   int32_t first_segment_len;
+  int32_t helper_waves;
 } ssm_fwd_plan;
 
 int ssm_fwd_plan_for(const ssm_dims* dims, ssm_fwd_plan* plan);

@@ -63,6 +63,7 @@ class SsmFwdPlan(ctypes.Structure):
         ("workgroups", ctypes.c_int64),
         ("whole_chains", ctypes.c_int32),
         ("first_segment_len", ctypes.c_int32),
+        ("helper_waves", ctypes.c_int32),
     ]
 
 

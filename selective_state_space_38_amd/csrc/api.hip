@@ -166,6 +166,7 @@ void plan_forward(const ssm_dims& d, ssm_fwd_plan* p) {
   p->workgroups = whole + (chains - whole) * n_seg;
   p->whole_chains = static_cast<int32_t>(whole);
   p->first_segment_len = static_cast<int32_t>(first_len);
+  p->helper_waves = ssm::helper_waves(groups, g);
 }
 
 int check_dims(const ssm_dims* dims) {
@@ -284,7 +285,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.n_ckpt = div_up(dims->seqlen, ssm::kBwdChunk);
   {
     // per-thread runs of the chunk tile: chunk / helper waves consecutive channels
-    const int64_t ept = plan.chunk / ssm::helper_waves(plan.state_groups);
+    const int64_t ept = plan.chunk / plan.helper_waves;
     const int64_t esz = dims->dtype == SSM_BF16 ? 2 : 4;
     const uintptr_t need = static_cast<uintptr_t>(ept * esz >= 16 ? 16 : ept * esz);
     bool ok = ept * esz >= 4 && dims->dim % ept == 0;

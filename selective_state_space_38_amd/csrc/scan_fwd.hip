@@ -15,18 +15,19 @@
 // MambaMini" Step 2, (a_j a_i, a_j b_i + b_j), applied to segment aggregates.
 //
 // Work decomposition.  A workgroup owns one (batch, block of 64 channels,
-// sequence segment).  Its NG waves split the N states of every channel into
-// groups of G (lane = channel, registers = the group's states), so every lane
-// of a wave reads the same B_t / C_t slice (an LDS broadcast) and no lane
-// ever exchanges data with another lane.  Time is walked serially inside the
-// segment in chunks of TC steps:
-//   P  (per chunk, one chunk ahead): coalesced loads of dt/u for steps
-//      t = w mod NG and of the chunk's B/C rows; Delta, Delta*u, D*u and
-//      float B/C -> LDS (double buffered);
-//   S  (all steps): per state exp2(Delta*A*log2 e), h = a*h + Delta*u*B,
-//      y_partial += C*h -> LDS;
-//   E  (steps t = w mod NG): sum the NG partials, add D*u, gate with SiLU(z),
-//      round and store.
+// sequence segment).  Its NG scan waves split the N states of every channel
+// into groups of G (lane = channel, registers = the group's states), so every
+// lane of a wave reads the same B_t / C_t slice (an LDS broadcast) and no
+// lane ever exchanges data with another lane.  NP helper waves do the
+// rest; each helper thread owns one run of TC / NP channels of one tile row.
+// Time is walked serially inside the segment in chunks of TC steps:
+//   P  (helpers, one chunk ahead): coalesced loads of the chunk's dt/u/z
+//      rows and B/C rows; Delta, Delta*u and float B/C -> LDS (double
+//      buffered), D*u and z kept in registers;
+//   S  (scan waves, all steps): per state exp2(Delta*A*log2 e),
+//      h = a*h + Delta*u*B, y_partial += C*h -> LDS;
+//   E  (helpers, one chunk behind): sum the NG partials, add D*u, gate with
+//      SiLU(z), round and store.
 // The expanded state (B, L, D, N) exists only in registers.
 //
 // Segments of the same channel block are ordered by an atomic ticket
@@ -724,7 +725,7 @@ template <typename T, int NG, int G>
 static hipError_t launch_typed(const FwdPtrs& p, const FwdScratch& s, const FwdShape& sh,
                                int64_t workgroups, hipStream_t stream) {
   constexpr int TC = chunk_for_groups(NG);
-  constexpr int NP = helper_waves(NG);
+  constexpr int NP = helper_waves(NG, G);
   const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * (NG + NP));
 #define SSM_LAUNCH_FWD(Z, V)                                                                 \
   hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, NP, TC, Z, V>), grid, block, 0, stream,       \

@@ -62,14 +62,21 @@ struct FwdPtrs {
 };
 
 // Forward workgroup shape: `groups` scan waves (one per state group) plus
-// four helper waves (one per SIMD) that stage the chunk tiles and finish the
-// outputs.  Chunk length (timesteps staged
-// through LDS per iteration): 32 for one or two state groups, 16 from four
-// on, where two workgroups of 8 waves must fit a CU's LDS (the tiles and the
-// partial readouts of every group are double buffered).  Segments are a
-// multiple of the instance's chunk.
+// helper waves that stage the chunk tiles and finish the outputs.  Chunk
+// length (timesteps staged through LDS per iteration): 32 for one or two
+// state groups, 16 from four on, where two workgroups must fit a CU's LDS
+// (the tiles and the partial readouts of every group are double buffered).
+// Segments are a multiple of the instance's chunk.
 constexpr int chunk_for_groups(int groups) { return groups >= 4 ? 16 : 32; }
-constexpr int helper_waves(int /*groups*/) { return 4; }
+// Helpers: eight (two runs of a tile row each) where the chunk is 16 and a
+// scan wave holds at most four states, so the helpers' part of every
+// iteration is short and two 12-wave workgroups still fit a CU's registers
+// (measured, warm: d_state 16 at 1536 and 5120 channels 2.0% and 0.6%
+// faster, d_state 32 0.8%); four otherwise (d_state 64 with eight states a
+// wave measured 1.9% slower with eight, and a lone state group spills).
+constexpr int helper_waves(int groups, int per_group) {
+  return groups >= 4 && per_group <= 4 ? 8 : 4;
+}
 
 // The forward is built once per activation type; each build lives in its own
 // namespace (fwd_f32, fwd_bf16) with the same interface:

@@ -211,6 +211,22 @@ def test_plan_covers_every_supported_state_size():
                                         ctypes.byref(plan)) == SSM_OK
             assert plan.state_groups * plan.states_per_group == n
             assert (plan.segments - 1) * plan.segment_len < L <= plan.segments * plan.segment_len
+            # every helper thread owns a whole run of a tile row; a workgroup
+            # stays within the hardware's 1024 threads
+            assert plan.helper_waves in (4, 8) and plan.chunk % plan.helper_waves == 0
+            assert 64 * (plan.state_groups + plan.helper_waves) <= 1024
+
+
+def test_plan_helper_waves():
+    # eight helpers where the chunk is 16 steps and a scan wave holds at most
+    # four states, four otherwise
+    lib = _lib.load()
+    plan = _lib.SsmFwdPlan()
+    for n, want in ((4, 4), (8, 4), (16, 8), (32, 8), (64, 4)):
+        assert lib.ssm_fwd_plan_for(ctypes.byref(_dims(b=4, L=2048, d=5120, n=n, dtype=1)),
+                                    ctypes.byref(plan)) == SSM_OK
+        assert plan.helper_waves == want, (n, plan.state_groups, plan.states_per_group)
+        assert (plan.chunk == 16) == (plan.state_groups >= 4)
 
 
 @pytest.mark.parametrize("bbar", [-1, 2, 7])
