@@ -45,6 +45,12 @@ RAGGED = [
     ("mamba130m", 1, 257, 130, 32, "random"),
     ("mamba130m", 1, 257, 130, 64, "random"),
     ("mamba2p8b", 1, 129, 70, 64, "random"),
+    # bfloat16 with eight helper waves: 32 states (eight scan waves, 1024-thread
+    # workgroups) and an odd channel count (helper runs of two channels take
+    # the element path)
+    ("mamba2p8b", 2, 300, 100, 32, "random"),
+    ("mamba2p8b", 1, 129, 131, 16, "random"),
+    ("mamba130m", 1, 129, 131, 16, "random"),
 ]
 
 
@@ -120,14 +126,16 @@ def test_first_segment_length(tag, lookback, seg, first):
     check_forward(x, tag, got, st, ref, ref_st)
 
 
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
 @pytest.mark.parametrize("groups_per", [1, 2, 4, 8])
-def test_state_group_layouts(groups_per):
+def test_state_group_layouts(groups_per, tag):
     """Every instantiated split of 16 states over waves gives the same answer."""
-    x = _case("mamba130m", batch=2, seqlen=190, dim=70, dstate=16, a_init="random")
+    wl = "mamba130m" if tag == "f32" else "mamba2p8b"
+    x = _case(wl, batch=2, seqlen=190, dim=70, dstate=16, a_init="random")
     with env(SSM_FORCE_STATES_PER_GROUP=16 // groups_per):
-        got, st = gpu_forward(x, "f32")
+        got, st = gpu_forward(x, tag)
     ref, ref_st = oracle_forward(x)
-    check_forward(x, "f32", got, st, ref, ref_st)
+    check_forward(x, tag, got, st, ref, ref_st)
 
 
 def test_initial_state_and_resume():
