@@ -68,12 +68,13 @@ struct FwdPtrs {
 // (the tiles and the partial readouts of every group are double buffered).
 // Segments are a multiple of the instance's chunk.
 constexpr int chunk_for_groups(int groups) { return groups >= 4 ? 16 : 32; }
-// Helpers: eight (two runs of a tile row each) where the chunk is 16 and a
-// scan wave holds at most four states, so the helpers' part of every
-// iteration is short and two 12-wave workgroups still fit a CU's registers
-// (measured, warm: d_state 16 at 1536 and 5120 channels 2.0% and 0.6%
-// faster, d_state 32 0.8%); four otherwise (d_state 64 with eight states a
-// wave measured 1.9% slower with eight, and a lone state group spills).
+// Helpers: eight where the chunk is 16 and a scan wave holds at most four
+// states (each helper thread then owns a run of two channels of one tile
+// row), so the helpers' part of every iteration is short; at d_state 16 two
+// 12-wave workgroups still fit a CU's registers.  Measured warm: d_state 16
+// at 1536 and 5120 channels 2.0% and 0.6% faster than with four, d_state 32
+// 0.8%.  Four otherwise: d_state 64 with eight states a wave measured 1.9%
+// slower with eight, and a lone 16-state group spills.
 constexpr int helper_waves(int groups, int per_group) {
   return groups >= 4 && per_group <= 4 ? 8 : 4;
 }
