@@ -98,6 +98,17 @@ def test_zoh_2p8b_workload_sampled():
     check("last_state", g_st, ref_st, scale, TOL["bf16"])
 
 
+def test_zoh_130m_workload_full():
+    """The 130M-shaped layer (8 x 2048 x 1536 x 16, float32) with the exact
+    zero-order hold, every output and final state checked."""
+    x = synth.make("mamba130m")
+    _log("zoh 130M full-size")
+    got, st = gpu_forward(x, "f32", bbar="zoh")
+    ref, ref_st = oracle_forward(x, bbar="zoh")
+    e1, e2, s = check_forward(x, "f32", got, st, ref, ref_st)
+    _log(f"  err/scale {e1 / s:.2e} state {e2 / s:.2e}")
+
+
 def test_zoh_seq1m_workload_sampled():
     """The million-token sequence with the exact zero-order hold: 128
     look-back segments per channel block, whose aggregates carry the ZOH
@@ -140,6 +151,18 @@ def test_zoh_decode_shapes(n, tag):
     scale = float(np.max(np.abs(ref)))
     check("decode out", got, ref, scale, TOL[tag])
     check("decode state", gst, ref_st, scale, TOL[tag])
+
+
+def test_zoh_decode_workload_full():
+    """The decode workload (256 sequences, 5120 channels, 16 states, bf16)
+    with the exact zero-order hold, every output and state checked."""
+    x = synth.make("decode")
+    got, gst = _gpu_update(x, "bf16", x["state"], "zoh")
+    ref, ref_st = oracle.state_update(x["state"], x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                      x["D"], x["z"], x["dt_bias"], bbar="zoh")
+    scale = float(np.max(np.abs(ref)))
+    check("decode out", got, ref, scale, TOL["bf16"])
+    check("decode state", gst, ref_st, scale, TOL["bf16"])
 
 
 def test_zoh_decode_loop_equals_forward():
