@@ -28,6 +28,8 @@ from .scan import (  # noqa: F401
     scan_fwd,
     state_update,
     scan_pairs_blelloch,
+    segment_aggregate,
+    carry_combine,
 )
 from .scan_bwd import scan_bwd  # noqa: F401
 from .conv1d import causal_conv1d, conv1d_update  # noqa: F401

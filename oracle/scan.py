@@ -204,3 +204,55 @@ def scan_pairs_blelloch(a, b):
     # inclusive = own element applied after the exclusive prefix
     ia, ib = combine((oa, ob), (xa, xb))
     return ia[..., :L], ib[..., :L]
+
+
+def segment_aggregate(u, delta, A, B, dt_bias=None, delta_softplus=True, h0=None,
+                      bbar="delta"):
+    """Carry record of one sequence segment: its sum of Delta and its end state.
+
+    "Mamba / MambaMini", Steps 2-4: the steps of a segment compose under the
+    pair operator into one transform (A_cum, B_cum), and the state after the
+    segment is A_cum * h_start + B_cum.  A is time-invariant, so the product
+    of the per-step decays exp(Delta_t A) is exp(A * sum_t Delta_t): a
+    segment's A_cum is carried by one number per (batch, channel).  B_cum is
+    the state the segment reaches from h_start = 0.
+
+    Returns (sum_delta [batch, dim], state [batch, dim, dstate]) where
+    ``state`` is the state after the last step starting from ``h0`` (zeros
+    when None, which makes it B_cum).  No readout is formed.
+    """
+    u, delta, A, B = map(_f64, (u, delta, A, B))
+    dt_bias, h0 = map(_f64, (dt_bias, h0))
+    bsz, L, dim = u.shape
+    h = np.zeros((bsz, dim, A.shape[1])) if h0 is None else h0.copy()
+    total = np.zeros((bsz, dim))
+    for t in range(L):
+        dl = _delta(delta[:, t], dt_bias, delta_softplus)
+        Abar, bx = discretise(dl, A, B[:, t], u[:, t], bbar)
+        h = Abar * h + bx
+        total = total + dl
+    return total, h
+
+
+def carry_combine(sum_delta, agg, A, h0=None):
+    """Start state of every segment of a sequence from the segments' records.
+
+    ``sum_delta`` [S, batch, dim] and ``agg`` [S, batch, dim, dstate] are the
+    records of S consecutive segments (each ``agg`` from a zero start).  The
+    start of segment 0 is h0 (zeros when None); segment s + 1 starts from
+    segment s's transform (exp(A sum_delta[s]), agg[s]) applied to segment s's
+    start: the exclusive prefix of the pair operator over the segment index
+    ("Mamba / MambaMini", Steps 2 and 4), folded in sequence order.
+
+    Returns (h_in [S, batch, dim, dstate], h_out [batch, dim, dstate]), h_out
+    being the state after the last segment.
+    """
+    sum_delta, agg, A, h0 = map(_f64, (sum_delta, agg, A, h0))
+    S = agg.shape[0]
+    h = np.zeros(agg.shape[1:]) if h0 is None else h0.copy()
+    h_in = np.empty(agg.shape)
+    for s in range(S):
+        h_in[s] = h
+        a = np.exp(sum_delta[s][..., None] * A)
+        _, h = combine((a, agg[s]), (np.ones_like(h), h))
+    return h_in, h
