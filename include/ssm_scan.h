@@ -24,6 +24,12 @@
  *                          Bbar = (Delta A)^-1 (exp(Delta A) - 1) Delta B,
  *                          which for the diagonal A is (exp(Delta A) - 1)/A * B
  *                          (limit Delta*B where A = 0).
+ *   selective_scan_fwd_aggregate, selective_scan_carry_combine
+ *                          A segment's carry record (sum of Delta, state
+ *                          reached) and the fold of consecutive segments'
+ *                          records into their start states ("Mamba /
+ *                          MambaMini" Steps 2-4): a sequence scanned in
+ *                          independent pieces.
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library
@@ -160,6 +166,54 @@ int selective_scan_fwd_ex(const void* u, const void* delta, const float* A,
                           const float* h0, int bbar, void* out,
                           float* last_state, const ssm_dims* dims,
                           void* stream);
+
+/*
+ * Carry record of a sequence segment: the forward's recurrence over the
+ * segment without its readout ("Mamba / MambaMini" Steps 2-4: a segment's
+ * steps compose under the pair operator into one transform (A_cum, B_cum);
+ * A being time-invariant, A_cum = exp(A * sum_t Delta_t), so the record is the
+ * sum of Delta per (batch, channel) plus the state reached).  This is the
+ * first pass of a sequence split into segments (or across devices): scan every
+ * segment from a zero state, combine the records (selective_scan_carry_combine),
+ * then produce each segment's outputs from its true start state
+ * (selective_scan_fwd_h0 / _ex with h0).  It reads only u, delta and B.
+ *   u, delta, B, A, dt_bias, softplus, bbar : as selective_scan_fwd_ex
+ *   h0         : [B][D][N] float32 start state (nullable = zeros, which gives
+ *                the segment's B_cum)
+ *   sum_delta  : [B][D] float32, written: sum over the L steps of Delta
+ *   state      : [B][D][N] float32, written: the state after step L-1
+ *                (equal, up to rounding order, to selective_scan_fwd_ex's
+ *                last_state on the same inputs)
+ * sum_delta and state are required and must not alias each other or an
+ * input (SSM_EINVAL).  Scratch, stream ordering and carry-wait bounds as
+ * selective_scan_fwd (long sequences are split into concurrently scanned
+ * pieces internally).
+ */
+int selective_scan_fwd_aggregate(const void* u, const void* delta, const float* A,
+                                 const void* B, const float* dt_bias, int softplus,
+                                 const float* h0, int bbar, float* sum_delta,
+                                 float* state, const ssm_dims* dims, void* stream);
+
+/*
+ * Start states of S consecutive sequence segments from their carry records
+ * (selective_scan_fwd_aggregate with h0 = NULL on each segment): h_in[0] = h0
+ * (zeros when NULL) and h_in[s+1] = exp(A * sum_delta[s]) * h_in[s] + agg[s],
+ * the exclusive prefix of the pair operator over the segment index
+ * ("Mamba / MambaMini" Steps 2 and 4), folded in segment order.
+ *   sum_delta : [S][B][D] float32;  agg : [S][B][D][N] float32
+ *   A         : [D][N] float32;     h0  : [B][D][N] float32 (nullable)
+ *   h_in      : [S][B][D][N] float32, written (required)
+ *   h_out     : [B][D][N] float32, written when non-NULL: the state after
+ *               the last segment
+ *   segments  : S >= 1.  dims: batch, dim, dstate as for the records;
+ *               dims->seqlen and dims->dtype are ignored (all float32).
+ * Outputs must not alias inputs or each other (SSM_EINVAL).  Allocates
+ * nothing; asynchronous on `stream`.
+ */
+int selective_scan_carry_combine(const float* sum_delta, const float* agg,
+                                 const float* A, const float* h0, float* h_in,
+                                 float* h_out, int64_t segments,
+                                 const ssm_dims* dims, void* stream);
 
 /*
  * One decode step, in place on `state`.

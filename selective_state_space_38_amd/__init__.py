@@ -3,6 +3,8 @@ with hand-written HIP kernels, and a thin PyTorch binding."""
 
 from .api import (  # noqa: F401
     selective_scan_fwd,
+    selective_scan_fwd_aggregate,
+    selective_scan_carry_combine,
     selective_scan_bwd,
     ckpt_buffer,
     selective_state_update,

@@ -27,6 +27,8 @@ EXPORTED = (
     "selective_scan_fwd_h0",
     "selective_scan_fwd_noalloc",
     "selective_scan_fwd_ex",
+    "selective_scan_fwd_aggregate",
+    "selective_scan_carry_combine",
     "selective_scan_bwd",
     "selective_scan_fwd_train",
     "selective_scan_bwd_ckpt",
@@ -135,6 +137,12 @@ def load():
     lib.selective_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                           vp, ctypes.c_int, vp, vp, dims_p, vp]
     lib.selective_scan_fwd_ex.restype = ctypes.c_int
+    lib.selective_scan_fwd_aggregate.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                                 ctypes.c_int, vp, vp, dims_p, vp]
+    lib.selective_scan_fwd_aggregate.restype = ctypes.c_int
+    lib.selective_scan_carry_combine.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64,
+                                                 dims_p, vp]
+    lib.selective_scan_carry_combine.restype = ctypes.c_int
     lib.selective_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp]
     lib.selective_scan_bwd.restype = ctypes.c_int

@@ -144,6 +144,70 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return (out, last_state) if return_last_state else out
 
 
+def selective_scan_fwd_aggregate(u, delta, A, B, delta_bias=None, delta_softplus=True,
+                                 h0=None, bbar="delta", sum_delta=None, state=None):
+    """Carry record of a sequence segment on the GPU: (sum of Delta
+    [batch, dim], state after the last step [batch, dim, dstate]), both
+    float32, from h0 (zeros when None).  Shapes and dtypes as
+    selective_scan_fwd; C, D and z play no part."""
+    code = _bbar_code(bbar)
+    if u.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {u.dtype}")
+    bsz, L, dim = u.shape
+    dstate = A.shape[1]
+    dev = u.device
+    act = u.dtype
+    _check(u, "u", act, (bsz, L, dim), dev)
+    _check(delta, "delta", act, (bsz, L, dim), dev)
+    _check(B, "B", act, (bsz, L, dstate), dev)
+    _check(A, "A", torch.float32, (dim, dstate), dev)
+    _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _check(h0, "h0", torch.float32, (bsz, dim, dstate), dev)
+    if sum_delta is None:
+        sum_delta = torch.empty((bsz, dim), dtype=torch.float32, device=dev)
+    if state is None:
+        state = torch.empty((bsz, dim, dstate), dtype=torch.float32, device=dev)
+    _check(sum_delta, "sum_delta", torch.float32, (bsz, dim), dev)
+    _check(state, "state", torch.float32, (bsz, dim, dstate), dev)
+    dims = _lib.SsmDims(bsz, L, dim, dstate, _DTYPES[act])
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.selective_scan_fwd_aggregate(
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(delta_bias),
+            1 if delta_softplus else 0, _ptr(h0), code, _ptr(sum_delta), _ptr(state),
+            ctypes.byref(dims), _stream(dev))
+    _raise(rc)
+    return sum_delta, state
+
+
+def selective_scan_carry_combine(sum_delta, agg, A, h0=None, h_in=None, h_out=None):
+    """Start states of S consecutive segments from their carry records:
+    sum_delta [S, batch, dim], agg [S, batch, dim, dstate] (float32, each
+    from selective_scan_fwd_aggregate with h0=None).  Returns (h_in
+    [S, batch, dim, dstate], h_out [batch, dim, dstate]): every segment's
+    start state from h0 (zeros when None) and the state after the last."""
+    S, bsz, dim, dstate = agg.shape
+    dev = agg.device
+    _check(sum_delta, "sum_delta", torch.float32, (S, bsz, dim), dev)
+    _check(agg, "agg", torch.float32, (S, bsz, dim, dstate), dev)
+    _check(A, "A", torch.float32, (dim, dstate), dev)
+    _check(h0, "h0", torch.float32, (bsz, dim, dstate), dev)
+    if h_in is None:
+        h_in = torch.empty_like(agg)
+    if h_out is None:
+        h_out = torch.empty((bsz, dim, dstate), dtype=torch.float32, device=dev)
+    _check(h_in, "h_in", torch.float32, (S, bsz, dim, dstate), dev)
+    _check(h_out, "h_out", torch.float32, (bsz, dim, dstate), dev)
+    dims = _lib.SsmDims(bsz, 1, dim, dstate, _lib.SSM_F32)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.selective_scan_carry_combine(
+            _ptr(sum_delta), _ptr(agg), _ptr(A), _ptr(h0), _ptr(h_in), _ptr(h_out), S,
+            ctypes.byref(dims), _stream(dev))
+    _raise(rc)
+    return h_in, h_out
+
+
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
                        delta_softplus=True, h0=None, dlast=None, ckpt=None):
     """Backward of selective_scan_fwd (Delta*B input) on the GPU.

@@ -22,6 +22,7 @@ SOURCES = [
     ("scan_fwd.hip", "scan_fwd_bf16", ["-DSSM_FWD_DTYPE=1"]),
     ("scan_bwd.hip", "scan_bwd", []),
     ("state_update.hip", "state_update", []),
+    ("carry.hip", "carry", []),
     ("conv1d.hip", "conv1d", []),
     ("gemm.hip", "gemm", []),
 ]

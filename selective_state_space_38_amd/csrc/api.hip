@@ -197,19 +197,25 @@ int64_t ckpt_y_offset(const ssm_dims* dims) { return div_up(ckpt_state_bytes(dim
 int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
              const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
              int bbar, void* out, float* last_state, float* ckpt, const ssm_dims* dims,
-             void* stream, bool no_out = false, bool no_alloc = false) {
+             void* stream, bool no_out = false, bool no_alloc = false,
+             float* sum_delta_out = nullptr) {
   int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
   if (bbar != SSM_BBAR_DELTA && bbar != SSM_BBAR_ZOH) return SSM_EINVAL;
-  if (!u || !delta || !A || !B || !C || (!out && !no_out) || (no_out && !ckpt))
+  // aggregate-only mode (the carry record of a segment): no C, readout or outputs
+  const bool agg_only = sum_delta_out != nullptr;
+  if (agg_only && (!last_state || out || ckpt || C || D || z || no_out)) return SSM_EINVAL;
+  if (!u || !delta || !A || !B || (!C && !agg_only) || (!out && !no_out && !agg_only) ||
+      (no_out && !ckpt))
     return SSM_EINVAL;
-  const void* ptrs[] = {u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
+  const void* ptrs[] = {u, delta, A, B, C, D, z, dt_bias, h0, out, last_state, sum_delta_out};
   for (const void* p : ptrs)
     if (p && !aligned(p, 4)) return SSM_EALIGN;
   const void* inputs[] = {u, delta, A, B, C, D, z, dt_bias, h0};
   for (const void* p : inputs)
-    if (p && (p == out || p == last_state)) return SSM_EINVAL;
+    if (p && (p == out || p == last_state || p == sum_delta_out)) return SSM_EINVAL;
   if (last_state && last_state == out) return SSM_EINVAL;
+  if (sum_delta_out && sum_delta_out == last_state) return SSM_EINVAL;
 
   ssm_fwd_plan plan;
   plan_forward(*dims, &plan);
@@ -229,7 +235,11 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const int64_t off_inc = up256(n_int * 4);
   const int64_t inc_bytes = need_carry ? up256(recs * N * 64 * 4) : 0;
   const int64_t aggb_bytes = plan.lookback ? up256(recs * N * 64 * 4) : 0;
-  const int64_t aggs_bytes = plan.lookback ? up256(recs * plan.state_groups * 64 * 4) : 0;
+  // sums of Delta: read by look-back walks, and in aggregate-only mode by a
+  // chain's last segment (which adds up the chain's total)
+  const int64_t aggs_bytes = (plan.lookback || (agg_only && need_carry))
+                                 ? up256(recs * plan.state_groups * 64 * 4)
+                                 : 0;
   const int64_t total = off_inc + inc_bytes + aggb_bytes + aggs_bytes;
 
   // a plan of whole chains only takes no ticket and publishes no carry: no
@@ -282,6 +292,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.has_h0 = h0 != nullptr;
   sh.has_last = last_state != nullptr;
   sh.zoh = bbar == SSM_BBAR_ZOH ? 1 : 0;
+  sh.agg_only = agg_only ? 1 : 0;
   sh.n_ckpt = div_up(dims->seqlen, ssm::kBwdChunk);
   {
     // per-thread runs of the chunk tile: chunk / helper waves consecutive channels
@@ -297,7 +308,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     sh.vec_io = ok ? 1 : 0;
   }
 
-  ssm::FwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
+  ssm::FwdPtrs p{u, delta, A, B, C, D, z, dt_bias, h0, out, last_state, sum_delta_out};
 
   rc = SSM_OK;
   const bool f32 = dims->dtype == SSM_F32;
@@ -721,6 +732,41 @@ int selective_scan_fwd_train(const void* u, const void* delta, const float* A, c
     if (q && q == ckpt) return SSM_EINVAL;
   return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, SSM_BBAR_DELTA, out,
                   last_state, ckpt, dims, stream);
+}
+
+int selective_scan_fwd_aggregate(const void* u, const void* delta, const float* A,
+                                 const void* B, const float* dt_bias, int softplus,
+                                 const float* h0, int bbar, float* sum_delta, float* state,
+                                 const ssm_dims* dims, void* stream) {
+  if (!sum_delta || !state) return SSM_EINVAL;
+  return fwd_impl(u, delta, A, B, nullptr, nullptr, nullptr, dt_bias, softplus, h0, bbar,
+                  nullptr, state, nullptr, dims, stream, /*no_out=*/false, /*no_alloc=*/false,
+                  sum_delta);
+}
+
+int selective_scan_carry_combine(const float* sum_delta, const float* agg, const float* A,
+                                 const float* h0, float* h_in, float* h_out, int64_t segments,
+                                 const ssm_dims* dims, void* stream) {
+  if (!dims) return SSM_EINVAL;
+  ssm_dims d1 = *dims;
+  d1.seqlen = 1;  // the sequence length plays no part here
+  d1.dtype = SSM_F32;
+  const int rc = check_dims(&d1);
+  if (rc != SSM_OK) return rc;
+  if (segments < 1 || segments > (1LL << 31) - 1) return SSM_EINVAL;
+  if (div_up(d1.batch * d1.dim * d1.dstate, 256) > (1LL << 31) - 1) return SSM_EINVAL;
+  if (!sum_delta || !agg || !A || !h_in) return SSM_EINVAL;
+  const void* ptrs[] = {sum_delta, agg, A, h0, h_in, h_out};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return SSM_EALIGN;
+  const void* inputs[] = {sum_delta, agg, A, h0};
+  for (const void* p : inputs)
+    if (p && (p == h_in || p == h_out)) return SSM_EINVAL;
+  if (h_out && h_out == h_in) return SSM_EINVAL;
+  const hipError_t e = ssm::launch_carry_combine(sum_delta, agg, A, h0, h_in, h_out, segments,
+                                                 d1.batch, d1.dim, static_cast<int>(d1.dstate),
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSM_OK : SSM_ELAUNCH;
 }
 
 int64_t ssm_ckpt_bytes(const ssm_dims* dims) {

@@ -44,6 +44,11 @@
 //                     outputs (and publishes its final state at the end).
 // Every wait is bounded; a wait that hits the bound bumps a device error
 // counter and continues with the carry gathered so far.
+//
+// Aggregate-only instances (AGG) stop before the outputs: they return the
+// sequence's end state and its sum of Delta, the carry record with which
+// independently scanned pieces of a sequence are joined ("Mamba / MambaMini"
+// Steps 2-4).  Only u, dt and B are read.
 
 #include "ssm_device.h"
 #include "ssm_internal.h"
@@ -92,7 +97,7 @@ __device__ __forceinline__ int wait_status(const int* p, int need, int limit) {
   return v;
 }
 
-template <typename T, int NG, int G, int NP, int TC, bool ZOH, bool VEC>
+template <typename T, int NG, int G, int NP, int TC, bool ZOH, bool VEC, bool AGG>
 __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     const T* __restrict__ u, const T* __restrict__ dtp,
     const float* __restrict__ A, const T* __restrict__ Bm,
@@ -444,11 +449,10 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     }
   };
 
-  // aggregate pass of a look-back segment: own final state from zero and
-  // the sum of Delta (the helpers stage dt, u and B only)
+  // aggregate pass: the state reached from hA's initial value (zero for a
+  // look-back segment's own aggregate) and the sum of Delta; the helpers
+  // stage dt, u and B only
   auto scan_aggregate = [&](float (&hA)[G], float& sum_delta) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) hA[g] = 0.0f;
     sum_delta = 0.0f;
     lds_barrier();  // helpers' prologue staged chunk 0
     for (int c = 0; c < n_chunks; ++c) {
@@ -554,6 +558,7 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
 
   // ---- carry-in ------------------------------------------------------------
   float h[G];
+  float own_sum_delta = 0.0f;  // aggregate-only mode: this segment's sum of Delta
   const int64_t rec_state = static_cast<int64_t>(rec) * N * 64;
   bool published = false;
   // Look-back segment: skip the aggregate pass when the predecessor has
@@ -571,16 +576,30 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     pred_final = __builtin_amdgcn_readfirstlane(s_pred_final) != 0;
   }
   const bool run_aggregate = seg != 0 && sh.lookback && !pred_final;
+  // AGG instances compute a sequence's carry record (its sum of Delta and
+  // end state) and no outputs: every workgroup runs exactly one aggregate
+  // pass, a look-back segment's own (from zero, before its carry is known)
+  // or, for the others, the whole work from the carry-in.  Their `out`
+  // argument carries the [batch][dim] float32 sums of Delta.
+  float* const sum_delta_out = AGG ? reinterpret_cast<float*>(out) : nullptr;
 
   if (!scan_wave) {
     using kOn = std::integral_constant<bool, true>;
     using kOff = std::integral_constant<bool, false>;
-    if (sh.softplus != 0 && sh.has_z) {
-      if (run_aggregate) helper_loop(kOff{}, kOn{});
-      helper_loop(kOn{}, kOn{});
+    if constexpr (AGG) {
+      if (sh.softplus != 0) {
+        helper_loop(kOff{}, kOn{});
+      } else {
+        helper_loop(kOff{}, kOff{});
+      }
     } else {
-      if (run_aggregate) helper_loop(kOff{}, kOff{});
-      helper_loop(kOn{}, kOff{});
+      if (sh.softplus != 0 && sh.has_z) {
+        if (run_aggregate) helper_loop(kOff{}, kOn{});
+        helper_loop(kOn{}, kOn{});
+      } else {
+        if (run_aggregate) helper_loop(kOff{}, kOff{});
+        helper_loop(kOn{}, kOff{});
+      }
     }
     return;
   }
@@ -606,6 +625,8 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
   } else {
     float hA[G];
     float sum_delta;
+#pragma unroll
+    for (int g = 0; g < G; ++g) hA[g] = 0.0f;
     scan_aggregate(hA, sum_delta);
 #pragma unroll
     for (int g = 0; g < G; ++g) sc.agg_b[rec_state + (gidx + g) * 64 + lane] = hA[g];
@@ -691,10 +712,33 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
             fmaf(exp2_hw(A2[g] * sum_delta), h[g], hA[g]);
       if (lane == 0) store_release(&sc.status[rec * NG + w], kInclusive);
     }
+    if constexpr (AGG) {
+      // the segment's end state is the result
+#pragma unroll
+      for (int g = 0; g < G; ++g) h[g] = fmaf(exp2_hw(A2[g] * sum_delta), h[g], hA[g]);
+      own_sum_delta = sum_delta;
+    }
     published = true;
   }
 
-  scan_output(h);
+  if constexpr (AGG) {
+    if (!run_aggregate) {
+      // one pass from the carry-in found above
+      float hA[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) hA[g] = h[g];
+      scan_aggregate(hA, own_sum_delta);
+#pragma unroll
+      for (int g = 0; g < G; ++g) h[g] = hA[g];
+      // every record of a split chain carries its segment's sum of Delta (a
+      // look-back segment stored it with its aggregate), released with the
+      // record's status, so that the chain's last segment can add them up
+      if (seg + 1 < nseg_c)
+        sc.agg_s[(static_cast<int64_t>(rec) * NG + w) * 64 + lane] = own_sum_delta;
+    }
+  } else {
+    scan_output(h);
+  }
 
   if (!published && seg + 1 < nseg_c) {
 #pragma unroll
@@ -705,6 +749,13 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g)
       last_state[(static_cast<int64_t>(b) * dim + d) * N + gidx + g] = h[g];
+  }
+  if (AGG && seg + 1 == nseg_c && w == 0 && dvalid) {
+    // the chain's sum of Delta, segment by segment in sequence order (every
+    // earlier record was released before this segment acquired its carry)
+    float total = 0.0f;
+    for (int s = 0; s < seg; ++s) total += sc.agg_s[(static_cast<int64_t>(rec0 + s) * NG) * 64 + lane];
+    sum_delta_out[static_cast<int64_t>(b) * dim + d] = total + own_sum_delta;
   }
 }
 
@@ -728,10 +779,17 @@ static hipError_t launch_typed(const FwdPtrs& p, const FwdScratch& s, const FwdS
   constexpr int NP = helper_waves(NG, G);
   const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * (NG + NP));
 #define SSM_LAUNCH_FWD(Z, V)                                                                 \
-  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, NP, TC, Z, V>), grid, block, 0, stream,       \
+  if (sh.agg_only) {                                                                         \
+    SSM_LAUNCH_FWD_K(Z, V, true);                                                            \
+  } else {                                                                                   \
+    SSM_LAUNCH_FWD_K(Z, V, false);                                                           \
+  }
+#define SSM_LAUNCH_FWD_K(Z, V, AG)                                                           \
+  hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, NP, TC, Z, V, AG>), grid, block, 0, stream,   \
                      static_cast<const T*>(p.u), static_cast<const T*>(p.delta), p.A,         \
                      static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,             \
-                     static_cast<const T*>(p.z), p.dt_bias, p.h0, static_cast<T*>(p.out),     \
+                     static_cast<const T*>(p.z), p.dt_bias, p.h0,                             \
+                     static_cast<T*>(AG ? static_cast<void*>(p.sum_delta) : p.out),           \
                      p.last_state, s, sh)
   if (sh.zoh) {
     if (sh.vec_io) {
@@ -747,6 +805,7 @@ static hipError_t launch_typed(const FwdPtrs& p, const FwdScratch& s, const FwdS
     }
   }
 #undef SSM_LAUNCH_FWD
+#undef SSM_LAUNCH_FWD_K
   return hipGetLastError();
 }
 

@@ -44,6 +44,7 @@ struct FwdShape {
   int32_t has_bias, has_D, has_z, has_h0, has_last;
   int32_t vec_io;    // activation rows may be moved in aligned vector runs
   int32_t zoh;       // 1: exact zero-order-hold input term, 0: Delta * B
+  int32_t agg_only;  // 1: carry record only (sum of Delta and end state), no outputs
   int64_t n_ckpt;    // ceil(seqlen / kBwdChunk): checkpoints per chain
 };
 
@@ -59,6 +60,7 @@ struct FwdPtrs {
   const float* h0;
   void* out;
   float* last_state;
+  float* sum_delta;  // [batch][dim], written in aggregate-only mode
 };
 
 // Forward workgroup shape: `groups` scan waves (one per state group) plus
@@ -98,6 +100,13 @@ SSM_DECLARE_FWD(fwd_f32)
 SSM_DECLARE_FWD(fwd_bf16)
 #undef SSM_DECLARE_FWD
 
+// Start state of every one of `segments` consecutive sequence segments from
+// their carry records (sum of Delta [S][batch][dim], state from zero
+// [S][batch][dim][n]), folded in order from h0 (nullable = zeros); h_out
+// (nullable) receives the state after the last segment.
+hipError_t launch_carry_combine(const float* sum_delta, const float* agg, const float* A,
+                                const float* h0, float* h_in, float* h_out, int64_t segments,
+                                int64_t batch, int64_t dim, int n, hipStream_t stream);
 // rows_override (1, 2, 4 or 8) fixes the batch rows each workgroup walks
 // (tuning); otherwise one row per workgroup.
 hipError_t launch_state_update(int dtype, int dstate, float* state,

@@ -320,3 +320,44 @@ def test_noalloc_rejects_plans_beyond_its_static_scratch(monkeypatch):
     monkeypatch.setenv("SSM_FORCE_SEGMENT", "16")
     assert _fwd_noalloc(_dims(b=1, L=65536, d=256, n=16)) == -7
     assert "SSM_ESCRATCH" in _lib.status_string(-7)
+
+
+def _agg(dims, *, u=P[0], dt=P[1], A=P[2], B=P[3], bias=None, h0=None, bbar=0, sd=P[4],
+         st=P[5]):
+    lib = _lib.load()
+    return lib.selective_scan_fwd_aggregate(u, dt, A, B, bias, 1, h0, bbar, sd, st,
+                                            ctypes.byref(dims), None)
+
+
+def test_aggregate_entry_point_validation():
+    d = _dims()
+    assert _agg(d, sd=None) == SSM_EINVAL
+    assert _agg(d, st=None) == SSM_EINVAL
+    assert _agg(d, u=None) == SSM_EINVAL
+    assert _agg(d, B=None) == SSM_EINVAL
+    assert _agg(d, bbar=2) == SSM_EINVAL
+    assert _agg(_dims(n=3)) == SSM_EINVAL
+    assert _agg(_dims(dtype=5)) == SSM_EDTYPE
+    assert _agg(d, sd=P[0]) == SSM_EINVAL          # aliases u
+    assert _agg(d, st=P[4]) == SSM_EINVAL          # state aliases sum_delta
+    assert _agg(d, h0=P[5]) == SSM_EINVAL          # h0 aliases state
+    assert _agg(d, sd=ctypes.c_void_p(0x100002)) == SSM_EALIGN
+
+
+def _comb(dims, S=3, *, sd=P[0], agg=P[1], A=P[2], h0=None, h_in=P[3], h_out=None):
+    lib = _lib.load()
+    return lib.selective_scan_carry_combine(sd, agg, A, h0, h_in, h_out, S, ctypes.byref(dims),
+                                            None)
+
+
+def test_carry_combine_validation():
+    d = _dims()
+    assert _comb(d, S=0) == SSM_EINVAL
+    assert _comb(d, h_in=None) == SSM_EINVAL
+    assert _comb(d, sd=None) == SSM_EINVAL
+    assert _comb(d, A=None) == SSM_EINVAL
+    assert _comb(_dims(n=5)) == SSM_EINVAL
+    assert _comb(d, h_in=P[1]) == SSM_EINVAL       # aliases agg
+    assert _comb(d, h_out=P[3]) == SSM_EINVAL      # h_out aliases h_in
+    assert _comb(d, h0=P[4], h_out=P[4]) == SSM_EINVAL
+    assert _comb(d, agg=ctypes.c_void_p(0x100001)) == SSM_EALIGN
