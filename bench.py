@@ -793,6 +793,94 @@ def time_forward(torch, dev, w, steps, warmup, bbar="delta"):
     return ms, n_sets, region
 
 
+def aggregate_valu_slots_per_token_channel(n):
+    """Algorithmic fp32 VALU issue slots per token*channel of the carry
+    record (the recurrence without readout or gate): per state mul(Delta*A),
+    exp (2), mul(Delta*u*B), fma(h) = 5 slots; per channel step softplus
+    (11), Delta*u (1) and the sum of Delta (1)."""
+    return 5 * n + 13
+
+
+def time_pieces(torch, dev, w, pieces, steps, warmup):
+    """The million-token sequence as `pieces` equal pieces, as each device of
+    a sequence-sharded run would see it: the carry record of one piece, the
+    fold of all pieces' records, and one piece's forward from its start
+    state; plus the record of the whole sequence in one call (what one device
+    alone spends on the first pass).  Times in ms (region averages)."""
+    from selective_state_space_38_amd import (check_device_errors, selective_scan_carry_combine,
+                                              selective_scan_fwd, selective_scan_fwd_aggregate)
+    print(f"bench: {w.name} in {pieces} pieces", file=sys.stderr, flush=True)
+    x = synth.make(w)
+    u, dt_, z, Bm, Cm = (_upload(torch, dev, x[n]) for n in ("u", "delta", "z", "B", "C"))
+    A, Dv, bias = (_upload(torch, dev, x[n]) for n in ("A", "D", "dt_bias"))
+    del x
+    Lp = w.seqlen // pieces
+    sl = slice(Lp, 2 * Lp)   # piece 1 (batch 1: a piece along L is a contiguous view)
+    pu, pdt, pz, pB, pC = (t[:, sl] for t in (u, dt_, z, Bm, Cm))
+    sd_all = torch.empty((pieces, w.batch, w.dim), dtype=torch.float32, device=dev)
+    agg_all = torch.empty((pieces, w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+    for k in range(pieces):
+        ks = slice(k * Lp, (k + 1) * Lp)
+        selective_scan_fwd_aggregate(u[:, ks], dt_[:, ks], A, Bm[:, ks], delta_bias=bias,
+                                     sum_delta=sd_all[k], state=agg_all[k])
+    h_in = torch.empty_like(agg_all)
+    h_out = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+    pout = torch.empty_like(pu)
+    sd1 = torch.empty((w.batch, w.dim), dtype=torch.float32, device=dev)
+    st1 = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+    def agg_piece():
+        selective_scan_fwd_aggregate(pu, pdt, A, pB, delta_bias=bias, sum_delta=sd1, state=st1)
+
+    def combine():
+        selective_scan_carry_combine(sd_all, agg_all, A, h_in=h_in, h_out=h_out)
+
+    def fwd_piece():
+        selective_scan_fwd(pu, pdt, A, pB, pC, D=Dv, z=pz, delta_bias=bias, h0=h_in[1],
+                           out=pout)
+
+    def agg_whole():
+        selective_scan_fwd_aggregate(u, dt_, A, Bm, delta_bias=bias, sum_delta=sd1, state=st1)
+
+    res = {name: _time_region_ms(torch, fn, steps, warmup)
+           for name, fn in (("aggregate_piece", agg_piece), ("combine", combine),
+                            ("forward_h0_piece", fwd_piece), ("aggregate_whole", agg_whole))}
+    check_device_errors(dev)
+    del u, dt_, z, Bm, Cm, pout, sd_all, agg_all, h_in
+    torch.cuda.empty_cache()
+    return res, Lp
+
+
+def pieces_entry(w, pieces, res, Lp):
+    slots = aggregate_valu_slots_per_token_channel(w.dstate)
+    tokch = w.batch * w.seqlen * w.dim
+    agg_whole = res["aggregate_whole"]
+    alu = slots * tokch / (agg_whole / 1e3) / 1e12
+    # the record reads u, dt and B and writes the state and the sums of Delta
+    e_in = 2 if w.dtype == "bf16" else 4
+    rec_bytes = (2 * e_in * w.batch * w.seqlen * w.dim + e_in * w.batch * w.seqlen * w.dstate
+                 + 4 * (w.dim * w.dstate + w.dim) + 4 * w.batch * w.dim * (w.dstate + 1))
+    per_dev = res["aggregate_piece"] + res["combine"] + res["forward_h0_piece"]
+    return {
+        "pieces": pieces, "piece_len": Lp,
+        "aggregate_piece_ms": res["aggregate_piece"],
+        "combine_ms": res["combine"],
+        "forward_h0_piece_ms": res["forward_h0_piece"],
+        "per_device_ms_at_pieces_devices": per_dev,
+        "per_device_note": ("record of its piece + fold of all records + its piece's "
+                            "outputs; the all-gather of the records (17 KB each) between "
+                            "the first two is not included"),
+        "aggregate_whole_ms": agg_whole,
+        "aggregate_whole": {
+            "tokens_channels_per_s": tokch / (agg_whole / 1e3),
+            "algorithmic_bytes": rec_bytes,
+            "hbm_frac_of_8TBps": rec_bytes / (agg_whole / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "alu": {"slots_per_token_channel": slots, "achieved": alu, "unit": ALU_UNIT,
+                    "frac_of_nominal": alu / VALU_PEAK_TSLOTS}},
+        "timing": "region averages of back-to-back launches (one HIP event pair each)",
+    }
+
+
 # ------------------------------------------------- counter summaries --
 
 def _counter_rows(directory):
@@ -1123,6 +1211,11 @@ def main():
             configs[name]["plan"] = fwd_plan(ew.batch, ew.seqlen, ew.dim, ew.dstate,
                                              torch.bfloat16 if ew.dtype == "bf16"
                                              else torch.float32)
+        # the million-token sequence in 8 pieces (sequence sharding, one
+        # device's share at a time)
+        pw = synth.WORKLOADS["seq1m"]
+        pres, plen = time_pieces(torch, dev, pw, 8, args.extra_steps, args.warmup)
+        configs["seq1m_pieces"] = pieces_entry(pw, 8, pres, plen)
 
     head = configs[w.name]
     fwd_avg = head["avg_ms"]
