@@ -139,6 +139,9 @@ def parse():
                         "waves per SIMD, the full streaming sweep); one JSON line")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the million-token and 130M-shaped forwards timed beside the step")
+    p.add_argument("--no-pieces", action="store_true",
+                   help="skip the million-token sequence in pieces (its launches share the "
+                        "forward's kernel and grid, so profiling runs leave them out)")
     p.add_argument("--extra-steps", type=int, default=20,
                    help="timed launches of each extra forward workload")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -899,6 +902,12 @@ def _counter_rows(directory):
     return rows
 
 
+def _template_head(kernel_name):
+    """The kernel name up to its template argument list's end."""
+    m = re.match(r"(.*?>)\(", kernel_name)
+    return m.group(1) if m else kernel_name.split("(")[0]
+
+
 def summarize_counters(fetch_dir, write_dir):
     """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
     summed over the device's channels), each scaled by what the same counter
@@ -932,11 +941,16 @@ def summarize_counters(fetch_dir, write_dir):
              "algorithmic bytes | ratio |", "|---|---|---|---|---|---|"]
 
     def entry(name_key, grid, w, label):
-        fv = [v for (n, g), vs in fk.items() if name_key in n and g == grid for v in vs]
-        wv = [v for (n, g), vs in wk.items() if name_key in n and g == grid for v in vs]
+        def hit(n, g):
+            # the forward's own instances (last template flag false), not the
+            # carry-record instances of the same kernel
+            return name_key in n and g == grid and (
+                "scan_fwd_kernel" not in n or _template_head(n).endswith("false>"))
+        fv = [v for (n, g), vs in fk.items() if hit(n, g) for v in vs]
+        wv = [v for (n, g), vs in wk.items() if hit(n, g) for v in vs]
         if not fv or not wv:
             return None
-        kname = next(n for (n, g) in fk if name_key in n and g == grid)
+        kname = next(n for (n, g) in fk if hit(n, g))
         fb = float(np.mean(fv)) * 1024.0 * f_scale
         wb = float(np.mean(wv)) * 1024.0 * w_scale
         alg = synth.algorithmic_bytes(w)
@@ -1009,7 +1023,9 @@ def summarize_trace(directory):
     print("|---|---|---|---|---|---|---|")
     for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         label = next((n for (ns, gg), n in names.items() if ns in k and gg == g
-                      and "scan_fwd_kernel" in k), "")
+                      and "scan_fwd_kernel" in k and _template_head(k).endswith("false>")), "")
+        if "scan_fwd_kernel" in k and _template_head(k).endswith("true>"):
+            label = "carry record"
         if "state_update_kernel" in k:
             label = "decode"
         m = re.match(r"(.*?>)\(", k)
@@ -1211,6 +1227,7 @@ def main():
             configs[name]["plan"] = fwd_plan(ew.batch, ew.seqlen, ew.dim, ew.dstate,
                                              torch.bfloat16 if ew.dtype == "bf16"
                                              else torch.float32)
+    if not args.no_extra and not args.no_pieces:
         # the million-token sequence in 8 pieces (sequence sharding, one
         # device's share at a time)
         pw = synth.WORKLOADS["seq1m"]
