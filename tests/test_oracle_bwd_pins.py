@@ -120,3 +120,70 @@ def test_final_state_gradient_alone():
     mask[1, 2] = False
     assert np.all(g["dA"][mask] == 0.0)
     assert np.all(g["dh0"][0][mask] == 0.0)
+
+
+# ---------------------------------------------------- exact zero-order hold --
+
+def _loss_zoh(c, w, softplus=True):
+    out, last = oracle.scan_fwd(**c, delta_softplus=softplus, bbar="zoh")
+    return float(np.sum(out * w["dout"]) + np.sum(last * w["dlast"]))
+
+
+def _fd_zoh(c, w, key, softplus=True, eps=1e-6):
+    x = c[key]
+    g = np.empty_like(x)
+    for i in np.ndindex(x.shape):
+        cp = dict(c)
+        xp = x.copy()
+        xp[i] += eps
+        cp[key] = xp
+        lp = _loss_zoh(cp, w, softplus)
+        xp[i] -= 2 * eps
+        lm = _loss_zoh(cp, w, softplus)
+        g[i] = (lp - lm) / (2 * eps)
+    return g
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+def test_zoh_gradients_match_finite_differences(softplus):
+    """The ZOH input (reading guide, Method): every gradient against central
+    differences of the forward oracle in its ZOH mode."""
+    c, w = _case(210, gate=True, h0=True)
+    if not softplus:
+        c["delta"] = np.abs(c["delta"]) * 0.3
+        c["dt_bias"] = np.full(3, 0.05)
+    g = oracle.scan_bwd(**c, delta_softplus=softplus, bbar="zoh", **w)
+    for key, gk in GRADS.items():
+        fd = _fd_zoh(c, w, key, softplus)
+        np.testing.assert_allclose(g[gk], fd, rtol=1e-6, atol=1e-7 * np.max(np.abs(fd)),
+                                   err_msg=key)
+
+
+def test_zoh_gradients_near_zero_A():
+    """A at 0 and within 1e-4 of it, where (exp(Delta A) - 1)/A and its
+    derivative in A take their series forms."""
+    c, w = _case(211, gate=False, h0=True)
+    c["A"][0, 0] = 0.0
+    c["A"][1, 1] = -1e-7
+    c["A"][2, 2] = -3e-5
+    c["A"][0, 3] = 2e-6
+    g = oracle.scan_bwd(**c, bbar="zoh", **w)
+    for key in ("A", "delta", "u", "B"):
+        fd = _fd_zoh(c, w, key)
+        np.testing.assert_allclose(g[GRADS[key]], fd, rtol=1e-6,
+                                   atol=1e-7 * np.max(np.abs(fd)), err_msg=key)
+
+
+def test_zoh_gated_rnn_input_gradient():
+    """N = 1, A = -1, B = C = 1: the ZOH step is h_t = (1 - g_t) h_{t-1} + g_t x_t
+    with g_t = sigmoid(s_t) (reading guide, S6's gated-RNN special case), so
+    the final state's gradient in x_t is g_t prod_{r>t} (1 - g_r)."""
+    r = np.random.default_rng(212)
+    L = 6
+    s = r.standard_normal((1, L, 1))
+    x = r.standard_normal((1, L, 1))
+    g = oracle.scan_bwd(x, s, -np.ones((1, 1)), np.ones((1, L, 1)), np.ones((1, L, 1)),
+                        dout=np.zeros((1, L, 1)), dlast=np.ones((1, 1, 1)), bbar="zoh")
+    gate = 1.0 / (1.0 + np.exp(-s[0, :, 0]))
+    want = np.array([gate[t] * np.prod(1.0 - gate[t + 1:]) for t in range(L)])
+    np.testing.assert_allclose(g["du"][0, :, 0], want, rtol=1e-13)
