@@ -396,6 +396,35 @@ int selective_scan_bwd_ckpt(const void* u, const void* delta, const float* A,
                             float* dD, void* dz, float* ddt_bias, float* dh0,
                             const ssm_dims* dims, void* stream);
 
+/*
+ * The backward and the training forward for either input discretisation
+ * `bbar` (an ssm_bbar; another value returns SSM_EINVAL).  With
+ * SSM_BBAR_DELTA they are selective_scan_bwd / selective_scan_bwd_ckpt and
+ * selective_scan_fwd_train exactly.  With SSM_BBAR_ZOH the forward is
+ * selective_scan_fwd_ex's exact zero-order hold, h_t = Abar h_{t-1} + coef u B
+ * with coef = (exp(Delta A) - 1)/A (reading guide, Method), and the backward
+ * uses d coef/d Delta = exp(Delta A) and d coef/d A = (Delta exp(Delta A) -
+ * coef)/A (evaluated by a series where |Delta A| < 1/4, limit Delta^2/2 at
+ * A = 0).  selective_scan_bwd_ex takes ckpt NULL (it then runs the training
+ * forward itself, as selective_scan_bwd) or the buffer of a
+ * selective_scan_fwd_train_ex call with the same inputs and the same bbar.
+ */
+int selective_scan_fwd_train_ex(const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D,
+                                const void* z, const float* dt_bias, int softplus,
+                                const float* h0, int bbar, void* out,
+                                float* last_state, float* ckpt,
+                                const ssm_dims* dims, void* stream);
+
+int selective_scan_bwd_ex(const void* u, const void* delta, const float* A,
+                          const void* B, const void* C, const float* D,
+                          const void* z, const float* dt_bias, int softplus,
+                          const float* h0, int bbar, const void* dout,
+                          const float* dlast, const float* ckpt, void* du,
+                          void* ddelta, float* dA, void* dB, void* dC,
+                          float* dD, void* dz, float* ddt_bias, float* dh0,
+                          const ssm_dims* dims, void* stream);
+
 /* Bytes of the ckpt buffer for dims (a negative ssm_status if dims are invalid). */
 int64_t ssm_ckpt_bytes(const ssm_dims* dims);
 

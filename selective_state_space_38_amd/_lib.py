@@ -32,6 +32,8 @@ EXPORTED = (
     "selective_scan_bwd",
     "selective_scan_fwd_train",
     "selective_scan_bwd_ckpt",
+    "selective_scan_fwd_train_ex",
+    "selective_scan_bwd_ex",
     "ssm_ckpt_bytes",
     "selective_state_update",
     "selective_state_update_ex",
@@ -153,6 +155,13 @@ def load():
                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                             dims_p, vp]
     lib.selective_scan_bwd_ckpt.restype = ctypes.c_int
+    lib.selective_scan_fwd_train_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                                vp, ctypes.c_int, vp, vp, vp, dims_p, vp]
+    lib.selective_scan_fwd_train_ex.restype = ctypes.c_int
+    lib.selective_scan_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                          ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, dims_p, vp]
+    lib.selective_scan_bwd_ex.restype = ctypes.c_int
     lib.ssm_ckpt_bytes.argtypes = [dims_p]
     lib.ssm_ckpt_bytes.restype = ctypes.c_int64
     lib.selective_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,

@@ -81,14 +81,12 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return_last_state, the float32 final state [batch, dim, dstate].
     bbar: "delta" (Bbar = Delta*B) or "zoh" (exact zero-order hold,
     (exp(Delta A) - 1)/A * B).  ckpt: a buffer from ckpt_buffer() to keep the
-    backward's checkpoints (training mode; Delta*B only).  no_alloc: use the
+    backward's checkpoints (training mode; pass the same bbar to the backward).  no_alloc: use the
     entry point that allocates nothing (selective_scan_fwd_noalloc: its carry
     scratch is a static per-device array, so overlapping calls on one GPU
     race; Delta*B only, no checkpoints).
     """
     code = _bbar_code(bbar)
-    if ckpt is not None and code != _lib.SSM_BBAR_DELTA:
-        raise ValueError("checkpoints are kept for the Delta*B input only")
     if no_alloc and (ckpt is not None or code != _lib.SSM_BBAR_DELTA):
         raise ValueError("no_alloc covers the Delta*B forward without checkpoints only")
     if u.dtype not in _DTYPES:
@@ -120,7 +118,12 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         if ckpt.numel() * 4 < lib.ssm_ckpt_bytes(ctypes.byref(dims)):
             raise ValueError("ckpt is too small (use ckpt_buffer)")
     with torch.cuda.device(dev):
-        if ckpt is not None:
+        if ckpt is not None and code != _lib.SSM_BBAR_DELTA:
+            rc = lib.selective_scan_fwd_train_ex(
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), code, _ptr(out),
+                _ptr(last_state), _ptr(ckpt), ctypes.byref(dims), _stream(dev))
+        elif ckpt is not None:
             rc = lib.selective_scan_fwd_train(
                 _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                 _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(out),
@@ -209,8 +212,9 @@ def selective_scan_carry_combine(sum_delta, agg, A, h0=None, h_in=None, h_out=No
 
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
-                       delta_softplus=True, h0=None, dlast=None, ckpt=None):
-    """Backward of selective_scan_fwd (Delta*B input) on the GPU.
+                       delta_softplus=True, h0=None, dlast=None, ckpt=None, bbar="delta"):
+    """Backward of selective_scan_fwd on the GPU (either input discretisation:
+    bbar "delta" or "zoh", as the forward's).
 
     Inputs as in the forward, plus dout [batch, L, dim] (activation dtype),
     the gradient of the output, and dlast [batch, dim, dstate] float32
@@ -218,9 +222,10 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
     du, ddelta (of the raw dt), dz (if z is given) in the activation dtype;
     dB, dC [batch, L, dstate] in the activation dtype; dA [dim, dstate] and,
     for given D / delta_bias / h0, dD, ddt_bias, dh0 in float32.  ckpt: the
-    buffer a training-mode selective_scan_fwd filled on the same inputs (the
-    backward then skips its own forward pass).
+    buffer a training-mode selective_scan_fwd filled on the same inputs and
+    the same bbar (the backward then skips its own forward pass).
     """
+    code = _bbar_code(bbar)
     if u.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {u.dtype}")
     bsz, L, dim = u.shape
@@ -262,7 +267,9 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         tail = [_ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
                 _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddt_bias")),
                 _ptr(g.get("dh0")), ctypes.byref(dims), _stream(dev)]
-        if ckpt is not None:
+        if code != _lib.SSM_BBAR_DELTA:
+            rc = lib.selective_scan_bwd_ex(*head[:10], code, *head[10:], _ptr(ckpt), *tail)
+        elif ckpt is not None:
             rc = lib.selective_scan_bwd_ckpt(*head, _ptr(ckpt), *tail)
         else:
             rc = lib.selective_scan_bwd(*head, *tail)

@@ -371,9 +371,10 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
              const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
              const void* dout, const float* dlast, const float* ckpt_in, void* du, void* ddelta,
              float* dA, void* dB, void* dC, float* dD, void* dz, float* ddt_bias, float* dh0,
-             const ssm_dims* dims, void* stream) {
+             const ssm_dims* dims, void* stream, int bbar = SSM_BBAR_DELTA) {
   int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
+  if (bbar != SSM_BBAR_DELTA && bbar != SSM_BBAR_ZOH) return SSM_EINVAL;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
     return SSM_EINVAL;
   if (dz && !z) return SSM_EINVAL;  // no gate, no gate gradient
@@ -457,7 +458,7 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   const float* ckpt = ckpt_in ? ckpt_in : reinterpret_cast<const float*>(scratch);
   rc = SSM_OK;
   if (!ckpt_in) {
-    rc = fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, SSM_BBAR_DELTA, nullptr,
+    rc = fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, bbar, nullptr,
                   nullptr, reinterpret_cast<float*>(scratch), dims, stream, /*no_out=*/true);
   }
   const float* ysave =
@@ -496,6 +497,7 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.has_bias = dt_bias != nullptr;
   sh.has_h0 = h0 != nullptr;
   sh.has_dlast = dlast != nullptr;
+  sh.zoh = bbar == SSM_BBAR_ZOH ? 1 : 0;
   {
     // the helpers' runs of ept = kBwdChunk / 4 channels may move as one
     // vector when every run is whole and aligned (the saved readouts are
@@ -720,18 +722,27 @@ int selective_scan_fwd_ex(const void* u, const void* delta, const float* A, cons
                   nullptr, dims, stream);
 }
 
-int selective_scan_fwd_train(const void* u, const void* delta, const float* A, const void* B,
-                             const void* C, const float* D, const void* z,
-                             const float* dt_bias, int softplus, const float* h0, void* out,
-                             float* last_state, float* ckpt, const ssm_dims* dims,
-                             void* stream) {
+int selective_scan_fwd_train_ex(const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* dt_bias, int softplus, const float* h0, int bbar,
+                                void* out, float* last_state, float* ckpt,
+                                const ssm_dims* dims, void* stream) {
   if (!ckpt) return SSM_EINVAL;
   if (!aligned(ckpt, 4)) return SSM_EALIGN;
   const void* others[] = {u, delta, A, B, C, D, z, dt_bias, h0, out, last_state};
   for (const void* q : others)
     if (q && q == ckpt) return SSM_EINVAL;
-  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, SSM_BBAR_DELTA, out,
-                  last_state, ckpt, dims, stream);
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, bbar, out, last_state, ckpt,
+                  dims, stream);
+}
+
+int selective_scan_fwd_train(const void* u, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z,
+                             const float* dt_bias, int softplus, const float* h0, void* out,
+                             float* last_state, float* ckpt, const ssm_dims* dims,
+                             void* stream) {
+  return selective_scan_fwd_train_ex(u, delta, A, B, C, D, z, dt_bias, softplus, h0,
+                                     SSM_BBAR_DELTA, out, last_state, ckpt, dims, stream);
 }
 
 int selective_scan_fwd_aggregate(const void* u, const void* delta, const float* A,
@@ -810,6 +821,16 @@ int selective_scan_bwd_ckpt(const void* u, const void* delta, const float* A, co
   if (!ckpt) return SSM_EINVAL;
   return bwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, dout, dlast, ckpt, du, ddelta,
                   dA, dB, dC, dD, dz, ddt_bias, dh0, dims, stream);
+}
+
+int selective_scan_bwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                          const void* C, const float* D, const void* z, const float* dt_bias,
+                          int softplus, const float* h0, int bbar, const void* dout,
+                          const float* dlast, const float* ckpt, void* du, void* ddelta,
+                          float* dA, void* dB, void* dC, float* dD, void* dz, float* ddt_bias,
+                          float* dh0, const ssm_dims* dims, void* stream) {
+  return bwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, dout, dlast, ckpt, du, ddelta,
+                  dA, dB, dC, dD, dz, ddt_bias, dh0, dims, stream, bbar);
 }
 
 int causal_conv1d_fwd(const void* x, const float* weight, const float* bias,

@@ -53,10 +53,13 @@ enum : int { kBwdEmpty = 0, kBwdAggregate = 1, kBwdInclusive = 2 };
 
 // FAST: softplus on and a gate (the layer's usual configuration), compiled as
 // its own kernel so the helpers test neither flag per element.
-template <typename T, int NG, int G, int NP, int TC, bool VEC, bool FAST>
+template <typename T, int NG, int G, int NP, int TC, bool VEC, bool FAST, bool ZOH>
 // Up to four state groups, two workgroups must share a CU (whole chains plus
-// the split chains' segments): that caps the registers at 128.
-__global__ __launch_bounds__(64 * (NG + NP)) __attribute__((amdgpu_waves_per_eu(NG <= 4 ? 4 : 1)))
+// the split chains' segments): that caps the registers at 128.  ZOH: the
+// exact zero-order-hold input term, whose coefficient and its derivative
+// need more registers than that cap (it spilled): its instances are allowed
+// 256, one workgroup per CU.
+__global__ __launch_bounds__(64 * (NG + NP)) __attribute__((amdgpu_waves_per_eu(ZOH ? 2 : (NG <= 4 ? 4 : 1))))
 void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
   constexpr int N = NG * G;
   constexpr int PT = 64 * NP;                  // helper threads
@@ -72,7 +75,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
 
   // one chunk's staged inputs
   struct Tile {
-    float2 dd[TC][64];         // Delta, Delta*u: one 8-byte read per step
+    float2 dd[TC][64];         // Delta, Delta*u (u with ZOH): one 8-byte read per step
     float dy[TC][64];
     float B[TC][N];
     float C[TC][N];
@@ -81,8 +84,9 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
   // the G-state groups in a rotated order (swz below) so that the 16 quads
   // of a wave write their G floats to different banks
   struct Red {
-    float p1[NG][TC][64];      // sum over the group's states of lambda B
+    float p1[NG][TC][64];      // sum over the group's states of lambda B (ZOH: lambda coef B)
     float p2[NG][TC][64];      // sum over the group's states of lambda Abar h_{t-1} A
+                               // (ZOH: lambda Abar (A h_{t-1} + u B))
     float rB[TC][NQ][N];       // quad sums of lambda Delta u
     float rC[TC][NQ][N];       // quad sums of dy h
   };
@@ -310,7 +314,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         v.dl[e] = ok ? dl : 0.0f;
         v.sig[e] = sg_s;
         v.dy[e] = ok ? dyv : 0.0f;
-        tl.dd[tr][tc + e] = make_float2(v.dl[e], ok ? dl * uv : 0.0f);
+        tl.dd[tr][tc + e] = make_float2(v.dl[e], ok ? (ZOH ? uv : dl * uv) : 0.0f);
         tl.dy[tr][tc + e] = v.dy[e];
         if constexpr (OUT) dD_acc[e] = fmaf(v.dy[e], uv, dD_acc[e]);
       }
@@ -364,8 +368,14 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
           S1 += rd.p1[q][tr][tc + e];
           S2 += rd.p2[q][tr][tc + e];
         }
-        duv[e] = fmaf(v.dl[e], S1, rD[e] * v.dy[e]);
-        ddv[e] = fmaf(v.u[e], S1, S2) * v.sig[e];
+        if constexpr (ZOH) {
+          // du = sum_n lambda coef B + D dy; the u B part of dDelta is in S2
+          duv[e] = fmaf(rD[e], v.dy[e], S1);
+          ddv[e] = S2 * v.sig[e];
+        } else {
+          duv[e] = fmaf(v.dl[e], S1, rD[e] * v.dy[e]);
+          ddv[e] = fmaf(v.u[e], S1, S2) * v.sig[e];
+        }
         dbias_acc[e] += ok ? ddv[e] : 0.0f;
       }
       if (ALLOK || (tr < n && run_valid)) {
@@ -445,11 +455,12 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
   // =========================================================================
   // Scan waves
   // =========================================================================
-  float Af[G], A2[G];
+  float Af[G], A2[G], iA[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     Af[g] = scan_wave ? p.A[dc * N + gidx + g] : 0.0f;
     A2[g] = Af[g] * kLog2e;
+    iA[g] = (ZOH && scan_wave) ? 1.0f / Af[g] : 0.0f;
   }
   const float* const ckpt = p.ckpt + (static_cast<int64_t>(chain) * sh.nchunks) * N * 64;
   float lamn[G], dA_acc[G];   // lamn = Abar_{t+1} lambda_{t+1}
@@ -505,8 +516,13 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         const float dl = dd.x, du = dd.y;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float a = exp2_hw(dl * A2[g]);
-          h[g] = fmaf(a, h[g], du * tl.B[t][gidx + g]);
+          const float x2 = dl * A2[g];
+          const float a = exp2_hw(x2);
+          if constexpr (ZOH) {
+            h[g] = fmaf(a, h[g], zoh_coef(x2, a, dl, iA[g]) * (du * tl.B[t][gidx + g]));
+          } else {
+            h[g] = fmaf(a, h[g], du * tl.B[t][gidx + g]);
+          }
           as[t][g] = a;
           hs[t][g] = h[g];
         }
@@ -545,13 +561,29 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
         for (int g = 0; g < G; ++g) {
           const float lam = fmaf(dyt, qC[q][g], lamn[g]);
           pC[g] = dyt * hs[t][g];
-          pB[g] = lam * du;
-          s1 = fmaf(lam, qB[q][g], s1);
           const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][g] : hstart[g];
-          lamn[g] = as[t][g] * lam;               // Abar_t lambda_t, carried to step t-1
-          const float lq = lamn[g] * hp;          // lambda_t Abar_t h_{t-1}
-          s2 = fmaf(lq, Af[g], s2);
-          dA_acc[g] = fmaf(lq, dl, dA_acc[g]);
+          if constexpr (ZOH) {
+            // h_t = Abar h_{t-1} + coef u B (du holds u): d coef/d Delta = Abar,
+            // d coef/d A = Delta^2 psi(Delta A)
+            const float x2 = dl * A2[g];
+            const float a = as[t][g];
+            const float cf = zoh_coef(x2, a, dl, iA[g]);
+            const float ub = du * qB[q][g];
+            const float lc = lam * cf;
+            pB[g] = lc * du;
+            s1 = fmaf(lc, qB[q][g], s1);
+            lamn[g] = a * lam;                    // Abar_t lambda_t, carried to step t-1
+            s2 = fmaf(lamn[g], fmaf(Af[g], hp, ub), s2);
+            dA_acc[g] = fmaf(lamn[g] * hp, dl, dA_acc[g]);
+            dA_acc[g] = fmaf(lam * ub, zoh_coef_dA(x2, a, dl, cf, iA[g]), dA_acc[g]);
+          } else {
+            pB[g] = lam * du;
+            s1 = fmaf(lam, qB[q][g], s1);
+            lamn[g] = as[t][g] * lam;             // Abar_t lambda_t, carried to step t-1
+            const float lq = lamn[g] * hp;        // lambda_t Abar_t h_{t-1}
+            s2 = fmaf(lq, Af[g], s2);
+            dA_acc[g] = fmaf(lq, dl, dA_acc[g]);
+          }
         }
         rd.p1[w][t][lane] = s1;
         rd.p2[w][t][lane] = s2;
@@ -814,8 +846,14 @@ static hipError_t launch_bwd_typed(const BwdPtrs& p, const BwdShape& sh, hipStre
   const int64_t workgroups = sh.n_full + static_cast<int64_t>(sh.chains - sh.n_full) * sh.n_seg;
   const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * (NG + NP));
   const bool fast = sh.softplus != 0 && sh.has_z != 0;
-#define SSM_LAUNCH_BWD(V, F) \
-  hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, NP, TC, V, F>), grid, block, 0, st, p, sh)
+#define SSM_LAUNCH_BWD(V, F)                                                                  \
+  if (sh.zoh) {                                                                               \
+    hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, NP, TC, V, F, true>), grid, block, 0, st, p,  \
+                       sh);                                                                   \
+  } else {                                                                                    \
+    hipLaunchKernelGGL((scan_bwd_kernel<T, NG, G, NP, TC, V, F, false>), grid, block, 0, st, p, \
+                       sh);                                                                   \
+  }
   if (sh.vec_io) {
     if (fast) {
       SSM_LAUNCH_BWD(true, true);

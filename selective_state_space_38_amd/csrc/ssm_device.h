@@ -91,6 +91,27 @@ __device__ __forceinline__ float zoh_coef(float x2, float a, float delta, float 
   return fabsf(x2) < 0.36067376f ? series : diff;
 }
 
+// Derivative in A of the zero-order-hold coefficient: d/dA (exp(Delta A) -
+// 1)/A = (Delta a - coef)/A = Delta^2 psi(x), psi(x) = (x e^x - (e^x - 1))/x^2
+// = sum_k (k+1) x^k / (k+2)!, x = Delta A.  |x| < 1/4 (where the difference
+// cancels) uses the series up to x^5 (truncation below 1e-7 relative), A = 0
+// included (limit Delta^2 / 2); elsewhere the difference form, which loses
+// about three bits to the cancellation at |x| = 1/4.  Arguments as
+// zoh_coef, plus coef, its value.
+__device__ __forceinline__ float zoh_coef_dA(float x2, float a, float delta, float coef,
+                                             float inv_a) {
+  // coefficients (k+1) ln(2)^k / (k+2)! of the series in x2
+  float p = 1.9047940e-4f;
+  p = fmaf(p, x2, 1.6030215e-3f);
+  p = fmaf(p, x2, 1.1100822e-2f);
+  p = fmaf(p, x2, 6.0056627e-2f);
+  p = fmaf(p, x2, 2.3104906e-1f);
+  p = fmaf(p, x2, 0.5f);
+  const float series = (delta * delta) * p;
+  const float diff = fmaf(delta, a, -coef) * inv_a;
+  return fabsf(x2) < 0.36067376f ? series : diff;
+}
+
 // y * SiLU(z) = y * z / (1 + e^-z)
 __device__ __forceinline__ float silu_gate(float y, float z) {
   return y * (z * rcp_hw(1.0f + exp2_hw(-z * kLog2e)));

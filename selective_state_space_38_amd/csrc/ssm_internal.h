@@ -171,6 +171,7 @@ struct BwdShape {
   int32_t softplus;
   int32_t has_D, has_z, has_bias, has_h0, has_dlast;
   int32_t vec_io;    // the helpers' runs (kBwdChunk / 4 channels) may be vector moves
+  int32_t zoh;       // 1: the exact zero-order-hold input term, 0: Delta * B
 };
 
 // Segment lengths of the backward's split chains are multiples of this.
