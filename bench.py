@@ -70,15 +70,21 @@ def valu_slots_per_token_channel(n, bbar="delta"):
     return (16 if bbar == "zoh" else 6) * n + 20
 
 
-def bwd_valu_slots_per_token_channel(n):
+def bwd_valu_slots_per_token_channel(n, bbar="delta"):
     """Algorithmic fp32 VALU issue slots per token*channel of the backward
     with recomputation: per state the recomputed step and readout (mul, exp
     (2), mul, fma, fma = 6), the adjoint (lambda fma, dC and dB products,
     sum lambda B fma, Abar h_{t-1} and its product with lambda, sum with A,
     dA fma, the carried Abar lambda = 9) and the two channel sums of dB and
     dC (2): 17 slots; per channel step softplus and its derivative (14), the
-    gate and its derivative (12), du and dDelta (4): 30 slots."""
-    return 17 * n + 30
+    gate and its derivative (12), du and dDelta (4): 30 slots.  The
+    zero-order-hold input adds per state the coefficient (exp(Delta A) - 1)/A
+    in the recomputed step (9, plus its product: 10) and again in the adjoint
+    (9), its derivative in A (a 5-term series, its scaling, the difference
+    form and the choice: 11) and four products and sums more (u B, lambda
+    coef, lambda u B, the second dA term): 51 slots per state, and one
+    product fewer per channel step (du needs no Delta): 29."""
+    return 51 * n + 29 if bbar == "zoh" else 17 * n + 30
 
 
 def bwd_algorithmic_bytes(w):
@@ -254,7 +260,8 @@ def bwd_bench(args, torch, dev):
     fout = torch.empty_like(u)
 
     def fwd_train():
-        selective_scan_fwd(u, dt, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, out=fout, ckpt=ck)
+        selective_scan_fwd(u, dt, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, out=fout, ckpt=ck,
+                           bbar=args.bbar)
 
     if args.train:
         fwd_train()
@@ -262,7 +269,8 @@ def bwd_bench(args, torch, dev):
         fwd_ms = _time_region_ms(torch, fwd_train, args.steps, args.warmup)
 
     def bwd():
-        return selective_scan_bwd(u, dt, A, Bm, Cm, dout, D=Dv, z=z, delta_bias=bias, ckpt=ck)
+        return selective_scan_bwd(u, dt, A, Bm, Cm, dout, D=Dv, z=z, delta_bias=bias, ckpt=ck,
+                                  bbar=args.bbar)
 
     for _ in range(args.warmup):
         bwd()
@@ -274,7 +282,7 @@ def bwd_bench(args, torch, dev):
     ms = _time_ms(torch, bwd, args.steps, 0)
     check_device_errors(dev)
     tokch = w.batch * w.seqlen * w.dim
-    slots = bwd_valu_slots_per_token_channel(w.dstate) * tokch
+    slots = bwd_valu_slots_per_token_channel(w.dstate, args.bbar) * tokch
     achieved = slots / (avg / 1e3) / 1e12
     nbytes = bwd_algorithmic_bytes(w)
     line = {
@@ -289,13 +297,16 @@ def bwd_bench(args, torch, dev):
         "config": {"workload": (f"{w.name} backward (B={w.batch}, L={w.seqlen}, D={w.dim}, "
                                 f"N={w.dstate}, {w.dtype} activations)"
                                 + (", from the training-mode forward's checkpoints"
-                                   if args.train else ", recomputing its own checkpoints"))},
+                                   if args.train else ", recomputing its own checkpoints")
+                                + (", exact zero-order-hold input" if args.bbar == "zoh"
+                                   else "")),
+                   "bbar": args.bbar},
         "roofline": {
             "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TSLOTS, "unit": ALU_UNIT,
             "frac": achieved / VALU_PEAK_TSLOTS, "traffic": None,
             "kernel": "scan_bwd_kernel (+ reductions)",
-            "ops_per_unit": f"{bwd_valu_slots_per_token_channel(w.dstate)} fp32 VALU issue "
-                            "slots per token*channel",
+            "ops_per_unit": f"{bwd_valu_slots_per_token_channel(w.dstate, args.bbar)} fp32 "
+                            "VALU issue slots per token*channel",
             "units_per_launch": tokch, "avg_launch_ms": avg,
             "median_launch_ms": float(np.median(ms)), "min_launch_ms": float(np.min(ms)),
             "timing": "average over a region of back-to-back launches; median and min per launch",
@@ -316,11 +327,11 @@ def bwd_bench(args, torch, dev):
                         dout=dout_np[:, sl])
 
         t0 = time.perf_counter()
-        oracle.scan_bwd(**sample(4))
+        oracle.scan_bwd(**sample(4), bbar=args.bbar)
         per_step = (time.perf_counter() - t0) / 4
         Lp = int(max(4, min(w.seqlen, args.cpu_seconds / max(per_step, 1e-6))))
         t0 = time.perf_counter()
-        oracle.scan_bwd(**sample(Lp))
+        oracle.scan_bwd(**sample(Lp), bbar=args.bbar)
         tb = time.perf_counter() - t0
         line["cpu_baseline"] = {
             "value": w.batch * Lp * w.dim / tb, "unit": "tokens·channels/s", "cores": 1,
