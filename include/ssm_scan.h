@@ -245,7 +245,8 @@ int selective_state_update_ex(float* state, const void* x, const void* dt,
                               void* out, const ssm_dims* dims, void* stream);
 
 /*
- * Backward of selective_scan_fwd_h0 (Delta*B input): the gradients of
+ * Backward of selective_scan_fwd_h0 (Delta*B input; selective_scan_bwd_ex
+ * below takes either input discretisation): the gradients of
  *   sum(dout * out) + sum(dlast * last_state)
  * with respect to every input, by the chain rule through the recurrence with
  * the adjoint state run backwards in time.  The intermediate states are not

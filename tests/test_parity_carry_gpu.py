@@ -209,3 +209,22 @@ def test_million_token_sequence_in_eight_pieces():
     ref_sd, ref_agg = oracle.segment_aggregate(x["u"][:, :, ds], x["delta"][:, :, ds], x["A"][ds],
                                                x["B"], dt_bias=x["dt_bias"][ds])
     _check_record("f32", sd[bb, dd][None], agg[bb, dd][None], ref_sd, ref_agg)
+
+
+@pytest.mark.parametrize("mode", ["lookback", "chained"])
+def test_aggregate_without_softplus_or_bias(mode):
+    """Delta = dt as given (softplus off, no bias), including steps large
+    enough that exp(Delta A) underflows to 0 and the state resets onto the
+    current input ("Mamba / MambaMini" Q&A on how Delta acts on A)."""
+    from selective_state_space_38_amd import selective_scan_fwd_aggregate
+    x = synth.make("mamba130m", batch=1, seqlen=400, dim=80, dstate=16, a_init="random")
+    x["A"] = np.minimum(x["A"], np.float32(-0.1))
+    dt = np.abs(x["delta"]) * np.float32(0.05)
+    dt[:, 300:303] = np.float32(1e4)
+    ref_sd, ref_st = oracle.segment_aggregate(x["u"], dt, x["A"], x["B"], delta_softplus=False)
+    with env(**MODES[mode]):
+        sd, st = selective_scan_fwd_aggregate(
+            to_dev(x["u"], torch.float32), to_dev(dt, torch.float32),
+            to_dev(x["A"], torch.float32), to_dev(x["B"], torch.float32), delta_softplus=False)
+        torch.cuda.synchronize()
+    _check_record("f32", sd, st, ref_sd, ref_st)
