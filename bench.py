@@ -821,8 +821,9 @@ def time_pieces(torch, dev, w, pieces, steps, warmup):
     fold of all pieces' records, and one piece's forward from its start
     state; plus the record of the whole sequence in one call (what one device
     alone spends on the first pass).  Times in ms (region averages)."""
-    from selective_state_space_38_amd import (check_device_errors, selective_scan_carry_combine,
-                                              selective_scan_fwd, selective_scan_fwd_aggregate)
+    from selective_state_space_38_amd import (check_device_errors, record_buffer,
+                                              selective_scan_carry_combine, selective_scan_fwd,
+                                              selective_scan_fwd_aggregate)
     print(f"bench: {w.name} in {pieces} pieces", file=sys.stderr, flush=True)
     x = synth.make(w)
     u, dt_, z, Bm, Cm = (_upload(torch, dev, x[n]) for n in ("u", "delta", "z", "B", "C"))
@@ -856,11 +857,36 @@ def time_pieces(torch, dev, w, pieces, steps, warmup):
     def agg_whole():
         selective_scan_fwd_aggregate(u, dt_, A, Bm, delta_bias=bias, sum_delta=sd1, state=st1)
 
+    # the same piece with its record call keeping the inner carries, and the
+    # forward from them
+    rec = record_buffer(pu, w.dstate)
+
+    def agg_piece_kept():
+        selective_scan_fwd_aggregate(pu, pdt, A, pB, delta_bias=bias, sum_delta=sd1, state=st1,
+                                     rec=rec)
+
+    def fwd_piece_kept():
+        selective_scan_fwd(pu, pdt, A, pB, pC, D=Dv, z=pz, delta_bias=bias, h0=h_in[1],
+                           out=pout, rec=rec)
+
+    # the whole sequence as two launches: the record keeping every segment's
+    # carry, then every segment's outputs at once
+    rec_w = record_buffer(u, w.dstate)
+    wout = torch.empty_like(u)
+
+    def two_launch_whole():
+        selective_scan_fwd_aggregate(u, dt_, A, Bm, delta_bias=bias, sum_delta=sd1, state=st1,
+                                     rec=rec_w)
+        selective_scan_fwd(u, dt_, A, Bm, Cm, D=Dv, z=z, delta_bias=bias, out=wout, rec=rec_w)
+
     res = {name: _time_region_ms(torch, fn, steps, warmup)
            for name, fn in (("aggregate_piece", agg_piece), ("combine", combine),
-                            ("forward_h0_piece", fwd_piece), ("aggregate_whole", agg_whole))}
+                            ("forward_h0_piece", fwd_piece), ("aggregate_whole", agg_whole),
+                            ("aggregate_piece_kept", agg_piece_kept),
+                            ("forward_piece_from_kept", fwd_piece_kept),
+                            ("two_launch_whole", two_launch_whole))}
     check_device_errors(dev)
-    del u, dt_, z, Bm, Cm, pout, sd_all, agg_all, h_in
+    del u, dt_, z, Bm, Cm, pout, sd_all, agg_all, h_in, rec, rec_w, wout
     torch.cuda.empty_cache()
     return res, Lp
 
@@ -875,6 +901,7 @@ def pieces_entry(w, pieces, res, Lp):
     rec_bytes = (2 * e_in * w.batch * w.seqlen * w.dim + e_in * w.batch * w.seqlen * w.dstate
                  + 4 * (w.dim * w.dstate + w.dim) + 4 * w.batch * w.dim * (w.dstate + 1))
     per_dev = res["aggregate_piece"] + res["combine"] + res["forward_h0_piece"]
+    per_dev_kept = res["aggregate_piece_kept"] + res["combine"] + res["forward_piece_from_kept"]
     return {
         "pieces": pieces, "piece_len": Lp,
         "aggregate_piece_ms": res["aggregate_piece"],
@@ -884,6 +911,14 @@ def pieces_entry(w, pieces, res, Lp):
         "per_device_note": ("record of its piece + fold of all records + its piece's "
                             "outputs; the all-gather of the records (17 KB each) between "
                             "the first two is not included"),
+        "aggregate_piece_kept_ms": res["aggregate_piece_kept"],
+        "forward_piece_from_kept_ms": res["forward_piece_from_kept"],
+        "per_device_ms_kept": per_dev_kept,
+        "kept_note": ("the record call keeps the piece's inner segment carries, the forward "
+                      "starts every inner segment from them (no aggregate pass, no wait)"),
+        "whole_sequence_two_launches_ms": res["two_launch_whole"],
+        "two_launch_note": ("the whole sequence on one GPU as a record launch that keeps "
+                            "every segment's carry, then a forward launch from them"),
         "aggregate_whole_ms": agg_whole,
         "aggregate_whole": {
             "tokens_channels_per_s": tokch / (agg_whole / 1e3),

@@ -195,6 +195,44 @@ int selective_scan_fwd_aggregate(const void* u, const void* delta, const float* 
                                  float* state, const ssm_dims* dims, void* stream);
 
 /*
+ * A piece's carry record that also keeps the carries inside the piece, and
+ * the piece's forward from them.  Long pieces are scanned internally as
+ * concurrent segments; the forward over a piece then repeats the segments'
+ * aggregate passes that the record call already made.  With a record buffer:
+ *   ssm_fwd_record_bytes(dims)       bytes of the buffer for dims (a negative
+ *                                    ssm_status if dims are invalid)
+ *   selective_scan_fwd_aggregate_rec as selective_scan_fwd_aggregate with
+ *                                    h0 = NULL, and writes `rec`: every inner
+ *                                    segment's end state from a zero start and
+ *                                    its sum of Delta
+ *   selective_scan_fwd_from_rec      as selective_scan_fwd_ex (from h0,
+ *                                    nullable = zeros), reading `rec` from a
+ *                                    selective_scan_fwd_aggregate_rec call on
+ *                                    the same u, delta, A, B, dt_bias,
+ *                                    softplus, bbar and dims: each inner
+ *                                    segment starts at exp(A * sum of Delta
+ *                                    before it) * h0 + its kept start state,
+ *                                    so no segment waits for another or runs
+ *                                    an aggregate pass.
+ * rec is a device buffer owned by the caller, 256-byte aligned (SSM_EINVAL
+ * otherwise), not aliasing any other argument; its layout is internal.  The
+ * two calls must see the same launch plan (the same dims).
+ */
+int64_t ssm_fwd_record_bytes(const ssm_dims* dims);
+
+int selective_scan_fwd_aggregate_rec(const void* u, const void* delta, const float* A,
+                                     const void* B, const float* dt_bias, int softplus,
+                                     int bbar, float* sum_delta, float* state,
+                                     void* rec, const ssm_dims* dims, void* stream);
+
+int selective_scan_fwd_from_rec(const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D,
+                                const void* z, const float* dt_bias, int softplus,
+                                const float* h0, int bbar, const void* rec,
+                                void* out, float* last_state,
+                                const ssm_dims* dims, void* stream);
+
+/*
  * Start states of S consecutive sequence segments from their carry records
  * (selective_scan_fwd_aggregate with h0 = NULL on each segment): h_in[0] = h0
  * (zeros when NULL) and h_in[s+1] = exp(A * sum_delta[s]) * h_in[s] + agg[s],

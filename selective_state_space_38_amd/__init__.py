@@ -7,6 +7,7 @@ from .api import (  # noqa: F401
     selective_scan_carry_combine,
     selective_scan_bwd,
     ckpt_buffer,
+    record_buffer,
     selective_state_update,
     causal_conv1d_fwd,
     causal_conv1d_update,

@@ -29,6 +29,9 @@ EXPORTED = (
     "selective_scan_fwd_ex",
     "selective_scan_fwd_aggregate",
     "selective_scan_carry_combine",
+    "ssm_fwd_record_bytes",
+    "selective_scan_fwd_aggregate_rec",
+    "selective_scan_fwd_from_rec",
     "selective_scan_bwd",
     "selective_scan_fwd_train",
     "selective_scan_bwd_ckpt",
@@ -145,6 +148,14 @@ def load():
     lib.selective_scan_carry_combine.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64,
                                                  dims_p, vp]
     lib.selective_scan_carry_combine.restype = ctypes.c_int
+    lib.ssm_fwd_record_bytes.argtypes = [dims_p]
+    lib.ssm_fwd_record_bytes.restype = ctypes.c_int64
+    lib.selective_scan_fwd_aggregate_rec.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int,
+                                                     ctypes.c_int, vp, vp, vp, dims_p, vp]
+    lib.selective_scan_fwd_aggregate_rec.restype = ctypes.c_int
+    lib.selective_scan_fwd_from_rec.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                                vp, ctypes.c_int, vp, vp, vp, dims_p, vp]
+    lib.selective_scan_fwd_from_rec.restype = ctypes.c_int
     lib.selective_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, dims_p, vp]
     lib.selective_scan_bwd.restype = ctypes.c_int

@@ -60,6 +60,13 @@ def _bbar_code(bbar):
     return codes[bbar]
 
 
+def _check_record_buffer(rec, dims, dev):
+    if rec.device != dev or not rec.is_contiguous():
+        raise ValueError("rec must be a contiguous tensor on the same device")
+    if rec.numel() * rec.element_size() < _lib.load().ssm_fwd_record_bytes(ctypes.byref(dims)):
+        raise ValueError("rec is too small (use record_buffer)")
+
+
 def ckpt_buffer(u, dstate):
     """A float32 device buffer for the training pair's checkpoints (the state
     before every 8th step of every block of 64 channels) of activations u."""
@@ -72,7 +79,8 @@ def ckpt_buffer(u, dstate):
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                        delta_softplus=True, return_last_state=False, h0=None,
-                       out=None, last_state=None, bbar="delta", ckpt=None, no_alloc=False):
+                       out=None, last_state=None, bbar="delta", ckpt=None, no_alloc=False,
+                       rec=None):
     """Selective-scan forward on the GPU.
 
     u, delta, z: [batch, L, dim]; B, C: [batch, L, dstate] (float32 or
@@ -84,7 +92,9 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     backward's checkpoints (training mode; pass the same bbar to the backward).  no_alloc: use the
     entry point that allocates nothing (selective_scan_fwd_noalloc: its carry
     scratch is a static per-device array, so overlapping calls on one GPU
-    race; Delta*B only, no checkpoints).
+    race; Delta*B only, no checkpoints).  rec: a record_buffer filled by
+    selective_scan_fwd_aggregate(rec=...) on the same inputs and bbar: every
+    inner segment then starts from its kept carry (selective_scan_fwd_from_rec).
     """
     code = _bbar_code(bbar)
     if no_alloc and (ckpt is not None or code != _lib.SSM_BBAR_DELTA):
@@ -117,8 +127,17 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
             raise ValueError("ckpt must be a contiguous float32 tensor on the same device")
         if ckpt.numel() * 4 < lib.ssm_ckpt_bytes(ctypes.byref(dims)):
             raise ValueError("ckpt is too small (use ckpt_buffer)")
+    if rec is not None:
+        if ckpt is not None or no_alloc:
+            raise ValueError("rec excludes ckpt and no_alloc")
+        _check_record_buffer(rec, dims, dev)
     with torch.cuda.device(dev):
-        if ckpt is not None and code != _lib.SSM_BBAR_DELTA:
+        if rec is not None:
+            rc = lib.selective_scan_fwd_from_rec(
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), code, _ptr(rec),
+                _ptr(out), _ptr(last_state), ctypes.byref(dims), _stream(dev))
+        elif ckpt is not None and code != _lib.SSM_BBAR_DELTA:
             rc = lib.selective_scan_fwd_train_ex(
                 _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                 _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), code, _ptr(out),
@@ -147,13 +166,28 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return (out, last_state) if return_last_state else out
 
 
+def record_buffer(u, dstate):
+    """A device buffer for selective_scan_fwd_aggregate(rec=...) and
+    selective_scan_fwd(rec=...) on activations u (the launch plan's inner
+    segment carries)."""
+    bsz, L, dim = u.shape
+    dims = _lib.SsmDims(bsz, L, dim, dstate, _DTYPES[u.dtype])
+    nbytes = _lib.load().ssm_fwd_record_bytes(ctypes.byref(dims))
+    _raise(nbytes if nbytes < 0 else 0)
+    return torch.empty(nbytes, dtype=torch.uint8, device=u.device)
+
+
 def selective_scan_fwd_aggregate(u, delta, A, B, delta_bias=None, delta_softplus=True,
-                                 h0=None, bbar="delta", sum_delta=None, state=None):
+                                 h0=None, bbar="delta", sum_delta=None, state=None, rec=None):
     """Carry record of a sequence segment on the GPU: (sum of Delta
     [batch, dim], state after the last step [batch, dim, dstate]), both
     float32, from h0 (zeros when None).  Shapes and dtypes as
-    selective_scan_fwd; C, D and z play no part."""
+    selective_scan_fwd; C, D and z play no part.  rec (a record_buffer; h0
+    must be None) also keeps the carries inside the segment for
+    selective_scan_fwd(rec=...)."""
     code = _bbar_code(bbar)
+    if rec is not None and h0 is not None:
+        raise ValueError("a kept record starts from zero: h0 must be None")
     if u.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {u.dtype}")
     bsz, L, dim = u.shape
@@ -174,11 +208,19 @@ def selective_scan_fwd_aggregate(u, delta, A, B, delta_bias=None, delta_softplus
     _check(state, "state", torch.float32, (bsz, dim, dstate), dev)
     dims = _lib.SsmDims(bsz, L, dim, dstate, _DTYPES[act])
     lib = _lib.load()
+    if rec is not None:
+        _check_record_buffer(rec, dims, dev)
     with torch.cuda.device(dev):
-        rc = lib.selective_scan_fwd_aggregate(
-            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(delta_bias),
-            1 if delta_softplus else 0, _ptr(h0), code, _ptr(sum_delta), _ptr(state),
-            ctypes.byref(dims), _stream(dev))
+        if rec is not None:
+            rc = lib.selective_scan_fwd_aggregate_rec(
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(delta_bias),
+                1 if delta_softplus else 0, code, _ptr(sum_delta), _ptr(state), _ptr(rec),
+                ctypes.byref(dims), _stream(dev))
+        else:
+            rc = lib.selective_scan_fwd_aggregate(
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(delta_bias),
+                1 if delta_softplus else 0, _ptr(h0), code, _ptr(sum_delta), _ptr(state),
+                ctypes.byref(dims), _stream(dev))
     _raise(rc)
     return sum_delta, state
 

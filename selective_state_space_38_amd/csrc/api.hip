@@ -192,19 +192,47 @@ int64_t ckpt_state_bytes(const ssm_dims* dims) {
 }
 int64_t ckpt_y_offset(const ssm_dims* dims) { return div_up(ckpt_state_bytes(dims), 256) * 256; }
 
+// The forward's scratch: the ticket and status words, then the split
+// segments' carry records (end state; aggregate from zero and sum of Delta
+// where the plan walks back; the sums also where they are kept for a record
+// or the chain's total), each piece 256-byte aligned.
+struct FwdScratchLayout {
+  int64_t n_int, off_inc, inc_bytes, aggb_bytes, aggs_bytes, total;
+};
+FwdScratchLayout fwd_scratch_layout(const ssm_fwd_plan& plan, int64_t recs, int64_t N,
+                                    bool keep_sums) {
+  auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
+  const bool need_carry = plan.segments > 1;
+  FwdScratchLayout l;
+  l.n_int = 1 + (need_carry ? recs * plan.state_groups : 0);
+  l.off_inc = up256(l.n_int * 4);
+  l.inc_bytes = need_carry ? up256(recs * N * 64 * 4) : 0;
+  l.aggb_bytes = plan.lookback ? up256(recs * N * 64 * 4) : 0;
+  l.aggs_bytes = (plan.lookback || (keep_sums && need_carry))
+                     ? up256(recs * plan.state_groups * 64 * 4)
+                     : 0;
+  l.total = l.off_inc + l.inc_bytes + l.aggb_bytes + l.aggs_bytes;
+  return l;
+}
+
 // out may be NULL only for the backward's own forward pass (no_out), which
 // keeps just the checkpoint buffer.
 int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
              const float* D, const void* z, const float* dt_bias, int softplus, const float* h0,
              int bbar, void* out, float* last_state, float* ckpt, const ssm_dims* dims,
              void* stream, bool no_out = false, bool no_alloc = false,
-             float* sum_delta_out = nullptr) {
+             float* sum_delta_out = nullptr, void* rec = nullptr) {
   int rc = check_dims(dims);
   if (rc != SSM_OK) return rc;
   if (bbar != SSM_BBAR_DELTA && bbar != SSM_BBAR_ZOH) return SSM_EINVAL;
   // aggregate-only mode (the carry record of a segment): no C, readout or outputs
   const bool agg_only = sum_delta_out != nullptr;
   if (agg_only && (!last_state || out || ckpt || C || D || z || no_out)) return SSM_EINVAL;
+  // rec: with agg_only, a buffer that keeps every split segment's carry
+  // (records from a zero start only); without, the forward starts every
+  // segment from those carries
+  const bool from_rec = rec != nullptr && !agg_only;
+  if (rec && (!aligned(rec, 256) || no_alloc || ckpt || (agg_only && h0))) return SSM_EINVAL;
   if (!u || !delta || !A || !B || (!C && !agg_only) || (!out && !no_out && !agg_only) ||
       (no_out && !ckpt))
     return SSM_EINVAL;
@@ -216,6 +244,10 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     if (p && (p == out || p == last_state || p == sum_delta_out)) return SSM_EINVAL;
   if (last_state && last_state == out) return SSM_EINVAL;
   if (sum_delta_out && sum_delta_out == last_state) return SSM_EINVAL;
+  if (rec) {
+    for (const void* p : ptrs)
+      if (p && p == rec) return SSM_EINVAL;
+  }
 
   ssm_fwd_plan plan;
   plan_forward(*dims, &plan);
@@ -229,18 +261,9 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t N = dims->dstate;
   // scratch: ticket + status (ints), then records (floats), 256-byte aligned pieces
-  auto up256 = [](int64_t bytes) { return div_up(bytes, 256) * 256; };
-  const bool need_carry = plan.segments > 1;
-  const int64_t n_int = 1 + (need_carry ? recs * plan.state_groups : 0);
-  const int64_t off_inc = up256(n_int * 4);
-  const int64_t inc_bytes = need_carry ? up256(recs * N * 64 * 4) : 0;
-  const int64_t aggb_bytes = plan.lookback ? up256(recs * N * 64 * 4) : 0;
-  // sums of Delta: read by look-back walks, and in aggregate-only mode by a
-  // chain's last segment (which adds up the chain's total)
-  const int64_t aggs_bytes = (plan.lookback || (agg_only && need_carry))
-                                 ? up256(recs * plan.state_groups * 64 * 4)
-                                 : 0;
-  const int64_t total = off_inc + inc_bytes + aggb_bytes + aggs_bytes;
+  const FwdScratchLayout lay = fwd_scratch_layout(plan, recs, N, agg_only || rec);
+  const int64_t n_int = lay.n_int, off_inc = lay.off_inc, inc_bytes = lay.inc_bytes,
+                aggb_bytes = lay.aggb_bytes, total = lay.total;
 
   // a plan of whole chains only takes no ticket and publishes no carry: no
   // scratch, no clearing launch
@@ -248,6 +271,9 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   char* buf = nullptr;
   if (!need_scratch) {
     // nothing to allocate
+  } else if (rec) {
+    // the caller's record buffer (ssm_fwd_record_bytes): nothing allocated
+    buf = static_cast<char*>(rec);
   } else if (no_alloc) {
     // the static array: nothing is allocated or freed by this call
     if (total > kStaticScratchBytes) return SSM_ESCRATCH;
@@ -292,7 +318,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   sh.has_h0 = h0 != nullptr;
   sh.has_last = last_state != nullptr;
   sh.zoh = bbar == SSM_BBAR_ZOH ? 1 : 0;
-  sh.agg_only = agg_only ? 1 : 0;
+  sh.mode = agg_only ? ssm::kModeRecord : (from_rec ? ssm::kModeFromRecord : ssm::kModeForward);
   sh.n_ckpt = div_up(dims->seqlen, ssm::kBwdChunk);
   {
     // per-thread runs of the chunk tile: chunk / helper waves consecutive channels
@@ -312,7 +338,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
 
   rc = SSM_OK;
   const bool f32 = dims->dtype == SSM_F32;
-  if (need_scratch) {
+  if (need_scratch && !from_rec) {
     const hipError_t ez = f32 ? ssm::fwd_f32::launch_fill_zero(sc.ticket, n_int, st)
                               : ssm::fwd_bf16::launch_fill_zero(sc.ticket, n_int, st);
     if (ez != hipSuccess) rc = SSM_ELAUNCH;
@@ -325,7 +351,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
                                              sh, plan.workgroups, st);
     if (el != hipSuccess) rc = SSM_ELAUNCH;
   }
-  if (need_scratch && !no_alloc && hipFreeAsync(buf, st) != hipSuccess && rc == SSM_OK)
+  if (need_scratch && !no_alloc && !rec && hipFreeAsync(buf, st) != hipSuccess && rc == SSM_OK)
     rc = SSM_ELAUNCH;
   return rc;
 }
@@ -753,6 +779,37 @@ int selective_scan_fwd_aggregate(const void* u, const void* delta, const float* 
   return fwd_impl(u, delta, A, B, nullptr, nullptr, nullptr, dt_bias, softplus, h0, bbar,
                   nullptr, state, nullptr, dims, stream, /*no_out=*/false, /*no_alloc=*/false,
                   sum_delta);
+}
+
+int64_t ssm_fwd_record_bytes(const ssm_dims* dims) {
+  const int rc = check_dims(dims);
+  if (rc != SSM_OK) return rc;
+  ssm_fwd_plan plan;
+  plan_forward(*dims, &plan);
+  const int64_t chains = dims->batch * div_up(dims->dim, 64);
+  const int64_t recs = (chains - plan.whole_chains) * plan.segments;
+  return fwd_scratch_layout(plan, recs, dims->dstate, true).total;
+}
+
+int selective_scan_fwd_aggregate_rec(const void* u, const void* delta, const float* A,
+                                     const void* B, const float* dt_bias, int softplus,
+                                     int bbar, float* sum_delta, float* state, void* rec,
+                                     const ssm_dims* dims, void* stream) {
+  if (!sum_delta || !state || !rec) return SSM_EINVAL;
+  return fwd_impl(u, delta, A, B, nullptr, nullptr, nullptr, dt_bias, softplus, nullptr, bbar,
+                  nullptr, state, nullptr, dims, stream, /*no_out=*/false, /*no_alloc=*/false,
+                  sum_delta, rec);
+}
+
+int selective_scan_fwd_from_rec(const void* u, const void* delta, const float* A, const void* B,
+                                const void* C, const float* D, const void* z,
+                                const float* dt_bias, int softplus, const float* h0, int bbar,
+                                const void* rec, void* out, float* last_state,
+                                const ssm_dims* dims, void* stream) {
+  if (!rec) return SSM_EINVAL;
+  return fwd_impl(u, delta, A, B, C, D, z, dt_bias, softplus, h0, bbar, out, last_state,
+                  nullptr, dims, stream, /*no_out=*/false, /*no_alloc=*/false, nullptr,
+                  const_cast<void*>(rec));
 }
 
 int selective_scan_carry_combine(const float* sum_delta, const float* agg, const float* A,

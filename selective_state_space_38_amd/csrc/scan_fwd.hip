@@ -48,7 +48,10 @@
 // Aggregate-only instances (AGG) stop before the outputs: they return the
 // sequence's end state and its sum of Delta, the carry record with which
 // independently scanned pieces of a sequence are joined ("Mamba / MambaMini"
-// Steps 2-4).  Only u, dt and B are read.
+// Steps 2-4).  Only u, dt and B are read.  Their scratch then holds every
+// split segment's end state (from a zero start) and sum of Delta; FROMREC
+// instances take those and an h0 and run every segment's output pass at
+// once, none waiting and none running an aggregate pass.
 
 #include "ssm_device.h"
 #include "ssm_internal.h"
@@ -97,7 +100,7 @@ __device__ __forceinline__ int wait_status(const int* p, int need, int limit) {
   return v;
 }
 
-template <typename T, int NG, int G, int NP, int TC, bool ZOH, bool VEC, bool AGG>
+template <typename T, int NG, int G, int NP, int TC, bool ZOH, bool VEC, int MODE>
 __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     const T* __restrict__ u, const T* __restrict__ dtp,
     const float* __restrict__ A, const T* __restrict__ Bm,
@@ -125,6 +128,10 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
   __shared__ int s_ticket;
   __shared__ int s_pred_final;
 
+  // MODE: kModeForward, kModeRecord (AGG: the carry record only) or
+  // kModeFromRecord (FROMREC: outputs from the carries a record launch kept)
+  constexpr bool AGG = MODE == kModeRecord;
+  constexpr bool FROMREC = MODE == kModeFromRecord;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave-uniform values go through readfirstlane so the compiler keeps them
@@ -142,7 +149,10 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
   // and one segment.
   const bool whole = static_cast<int>(blockIdx.x) < sh.n_full;
   int ticket = 0;
-  if (!whole) {
+  if constexpr (FROMREC) {
+    // no segment waits for another: the order is the workgroup index's
+    if (!whole) ticket = static_cast<int>(blockIdx.x) - sh.n_full;
+  } else if (!whole) {
     if (tid == 0) s_ticket = atomicAdd(sc.ticket, 1);
     __syncthreads();
     ticket = __builtin_amdgcn_readfirstlane(s_ticket);
@@ -566,7 +576,7 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
   // taken once for the workgroup (the aggregate pass stages tiles with
   // workgroup barriers, so every wave must take the same path).
   bool pred_final = false;
-  if (seg != 0 && sh.lookback) {
+  if (!FROMREC && seg != 0 && sh.lookback) {
     if (tid == 0) {
       int all = 1;
       for (int q = 0; q < NG; ++q) all &= load_relaxed(&sc.status[(rec - 1) * NG + q]) == kInclusive;
@@ -575,7 +585,7 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     lds_barrier();
     pred_final = __builtin_amdgcn_readfirstlane(s_pred_final) != 0;
   }
-  const bool run_aggregate = seg != 0 && sh.lookback && !pred_final;
+  const bool run_aggregate = !FROMREC && seg != 0 && sh.lookback && !pred_final;
   // AGG instances compute a sequence's carry record (its sum of Delta and
   // end state) and no outputs: every workgroup runs exactly one aggregate
   // pass, a look-back segment's own (from zero, before its carry is known)
@@ -604,7 +614,24 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     return;
   }
 
-  if (seg == 0) {
+  if constexpr (FROMREC) {
+    // this segment's start from zero (the end state the record launch kept
+    // for its predecessor) plus h0 carried over the segments before it:
+    // exp(A * their sum of Delta) * h0 (the pair operator, "Mamba /
+    // MambaMini" Step 2)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      h[g] = sh.has_h0 ? h0[(static_cast<int64_t>(b) * dim + dc) * N + gidx + g] : 0.0f;
+    if (seg != 0) {
+      float prefix = 0.0f;
+      for (int s = 0; s < seg; ++s)
+        prefix += sc.agg_s[(static_cast<int64_t>(rec0 + s) * NG + w) * 64 + lane];
+      const int64_t ps = static_cast<int64_t>(rec - 1) * N * 64;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        h[g] = fmaf(exp2_hw(A2[g] * prefix), h[g], sc.inc[ps + (gidx + g) * 64 + lane]);
+    }
+  } else if (seg == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
       h[g] = sh.has_h0 ? h0[(static_cast<int64_t>(b) * dim + dc) * N + gidx + g] : 0.0f;
@@ -740,7 +767,7 @@ __global__ __launch_bounds__(64 * (NG + NP)) void scan_fwd_kernel(
     scan_output(h);
   }
 
-  if (!published && seg + 1 < nseg_c) {
+  if (!FROMREC && !published && seg + 1 < nseg_c) {
 #pragma unroll
     for (int g = 0; g < G; ++g) sc.inc[rec_state + (gidx + g) * 64 + lane] = h[g];
     if (lane == 0) store_release(&sc.status[rec * NG + w], kInclusive);
@@ -779,17 +806,20 @@ static hipError_t launch_typed(const FwdPtrs& p, const FwdScratch& s, const FwdS
   constexpr int NP = helper_waves(NG, G);
   const dim3 grid(static_cast<unsigned>(workgroups)), block(64 * (NG + NP));
 #define SSM_LAUNCH_FWD(Z, V)                                                                 \
-  if (sh.agg_only) {                                                                         \
-    SSM_LAUNCH_FWD_K(Z, V, true);                                                            \
+  if (sh.mode == kModeRecord) {                                                              \
+    SSM_LAUNCH_FWD_K(Z, V, kModeRecord);                                                     \
+  } else if (sh.mode == kModeFromRecord) {                                                   \
+    SSM_LAUNCH_FWD_K(Z, V, kModeFromRecord);                                                 \
   } else {                                                                                   \
-    SSM_LAUNCH_FWD_K(Z, V, false);                                                           \
+    SSM_LAUNCH_FWD_K(Z, V, kModeForward);                                                    \
   }
 #define SSM_LAUNCH_FWD_K(Z, V, AG)                                                           \
   hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, NP, TC, Z, V, AG>), grid, block, 0, stream,   \
                      static_cast<const T*>(p.u), static_cast<const T*>(p.delta), p.A,         \
                      static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,             \
                      static_cast<const T*>(p.z), p.dt_bias, p.h0,                             \
-                     static_cast<T*>(AG ? static_cast<void*>(p.sum_delta) : p.out),           \
+                     static_cast<T*>(AG == kModeRecord ? static_cast<void*>(p.sum_delta)      \
+                                                       : p.out),                              \
                      p.last_state, s, sh)
   if (sh.zoh) {
     if (sh.vec_io) {

@@ -44,10 +44,15 @@ struct FwdShape {
   int32_t has_bias, has_D, has_z, has_h0, has_last;
   int32_t vec_io;    // activation rows may be moved in aligned vector runs
   int32_t zoh;       // 1: exact zero-order-hold input term, 0: Delta * B
-  int32_t agg_only;  // 1: carry record only (sum of Delta and end state), no outputs
+  int32_t mode;      // kModeForward, kModeRecord or kModeFromRecord
   int64_t n_ckpt;    // ceil(seqlen / kBwdChunk): checkpoints per chain
 };
 
+// Forward launch modes: the forward; the carry record only (sum of Delta
+// and end state, no outputs; it also leaves every split segment's carry in
+// its scratch); the outputs from the carries a record launch left (every
+// segment starts at once, none waits, none runs an aggregate pass).
+enum : int { kModeForward = 0, kModeRecord = 1, kModeFromRecord = 2 };
 struct FwdPtrs {
   const void* u;
   const void* delta;

@@ -361,3 +361,28 @@ def test_carry_combine_validation():
     assert _comb(d, h_out=P[3]) == SSM_EINVAL      # h_out aliases h_in
     assert _comb(d, h0=P[4], h_out=P[4]) == SSM_EINVAL
     assert _comb(d, agg=ctypes.c_void_p(0x100001)) == SSM_EALIGN
+
+
+def test_record_entry_points_validation():
+    lib = _lib.load()
+    d = _dims(L=4096, d=256)
+    nb = lib.ssm_fwd_record_bytes(ctypes.byref(d))
+    assert nb >= 256 and nb % 256 == 0
+    assert lib.ssm_fwd_record_bytes(ctypes.byref(_dims(n=3))) == SSM_EINVAL
+    rec = ctypes.c_void_p(0x200000)
+    agg = lib.selective_scan_fwd_aggregate_rec
+    assert agg(P[0], P[1], P[2], P[3], None, 1, 0, P[4], P[5], None, ctypes.byref(d),
+               None) == SSM_EINVAL                                   # no buffer
+    assert agg(P[0], P[1], P[2], P[3], None, 1, 0, P[4], P[5], ctypes.c_void_p(0x200010),
+               ctypes.byref(d), None) == SSM_EINVAL                  # not 256-byte aligned
+    assert agg(P[0], P[1], P[2], P[3], None, 1, 0, P[4], P[5], P[0], ctypes.byref(d),
+               None) == SSM_EINVAL                                   # aliases u
+    assert agg(P[0], P[1], P[2], P[3], None, 1, 5, P[4], P[5], rec, ctypes.byref(d),
+               None) == SSM_EINVAL                                   # bad bbar
+    frm = lib.selective_scan_fwd_from_rec
+    assert frm(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None, 0, None, P[5], None,
+               ctypes.byref(d), None) == SSM_EINVAL                  # no buffer
+    assert frm(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None, 0, P[5], P[5], None,
+               ctypes.byref(d), None) == SSM_EINVAL                  # rec aliases out
+    assert frm(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None, 0, rec, None, None,
+               ctypes.byref(d), None) == SSM_EINVAL                  # no out

@@ -140,35 +140,39 @@ def test_carry_combine_matches_oracle():
         check("h_out", h_out.double().cpu().numpy(), ref_out, scale, 1e-5)
 
 
-def _pieces_forward(x, tag, bounds, h0, bbar="delta"):
+def _pieces_forward(x, tag, bounds, h0, bbar="delta", keep=False):
     """The sequence in pieces: every piece's record from zero, the fold from
-    h0, then every piece's outputs from its start state.  Returns the
-    concatenated outputs and the state after the last piece."""
-    from selective_state_space_38_amd import (selective_scan_carry_combine, selective_scan_fwd,
-                                              selective_scan_fwd_aggregate)
+    h0, then every piece's outputs from its start state (with `keep`, from
+    the carries each piece's record call kept).  Returns the concatenated
+    outputs and the state after the last piece."""
+    from selective_state_space_38_amd import (record_buffer, selective_scan_carry_combine,
+                                              selective_scan_fwd, selective_scan_fwd_aggregate)
     dt = act_dtype(tag)
     A = to_dev(x["A"], torch.float32)
     bias = to_dev(x["dt_bias"], torch.float32)
     Dv = to_dev(x["D"], torch.float32)
     pieces = [slice(lo, hi) for lo, hi in zip(bounds[:-1], bounds[1:])]
     dev = {k: [to_dev(x[k][:, sl], dt) for sl in pieces] for k in ("u", "delta", "z", "B", "C")}
+    bufs = [record_buffer(dev["u"][i], x["A"].shape[1]) if keep else None
+            for i in range(len(pieces))]
     recs = [selective_scan_fwd_aggregate(dev["u"][i], dev["delta"][i], A, dev["B"][i],
-                                         delta_bias=bias, bbar=bbar)
+                                         delta_bias=bias, bbar=bbar, rec=bufs[i])
             for i in range(len(pieces))]
     h_in, h_out = selective_scan_carry_combine(
         torch.stack([r[0] for r in recs]), torch.stack([r[1] for r in recs]), A,
         h0=None if h0 is None else to_dev(h0, torch.float32))
     outs = [selective_scan_fwd(dev["u"][i], dev["delta"][i], A, dev["B"][i], dev["C"][i], D=Dv,
                                z=dev["z"][i], delta_bias=bias, h0=h_in[i].contiguous(),
-                               bbar=bbar)
+                               bbar=bbar, rec=bufs[i])
             for i in range(len(pieces))]
     torch.cuda.synchronize()
     return torch.cat(outs, dim=1), h_out
 
 
+@pytest.mark.parametrize("keep", [False, True])
 @pytest.mark.parametrize("bbar", ["delta", "zoh"])
 @pytest.mark.parametrize("tag", ["f32", "bf16"])
-def test_sequence_in_pieces_equals_whole_forward(tag, bbar):
+def test_sequence_in_pieces_equals_whole_forward(tag, bbar, keep):
     """Four pieces of unequal length (each long enough to be split into
     look-back segments inside its own calls) reproduce the forward over the
     whole 4,100-step sequence from a given h0."""
@@ -177,11 +181,12 @@ def test_sequence_in_pieces_equals_whole_forward(tag, bbar):
     h0 = np.random.default_rng(5).standard_normal((bsz, dim, n)).astype(np.float32)
     bounds = [0, 1000, 2104, 3100, L]
     ref, ref_st = oracle_forward(x, h0=h0, bbar=bbar)
-    out, st = _pieces_forward(x, tag, bounds, h0, bbar=bbar)
+    out, st = _pieces_forward(x, tag, bounds, h0, bbar=bbar, keep=keep)
     check_forward(x, tag, out.float().cpu().numpy(), st.cpu().numpy(), ref, ref_st)
 
 
-def test_million_token_sequence_in_eight_pieces():
+@pytest.mark.parametrize("keep", [False, True])
+def test_million_token_sequence_in_eight_pieces(keep):
     """The million-token sequence as eight pieces of 131,072 steps (one
     device's share each under sequence sharding): every piece's record,
     their fold and every piece's outputs, against the oracle over the whole
@@ -194,7 +199,7 @@ def test_million_token_sequence_in_eight_pieces():
     _log(f"seq1m pieces: oracle on {len(cols)} columns")
     ref, ref_st = oracle_forward(x, cols=cols)
     bounds = [k * (w.seqlen // 8) for k in range(9)]
-    out, st = _pieces_forward(x, "f32", bounds, None)
+    out, st = _pieces_forward(x, "f32", bounds, None, keep=keep)
     check_device_errors()
     bb = torch.tensor([b for b, _ in cols], device="cuda")
     dd = torch.tensor([d for _, d in cols], device="cuda")
@@ -228,3 +233,59 @@ def test_aggregate_without_softplus_or_bias(mode):
             to_dev(x["A"], torch.float32), to_dev(x["B"], torch.float32), delta_softplus=False)
         torch.cuda.synchronize()
     _check_record("f32", sd, st, ref_sd, ref_st)
+
+
+@pytest.mark.parametrize("bbar", ["delta", "zoh"])
+@pytest.mark.parametrize("mode", ["planner", "lookback", "chained", "whole"])
+@pytest.mark.parametrize("tag", ["f32", "bf16"])
+def test_forward_from_kept_record(tag, mode, bbar):
+    """A record call that keeps its inner carries, then the forward from
+    them and an h0: outputs and final state against the oracle's forward
+    from h0, in every carry mode of the launch plan."""
+    from selective_state_space_38_amd import record_buffer, selective_scan_fwd
+    x = synth.make(_wl(tag), batch=2, seqlen=600, dim=96, dstate=16, a_init="random")
+    h0 = np.random.default_rng(9).standard_normal((2, 96, 16)).astype(np.float32)
+    dt = act_dtype(tag)
+    ref, ref_st = oracle_forward(x, h0=h0, bbar=bbar)
+    ref_sd, ref_agg = oracle.segment_aggregate(x["u"], x["delta"], x["A"], x["B"],
+                                               dt_bias=x["dt_bias"], bbar=bbar)
+    with env(**MODES[mode]):
+        u = to_dev(x["u"], dt)
+        rec = record_buffer(u, 16)
+        from selective_state_space_38_amd import selective_scan_fwd_aggregate
+        sd, agg = selective_scan_fwd_aggregate(
+            u, to_dev(x["delta"], dt), to_dev(x["A"], torch.float32), to_dev(x["B"], dt),
+            delta_bias=to_dev(x["dt_bias"], torch.float32), bbar=bbar, rec=rec)
+        out, st = selective_scan_fwd(
+            u, to_dev(x["delta"], dt), to_dev(x["A"], torch.float32), to_dev(x["B"], dt),
+            to_dev(x["C"], dt), D=to_dev(x["D"], torch.float32), z=to_dev(x["z"], dt),
+            delta_bias=to_dev(x["dt_bias"], torch.float32), h0=to_dev(h0, torch.float32),
+            return_last_state=True, bbar=bbar, rec=rec)
+        torch.cuda.synchronize()
+    _check_record(tag, sd, agg, ref_sd, ref_agg)
+    check_forward(x, tag, out.float().cpu().numpy(), st.cpu().numpy(), ref, ref_st)
+
+
+def test_forward_from_kept_record_whole_and_split_chains():
+    """The 2.8B-style plan (256 whole chains, 44 split into five segments)
+    from a kept record: whole chains start from h0, split segments from their
+    kept carries."""
+    from selective_state_space_38_amd import (record_buffer, selective_scan_fwd,
+                                              selective_scan_fwd_aggregate)
+    bsz, L, dim, n = 1, 160, 64 * 300, 16
+    x = synth.make("mamba2p8b", batch=bsz, seqlen=L, dim=dim, dstate=n, a_init="random")
+    h0 = np.random.default_rng(10).standard_normal((bsz, dim, n)).astype(np.float32)
+    ref, ref_st = oracle_forward(x, h0=h0)
+    dt = torch.bfloat16
+    u = to_dev(x["u"], dt)
+    rec = record_buffer(u, n)
+    selective_scan_fwd_aggregate(u, to_dev(x["delta"], dt), to_dev(x["A"], torch.float32),
+                                 to_dev(x["B"], dt), delta_bias=to_dev(x["dt_bias"], torch.float32),
+                                 rec=rec)
+    out, st = selective_scan_fwd(
+        u, to_dev(x["delta"], dt), to_dev(x["A"], torch.float32), to_dev(x["B"], dt),
+        to_dev(x["C"], dt), D=to_dev(x["D"], torch.float32), z=to_dev(x["z"], dt),
+        delta_bias=to_dev(x["dt_bias"], torch.float32), h0=to_dev(h0, torch.float32),
+        return_last_state=True, rec=rec)
+    torch.cuda.synchronize()
+    check_forward(x, "bf16", out.float().cpu().numpy(), st.cpu().numpy(), ref, ref_st)
