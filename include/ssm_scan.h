@@ -29,7 +29,8 @@
  *                          reached) and the fold of consecutive segments'
  *                          records into their start states ("Mamba /
  *                          MambaMini" Steps 2-4): a sequence scanned in
- *                          independent pieces.
+ *                          independent pieces (with _aggregate_rec /
+ *                          _from_rec, the pieces' inner carries kept).
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library
