@@ -79,12 +79,12 @@ def bwd_valu_slots_per_token_channel(n, bbar="delta"):
     dC (2): 17 slots; per channel step softplus and its derivative (14), the
     gate and its derivative (12), du and dDelta (4): 30 slots.  The
     zero-order-hold input adds per state the coefficient (exp(Delta A) - 1)/A
-    in the recomputed step (9, plus its product: 10) and again in the adjoint
-    (9), its derivative in A (a 5-term series, its scaling, the difference
-    form and the choice: 11) and four products and sums more (u B, lambda
-    coef, lambda u B, the second dA term): 51 slots per state, and one
-    product fewer per channel step (du needs no Delta): 29."""
-    return 51 * n + 29 if bbar == "zoh" else 17 * n + 30
+    in the recomputed step (9, plus its product: 10; the adjoint reuses it),
+    its derivative in A (a 5-term series, its scaling, the difference form
+    and the choice: 11) and four products and sums more (u B, lambda coef,
+    lambda u B, the second dA term): 42 slots per state, and one product
+    fewer per channel step (du needs no Delta): 29."""
+    return 42 * n + 29 if bbar == "zoh" else 17 * n + 30
 
 
 def bwd_algorithmic_bytes(w):

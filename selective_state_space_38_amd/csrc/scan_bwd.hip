@@ -508,6 +508,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
       const Tile& tl = s_tile[k & 1];
       Red& rd = s_red[k % NRED];
       float h[G], hs[TC][G], as[TC][G];
+      float cs[ZOH ? TC : 1][G];  // ZOH: the recomputed input coefficients, for the adjoint
 #pragma unroll
       for (int g = 0; g < G; ++g) h[g] = hstart[g];
 #pragma unroll
@@ -519,7 +520,8 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
           const float x2 = dl * A2[g];
           const float a = exp2_hw(x2);
           if constexpr (ZOH) {
-            h[g] = fmaf(a, h[g], zoh_coef(x2, a, dl, iA[g]) * (du * tl.B[t][gidx + g]));
+            cs[ZOH ? t : 0][g] = zoh_coef(x2, a, dl, iA[g]);
+            h[g] = fmaf(a, h[g], cs[ZOH ? t : 0][g] * (du * tl.B[t][gidx + g]));
           } else {
             h[g] = fmaf(a, h[g], du * tl.B[t][gidx + g]);
           }
@@ -567,7 +569,7 @@ void scan_bwd_kernel(BwdPtrs p, BwdShape sh) {
             // d coef/d A = Delta^2 psi(Delta A)
             const float x2 = dl * A2[g];
             const float a = as[t][g];
-            const float cf = zoh_coef(x2, a, dl, iA[g]);
+            const float cf = cs[ZOH ? t : 0][g];
             const float ub = du * qB[q][g];
             const float lc = lam * cf;
             pB[g] = lc * du;
