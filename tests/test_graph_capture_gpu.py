@@ -1,4 +1,5 @@
-"""HIP graph capture of the decode step and of the allocation-free forward.
+"""HIP graph capture of the decode step, of the allocation-free forward and of
+a kept-carry record with the forward from it.
 
 The binding launches on the current stream, so torch.cuda.graph captures the
 library's kernels.  Each graph is replayed several times with eager work and
@@ -128,5 +129,64 @@ def test_noalloc_forward_replayed_from_a_graph():
               scale, TOL["f32"])
         # eager work between replays: the same entry point on the same array
         fwd(scratch_out, scratch_last)
+        torch.cuda.synchronize()
+    check_device_errors(dev)
+
+
+def test_kept_record_and_forward_replayed_from_a_graph():
+    """A piece's record keeping its inner carries, then the piece's forward
+    from them and an h0, captured together: both take their scratch from the
+    caller's record buffer, so neither allocates, and the record clears its
+    carry words with a fill kernel."""
+    from selective_state_space_38_amd import (check_device_errors, fwd_plan, record_buffer,
+                                              selective_scan_fwd, selective_scan_fwd_aggregate)
+    dev = torch.device("cuda", 0)
+    x = synth.make("seq1m", seqlen=65536)
+    bsz, L, dim = x["u"].shape
+    n = x["A"].shape[1]
+    plan = fwd_plan(bsz, L, dim, n, torch.float32)
+    assert plan["segments"] > 2 and plan["lookback"] == 1, plan
+    f32 = torch.float32
+    t = {k: to_dev(x[k], f32) for k in ("u", "delta", "A", "B", "C", "D", "z", "dt_bias")}
+    h0 = to_dev(np.random.default_rng(12).standard_normal((bsz, dim, n)).astype(np.float32), f32)
+
+    def run(rec, sd, agg, out, last):
+        selective_scan_fwd_aggregate(t["u"], t["delta"], t["A"], t["B"], delta_bias=t["dt_bias"],
+                                     sum_delta=sd, state=agg, rec=rec)
+        selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                           delta_bias=t["dt_bias"], h0=h0, out=out, last_state=last,
+                           return_last_state=True, rec=rec)
+
+    def bufs():
+        return (record_buffer(t["u"], n), torch.empty((bsz, dim), dtype=f32, device=dev),
+                torch.empty((bsz, dim, n), dtype=f32, device=dev), torch.empty_like(t["u"]),
+                torch.empty((bsz, dim, n), dtype=f32, device=dev))
+
+    eager = bufs()
+    run(*eager)
+    torch.cuda.synchronize()
+    graph_bufs = bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(*bufs())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(*graph_bufs)
+
+    ref = [b.double().cpu().numpy() for b in eager[1:]]
+    other = bufs()
+    for rep in range(3):
+        for b in graph_bufs:
+            b.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("sum_delta", "state", "out", "last_state"), graph_bufs[1:],
+                                   ref):
+            check(f"graph {name} (replay {rep})", got.double().cpu().numpy(), want,
+                  float(np.max(np.abs(want))), TOL["f32"])
+        run(*other)                                  # eager work between replays
         torch.cuda.synchronize()
     check_device_errors(dev)
