@@ -988,10 +988,10 @@ def summarize_counters(fetch_dir, write_dir):
 
     def entry(name_key, grid, w, label):
         def hit(n, g):
-            # the forward's own instances (last template flag false), not the
-            # carry-record instances of the same kernel
+            # the forward's own instances (last template argument, the launch
+            # mode, 0), not the carry-record or from-record instances
             return name_key in n and g == grid and (
-                "scan_fwd_kernel" not in n or _template_head(n).endswith("false>"))
+                "scan_fwd_kernel" not in n or _template_head(n).endswith(", 0>"))
         fv = [v for (n, g), vs in fk.items() if hit(n, g) for v in vs]
         wv = [v for (n, g), vs in wk.items() if hit(n, g) for v in vs]
         if not fv or not wv:
@@ -1069,9 +1069,11 @@ def summarize_trace(directory):
     print("|---|---|---|---|---|---|---|")
     for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         label = next((n for (ns, gg), n in names.items() if ns in k and gg == g
-                      and "scan_fwd_kernel" in k and _template_head(k).endswith("false>")), "")
-        if "scan_fwd_kernel" in k and _template_head(k).endswith("true>"):
+                      and "scan_fwd_kernel" in k and _template_head(k).endswith(", 0>")), "")
+        if "scan_fwd_kernel" in k and _template_head(k).endswith(", 1>"):
             label = "carry record"
+        if "scan_fwd_kernel" in k and _template_head(k).endswith(", 2>"):
+            label = "from kept carries"
         if "state_update_kernel" in k:
             label = "decode"
         m = re.match(r"(.*?>)\(", k)
