@@ -188,10 +188,12 @@ def measured_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, w, dec, budget_s, bbar="delta"):
+def cpu_baseline(x, w, dec, budget_s, bbar="delta", gpu_out=None):
     """Times the oracle (as it stands) on a bounded prefix of the workload:
     every batch row and channel, the first L' steps, L' sized to ~budget_s;
-    plus one decode step on a 32-sequence slice of the decode workload."""
+    plus one decode step on a 32-sequence slice of the decode workload.  With
+    the GPU forward's output (same inputs), also reports its max-abs error on
+    that prefix against the oracle, scaled by the oracle's max |out|."""
     import oracle
 
     def sample(L):
@@ -204,8 +206,14 @@ def cpu_baseline(x, w, dec, budget_s, bbar="delta"):
     per_step = (time.perf_counter() - t0) / 8
     L = int(max(8, min(w.seqlen, budget_s / max(per_step, 1e-6))))
     t0 = time.perf_counter()
-    oracle.scan_fwd(*sample(L), bbar=bbar)
+    ref, _ = oracle.scan_fwd(*sample(L), bbar=bbar)
     t_fwd = time.perf_counter() - t0
+    parity = None
+    if gpu_out is not None:
+        scale = float(np.max(np.abs(ref)))
+        err = float(np.max(np.abs(gpu_out[:, :L].astype(np.float64) - ref)))
+        parity = {"max_abs_err_over_max_abs_out": err / scale, "steps_compared": L,
+                  "tolerance": 2e-2 if w.dtype == "bf16" else 1e-4}
     nb = 32
     t0 = time.perf_counter()
     oracle.state_update(dec["state"][:nb], dec["u"][:nb], dec["delta"][:nb], dec["A"],
@@ -228,6 +236,7 @@ def cpu_baseline(x, w, dec, budget_s, bbar="delta"):
                    f"({t_fwd:.1f} s) + one decode step on {nb} sequences ({t_dec:.2f} s)"),
         "host_cpus_available": len(os.sched_getaffinity(0)),
         "blas_threads_idle": blas_threads,
+        "gpu_forward_vs_oracle": parity,
     }
 
 
@@ -1210,6 +1219,9 @@ def main():
     # the forward alone over a timed region: its average launch time
     fwd_region = _time_region_ms(torch, fwd, args.steps, 1)
     check_device_errors(dev)
+    # the forward's output (the last timed launch, same inputs) is kept on the
+    # host for the oracle comparison of the CPU baseline's sample
+    out_host = None if args.no_cpu_baseline else out.float().cpu().numpy()
     del u, dt_, z, Bm, Cm, out
     torch.cuda.empty_cache()
 
@@ -1334,7 +1346,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(x, w, dec, args.cpu_seconds, args.bbar)
+        line["cpu_baseline"] = cpu_baseline(x, w, dec, args.cpu_seconds, args.bbar,
+                                            gpu_out=out_host)
     print(json.dumps(line), flush=True)
 
 

@@ -58,3 +58,22 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_compares_the_gpu_output_on_its_sample():
+    """The baseline's oracle run doubles as a parity check of the GPU
+    forward's output on the same prefix: an exact output reports zero error,
+    a perturbed one its scaled error."""
+    import oracle
+    w = synth.WORKLOADS["tiny"]
+    x = synth.make(w)
+    dec = synth.make("decode", batch=32, dim=16, dstate=4)
+    full, _ = oracle.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
+                              x["dt_bias"])
+    r = bench.cpu_baseline(x, w, dec, 0.01, gpu_out=full.astype("float32"))
+    p = r["gpu_forward_vs_oracle"]
+    assert p["steps_compared"] >= 8 and p["max_abs_err_over_max_abs_out"] < 1e-6
+    bad = full.copy()
+    bad[0, 0, 0] += 0.5 * abs(full).max()
+    p2 = bench.cpu_baseline(x, w, dec, 0.01, gpu_out=bad)["gpu_forward_vs_oracle"]
+    assert 0.4 < p2["max_abs_err_over_max_abs_out"] < 0.6
