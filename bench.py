@@ -188,12 +188,14 @@ def measured_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, w, dec, budget_s, bbar="delta", gpu_out=None):
+def cpu_baseline(x, w, dec, budget_s, bbar="delta", gpu_out=None, gpu_dec=None):
     """Times the oracle (as it stands) on a bounded prefix of the workload:
     every batch row and channel, the first L' steps, L' sized to ~budget_s;
     plus one decode step on a 32-sequence slice of the decode workload.  With
     the GPU forward's output (same inputs), also reports its max-abs error on
-    that prefix against the oracle, scaled by the oracle's max |out|."""
+    that prefix against the oracle, scaled by the oracle's max |out|; with the
+    GPU decode step's (out, new state) from the workload's initial state, the
+    same for the 32 sequences the oracle's decode step covers."""
     import oracle
 
     def sample(L):
@@ -216,10 +218,21 @@ def cpu_baseline(x, w, dec, budget_s, bbar="delta", gpu_out=None):
                   "tolerance": 2e-2 if w.dtype == "bf16" else 1e-4}
     nb = 32
     t0 = time.perf_counter()
-    oracle.state_update(dec["state"][:nb], dec["u"][:nb], dec["delta"][:nb], dec["A"],
-                        dec["B"][:nb], dec["C"][:nb], dec["D"], dec["z"][:nb],
-                        dec["dt_bias"], bbar=bbar)
+    dec_y, dec_h = oracle.state_update(dec["state"][:nb], dec["u"][:nb], dec["delta"][:nb],
+                                       dec["A"], dec["B"][:nb], dec["C"][:nb], dec["D"],
+                                       dec["z"][:nb], dec["dt_bias"], bbar=bbar)
     t_dec = time.perf_counter() - t0
+    dec_parity = None
+    if gpu_dec is not None:
+        gy, gh = gpu_dec
+        sy = float(np.max(np.abs(dec_y)))
+        dec_parity = {
+            "out_max_abs_err_over_max_abs_out":
+                float(np.max(np.abs(gy[:nb].astype(np.float64) - dec_y))) / sy,
+            "state_max_abs_err_over_max_abs_out":
+                float(np.max(np.abs(gh[:nb].astype(np.float64) - dec_h))) / sy,
+            "sequences_compared": nb,
+            "tolerance": 2e-2 if synth.WORKLOADS["decode"].dtype == "bf16" else 1e-4}
     tokch = w.batch * L * w.dim + nb * dec_dim(dec)
     try:
         from threadpoolctl import threadpool_info
@@ -237,6 +250,7 @@ def cpu_baseline(x, w, dec, budget_s, bbar="delta", gpu_out=None):
         "host_cpus_available": len(os.sched_getaffinity(0)),
         "blas_threads_idle": blas_threads,
         "gpu_forward_vs_oracle": parity,
+        "gpu_decode_vs_oracle": dec_parity,
     }
 
 
@@ -1222,6 +1236,15 @@ def main():
     # the forward's output (the last timed launch, same inputs) is kept on the
     # host for the oracle comparison of the CPU baseline's sample
     out_host = None if args.no_cpu_baseline else out.float().cpu().numpy()
+    dec_host = None
+    if not args.no_cpu_baseline and not args.no_decode:
+        # one decode step from the workload's initial state (untimed)
+        fresh = _upload(torch, dev, dec["state"])
+        selective_state_update(fresh, dx, ddt, dA, dB, dC, D=dD, z=dz, dt_bias=dbias,
+                               dt_softplus=True, out=dout, bbar=args.bbar)
+        torch.cuda.synchronize()
+        dec_host = (dout.float().cpu().numpy(), fresh.cpu().numpy())
+        del fresh
     del u, dt_, z, Bm, Cm, out
     torch.cuda.empty_cache()
 
@@ -1347,7 +1370,7 @@ def main():
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(x, w, dec, args.cpu_seconds, args.bbar,
-                                            gpu_out=out_host)
+                                            gpu_out=out_host, gpu_dec=dec_host)
     print(json.dumps(line), flush=True)
 
 

@@ -70,9 +70,15 @@ def test_cpu_baseline_compares_the_gpu_output_on_its_sample():
     dec = synth.make("decode", batch=32, dim=16, dstate=4)
     full, _ = oracle.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
                               x["dt_bias"])
-    r = bench.cpu_baseline(x, w, dec, 0.01, gpu_out=full.astype("float32"))
+    y, h = oracle.state_update(dec["state"], dec["u"], dec["delta"], dec["A"], dec["B"],
+                               dec["C"], dec["D"], dec["z"], dec["dt_bias"])
+    r = bench.cpu_baseline(x, w, dec, 0.01, gpu_out=full.astype("float32"),
+                           gpu_dec=(y.astype("float32"), h.astype("float32")))
     p = r["gpu_forward_vs_oracle"]
     assert p["steps_compared"] >= 8 and p["max_abs_err_over_max_abs_out"] < 1e-6
+    d = r["gpu_decode_vs_oracle"]
+    assert d["out_max_abs_err_over_max_abs_out"] < 1e-6
+    assert d["state_max_abs_err_over_max_abs_out"] < 1e-6
     bad = full.copy()
     bad[0, 0, 0] += 0.5 * abs(full).max()
     p2 = bench.cpu_baseline(x, w, dec, 0.01, gpu_out=bad)["gpu_forward_vs_oracle"]
