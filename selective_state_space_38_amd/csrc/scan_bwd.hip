@@ -805,14 +805,26 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(const float* __restrict_
   store_act(dC, i, sc);
 }
 
-// out[i] = sum_k part[k * count + i]
+// out[i] = sum_k part[k * count + i], added in k order.  The loads of eight
+// consecutive parts are issued together before they are added (the order of
+// the additions, and so the result, is that of the plain loop): with few
+// outputs and many parts (the million-token sequence: 256 channels, 256
+// segment slots) one thread's serial loads were the kernel's whole time.
 __global__ __launch_bounds__(256) void reduce_sum_kernel(const float* __restrict__ part,
                                                          float* __restrict__ out, int64_t count,
                                                          int parts) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= count) return;
   float s = 0.0f;
-  for (int k = 0; k < parts; ++k) s += part[k * count + i];
+  int k = 0;
+  for (; k + 8 <= parts; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = part[(k + j) * count + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  for (; k < parts; ++k) s += part[k * count + i];
   out[i] = s;
 }
 
