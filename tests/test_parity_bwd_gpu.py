@@ -338,3 +338,35 @@ def test_training_pair_long_sequence_all_split():
     # dB and dC need every channel: all 256 are cheap enough here
     ref_all = oracle_backward(x, g)
     check_grads({"dB": got["dB"], "dC": got["dC"]}, ref_all, "f32", keys=["dB", "dC"])
+
+
+@pytest.mark.parametrize("split,tag", [(16, "f32"), (64, "f32"), (16, "bf16")])
+def test_split_backward_stress(split, tag):
+    """The reverse look-back of the adjoint carry under repetition: every
+    chain split into `split` segments (128 or 32 steps at L = 2048), the
+    backward run 20 times from the same checkpoints, every run's gradients
+    against the oracle and against the first run's (only the look-back's
+    summation order may differ), and the device error counter after each."""
+    from selective_state_space_38_amd import check_device_errors
+    wl = "mamba130m" if tag == "f32" else "mamba2p8b"
+    x = synth.make(wl, batch=2, seqlen=2048, dim=128, dstate=16, a_init="random")
+    g = _grads_in(x, tag, 60 + split)
+    _, ck = gpu_forward_train(x, tag, g)
+    ref = oracle_backward(x, g)
+    check_device_errors()
+    first = None
+    _log(f"split bwd stress split={split} {tag}")
+    with env(SSM_FORCE_BWD_SPLIT=split, SSM_FORCE_BWD_WHOLE=0):
+        for rep in range(20):
+            got = gpu_backward(x, tag, g, ckpt=ck)
+            check_device_errors()   # raises if an adjoint-carry wait timed out
+            check_grads(got, ref, tag)
+            if first is None:
+                first = got
+            else:
+                for k, v in got.items():
+                    scale = float(np.max(np.abs(ref[k])))
+                    d = float(np.max(np.abs(v - first[k])))
+                    assert d <= TOL[tag] * scale, (rep, k, d, scale)
+            if rep % 5 == 0:
+                _log(f"  rep {rep} ok")
