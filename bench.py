@@ -49,7 +49,7 @@ import synth  # noqa: E402
 # MI355X public figures: HBM3E at 8 TB/s; 256 CUs x 4 SIMD16 units at 2.4 GHz
 # -> 39.3 T fp32 vector lane-slots per second without packed math (the
 # published 157.3 TFLOP/s counts an FMA as 2 flops and packed pairs as 2
-# lanes; packed fp32 is off in this build).
+# lanes; the library is compiled with packed fp32 disabled).
 HBM_PEAK_GBS = 8000.0
 COMPUTE_UNITS = 256
 VALU_PEAK_TSLOTS = COMPUTE_UNITS * 4 * 16 * 2.4e9 / 1e12
