@@ -166,6 +166,32 @@ KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_38_amd", "csrc", f)
                             "api.hip")]
 
 
+BWD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_38_amd", "csrc", f)
+                      for f in ("scan_bwd.hip", "scan_fwd.hip", "ssm_device.h",
+                                "ssm_internal.h", "api.hip")]
+
+
+def bwd_traffic(workload, train, bbar):
+    """HBM bytes of one backward call (the backward kernel, its reductions and
+    clearing launches) from the committed FETCH_SIZE / WRITE_SIZE counters of
+    the training pair, or None when no counters match this run: another
+    workload or mode, or kernel sources changed since they were taken."""
+    import hashlib
+    import json
+    path = os.path.join(ROOT, "profiles", f"scan_bwd_traffic_{workload}.json")
+    if not train or bbar != "delta" or not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    h = hashlib.sha256()
+    for f in BWD_KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    if rec.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return float(rec["hbm_bytes_per_call"])
+
+
 def kernel_source_digest():
     import hashlib
     h = hashlib.sha256()
@@ -326,7 +352,8 @@ def bwd_bench(args, torch, dev):
                    "bbar": args.bbar},
         "roofline": {
             "bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TSLOTS, "unit": ALU_UNIT,
-            "frac": achieved / VALU_PEAK_TSLOTS, "traffic": None,
+            "frac": achieved / VALU_PEAK_TSLOTS,
+            "traffic": bwd_traffic(w.name, args.train, args.bbar),
             "kernel": "scan_bwd_kernel (+ reductions)",
             "ops_per_unit": f"{bwd_valu_slots_per_token_channel(w.dstate, args.bbar)} fp32 "
                             "VALU issue slots per token*channel",

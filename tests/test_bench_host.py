@@ -83,3 +83,14 @@ def test_cpu_baseline_compares_the_gpu_output_on_its_sample():
     bad[0, 0, 0] += 0.5 * abs(full).max()
     p2 = bench.cpu_baseline(x, w, dec, 0.01, gpu_out=bad)["gpu_forward_vs_oracle"]
     assert 0.4 < p2["max_abs_err_over_max_abs_out"] < 0.6
+
+
+def test_backward_traffic_only_for_matching_counters():
+    """The backward line's traffic comes from the committed counters of the
+    2.8B training pair, only in that mode and with the kernel sources they
+    were taken on; every other run reports none."""
+    t = bench.bwd_traffic("mamba2p8b", True, "delta")
+    assert t is not None and 4.7e9 < t < 6.0e9
+    assert bench.bwd_traffic("mamba2p8b", False, "delta") is None
+    assert bench.bwd_traffic("mamba2p8b", True, "zoh") is None
+    assert bench.bwd_traffic("seq1m", True, "delta") is None
